@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs for the SageAttention forward pass.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark.  It holds no step of the method: it only draws random numbers and
+rounds them to the 16-bit input type, so that both sides of every parity check
+see bit-identical inputs.
+
+Shapes and value distributions follow the workloads on the pages:
+
+* "SageAttention: Accurate 8-Bit Attention for Plug-and-Play Inference
+  Acceleration" (paper detail page), §3, Figure 4: K carries large
+  channel-wise outliers that are a bias shared by all tokens, Q has milder
+  outliers, V is benign.
+* Same page, §5, Table 7: real-model shapes (B, H, N, d), including the ragged
+  token counts 17776, 1105 and 197 used here as ragged-tail cases.
+
+The pages measure on real model activations, which are not available here;
+these seeded draws stand in for them.
+
+Generation recipe: ``numpy.random.default_rng(seed)``; float32
+``standard_normal`` drawn in the order Q, K, V, then the extras of the
+workload; then each tensor is rounded to its 16-bit type with
+round-to-nearest-even.  All tensors are contiguous [B, H, N, d].
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "round_to_bf16_bits",
+           "round_to_fp16", "bf16_bits_to_f32", "Inputs"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "fp16" or "bf16": element type of q, k, v and o
+    causal: bool
+    pv_mode: str        # "fp16" or "fp8"
+    seed: int
+    extras: str         # which outlier recipe to apply (see _apply_extras)
+    note: str = ""
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+    @property
+    def ops(self) -> float:
+        """Attention operation count 4*B*H*N^2*d, halved when causal."""
+        o = 4.0 * self.B * self.H * float(self.N) ** 2 * self.d
+        return o / 2 if self.causal else o
+
+
+# The five workloads of the build.  c3 is the headline throughput shape.
+WORKLOADS = {
+    "c1": Workload("c1", 1, 2, 1024, 64, "fp16", False, "fp16", 0, "kbias4",
+                   "small case: K plus a per-channel bias ~ N(0, 4^2)"),
+    "c2": Workload("c2", 4, 32, 4096, 128, "bf16", True, "fp16", 1, "kchan20",
+                   "LLM prefill: 4 K channels biased by +-20 for all tokens"),
+    "c3": Workload("c3", 1, 24, 16384, 128, "bf16", False, "fp16", 2, "q8_kbias5",
+                   "video DiT: 2 Q outlier channels x8, K bias ~ N(0, 5^2)"),
+    "c4": Workload("c4", 8, 16, 8192, 64, "fp16", False, "fp8", 3, "kbias4",
+                   "8+8 mode: FP8 P~V with per-channel V scales"),
+    "c5": Workload("c5", 1, 32, 32768, 128, "bf16", True, "fp8", 4, "kbias4",
+                   "long context, causal, FP8 P~V"),
+}
+
+
+def round_to_fp16(x: np.ndarray) -> np.ndarray:
+    """float32 -> float16 with round-to-nearest-even (numpy's cast)."""
+    return x.astype(np.float16)
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round-to-nearest-even.
+
+    Inputs are finite by construction, so no NaN handling is needed.
+    """
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class Inputs:
+    """One draw: 16-bit storage (``*_bits`` as uint16) and the exact float32 values."""
+    wl: Workload
+    q_bits: np.ndarray
+    k_bits: np.ndarray
+    v_bits: np.ndarray
+    qf: np.ndarray
+    kf: np.ndarray
+    vf: np.ndarray
+
+    def torch_tensors(self, device="cpu"):
+        """q, k, v as torch tensors of the 16-bit dtype (imports torch lazily)."""
+        import torch
+        dt = torch.float16 if self.wl.dtype == "fp16" else torch.bfloat16
+        out = []
+        for bits in (self.q_bits, self.k_bits, self.v_bits):
+            t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(dt)
+            out.append(t.to(device))
+        return tuple(out)
+
+
+def _apply_extras(wl: Workload, rng, q, k, v):
+    B, H, d = wl.B, wl.H, wl.d
+    e = wl.extras
+    if e == "none":
+        pass
+    elif e.startswith("kbias"):
+        std = float(e[len("kbias"):])
+        k += (rng.standard_normal((B, H, 1, d), dtype=np.float32) * np.float32(std))
+    elif e == "kchan20":
+        chans = rng.choice(d, 4, replace=False)
+        k[..., chans] += np.float32(20.0) * np.array([1, -1, 1, -1], np.float32)
+    elif e == "q8_kbias5":
+        qch = rng.choice(d, 2, replace=False)
+        q[..., qch] *= np.float32(8.0)
+        k += (rng.standard_normal((B, H, 1, d), dtype=np.float32) * np.float32(5.0))
+    elif e == "vout":
+        # one outlier token per channel in V (~3e4): most channel values then
+        # fall far below the per-channel FP8 scale.
+        N = v.shape[2]
+        tok = rng.integers(0, N, size=(B, H, 1, d))
+        np.put_along_axis(v, tok, np.float32(3.0e4), axis=2)
+    else:
+        raise ValueError(f"unknown extras recipe {e!r}")
+
+
+def make_inputs(wl: Workload | str, **overrides) -> Inputs:
+    """Draw q, k, v for a workload (or a named one with fields overridden)."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    if overrides:
+        wl = wl.with_(**overrides)
+    shape = (wl.B, wl.H, wl.N, wl.d)
+    rng = np.random.default_rng(wl.seed)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    _apply_extras(wl, rng, q, k, v)
+    if wl.dtype == "fp16":
+        qh, kh, vh = (round_to_fp16(t) for t in (q, k, v))
+        return Inputs(wl, qh.view(np.uint16), kh.view(np.uint16), vh.view(np.uint16),
+                      qh.astype(np.float32), kh.astype(np.float32), vh.astype(np.float32))
+    if wl.dtype == "bf16":
+        qb, kb, vb = (round_to_bf16_bits(t) for t in (q, k, v))
+        return Inputs(wl, qb, kb, vb, bf16_bits_to_f32(qb), bf16_bits_to_f32(kb),
+                      bf16_bits_to_f32(vb))
+    raise ValueError(f"dtype {wl.dtype!r}")
+
+
+def small(name="t", B=1, H=2, N=200, d=64, dtype="fp16", causal=False, pv_mode="fp16",
+          seed=11, extras="kbias4") -> Workload:
+    """A small ad-hoc workload for tests."""
+    return Workload(name, B, H, N, d, dtype, causal, pv_mode, seed, extras)
