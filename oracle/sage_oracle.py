@@ -206,6 +206,9 @@ def attention(q_op, q_rowscale, k_op, k_keyscale, v_op, v_chanscale, *, causal,
         m   = m'
       O = acc / l * v_chanscale[None, :]
 
+    For FP8 P~V, p_round(P~) = E4M3(448 P~)/448 (the static delta_P) and
+    v_chanscale = delta_V, so O = sum P^ V^ delta_P delta_V / l.
+
     q_op [R, d], q_rowscale [R], k_op [N, d], k_keyscale [N], v_op [N, d],
     v_chanscale [d]; rows = the query positions of the R rows (default 0..R-1).
     When `record`, also returns the per-tile P~ row maxima and the final m, l.
@@ -250,7 +253,9 @@ def _p_round_for(pv_mode: str):
     if pv_mode == "fp16":
         return fp16_round
     if pv_mode == "fp8":
-        return lambda p: e4m3_decode(e4m3_encode(p * 448.0))
+        # P^ = E4M3(P~ / delta_P) with the static delta_P = 1/448; the product
+        # P^ V^ is dequantised by delta_P here and by delta_V per channel.
+        return lambda p: e4m3_decode(e4m3_encode(p * 448.0)) * P_STATIC_FP8
     if pv_mode == "none":
         return lambda p: p
     raise ValueError(pv_mode)
@@ -289,7 +294,7 @@ def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
             qrs = pq["q_scale"][b, h, rows_arr // Q_BLOCK]
             k_op = pq["k_i8"][b, h].astype(np.float64)
             kks = pq["k_scale"][b, h, np.arange(N) // K_BLOCK]
-            vcs = (vscale[b, h].astype(np.float64) / 448.0) if vscale is not None else np.ones(d)
+            vcs = vscale[b, h].astype(np.float64) if vscale is not None else np.ones(d)
             res = attention(q_op, qrs, k_op, kks, vvals[b, h], vcs, causal=causal,
                             p_round=_p_round_for(pv_mode), rows=rows_arr, record=record)
             if record:

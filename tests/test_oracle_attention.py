@@ -97,6 +97,24 @@ def test_hand_worked_int8_fp16():
         np.testing.assert_allclose(o[0, 0, row], expect, rtol=1e-12)
 
 
+def test_hand_worked_fp8_static_scale():
+    # Two keys with scores [0, s], 448 e^s = 17.2: P^ = E4M3(448 P~) = [448, 18]
+    # (17.2 lies above the 16/18 midpoint), so with V unquantised
+    # O = (448 v0 + 18 v1) / (448 (1 + e^s)).  A wrong static scale moves P^.
+    s = math.log(17.2 / 448.0)
+    q = np.zeros((1, 1, 2, 4), np.float32)
+    k = np.zeros((1, 1, 2, 4), np.float32)
+    q[0, 0, 1, 0] = 2 * s                        # d = 4: S = q.k / 2
+    k[0, 0, 1, 0] = 1.0
+    v = np.arange(1, 9, dtype=np.float32).reshape(1, 1, 2, 4)
+    o = sage_attention(q, k, v, causal=False, pv_mode="fp8", quant="none", smooth=False)
+    s32 = float(np.float32(2 * s)) / 2
+    v64 = v.astype(np.float64)
+    expect = (448 * v64[0, 0, 0] + 18 * v64[0, 0, 1]) / (448 * (1 + math.exp(s32)))
+    np.testing.assert_allclose(o[0, 0, 1], expect, rtol=1e-12)
+    np.testing.assert_allclose(o[0, 0, 0], (v64[0, 0, 0] + v64[0, 0, 1]) / 2, rtol=1e-12)
+
+
 @pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ptilde_in_unit_interval_and_max_one(pv_mode, causal):
