@@ -1,0 +1,187 @@
+"""Benchmark of the SageAttention forward pass on one MI355X.
+
+One step = one full forward pass (smooth/quantise prepass + attention kernel)
+over one batch of seeded synthetic inputs already resident in HBM.  Default
+workload: B=1, H=24, N=16384, d=128, non-causal, bf16, FP16 P~V.
+
+Prints ONE JSON line: attention TOPS (4 B H N^2 d / t, halved when causal),
+the attention kernel's roofline position (timed live with HIP events on the
+launch stream), and the CPU oracle's throughput on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload c3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA (published)
+FP8_PEAK_TFLOPS = 5000.0
+FP16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_fwd_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "quantized_attention_qk_amd", "csrc", "attn_fwd.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_src_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_fwd.hip", "sage_common.h", "sage_launch.h"):
+        h.update(open(os.path.join(ROOT, "quantized_attention_qk_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary, or None when absent or the kernel changed."""
+    try:
+        data = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("kernel_src_hash") != kernel_src_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, min_seconds: float):
+    """Time the CPU oracle (as it stands) on whole heads of the workload until
+    at least `min_seconds` have elapsed (at most 4 heads)."""
+    import numpy as np
+
+    import oracle
+    from workloads import make_inputs
+    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
+    one = wl.with_(B=1, H=1)
+    done, t_total, ops = 0, 0.0, 0.0
+    while done < 4 and (t_total < min_seconds or done == 0):
+        inp = make_inputs(one.with_(seed=wl.seed + 1000 + done))
+        t0 = time.perf_counter()
+        pq = oracle.smooth_quant_qk(inp.qf, inp.kf)
+        oracle.sage_attention(inp.qf, inp.kf, inp.vf, causal=wl.causal, pv_mode=wl.pv_mode,
+                              prep=pq)
+        t_total += time.perf_counter() - t0
+        ops += one.ops
+        done += 1
+    return {"value": ops / t_total / 1e12, "unit": "TOPS", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} whole head(s) (B=1,H=1,N={wl.N},d={wl.d}, all query rows, "
+                      f"prepass included) of workload {wl.name}; {t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_attention_qk_amd as qa
+    from workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    wl = WORKLOADS[args.workload]
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    inp = make_inputs(wl)
+    q, k, v = inp.torch_tensors("cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(qa.workspace_bytes(B, H, N, d, wl.pv_mode), dtype=torch.uint8, device="cuda")
+
+    def step():
+        qa.sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    tops = wl.ops / (ms * 1e-3) / 1e12
+
+    # The attention kernel alone, on prepared operands, on the same stream.
+    qk = qa.smooth_quant_qk(q, k)
+    vp, vs = qa.quant_v(v, wl.pv_mode)
+    out2 = torch.empty_like(q)
+    for _ in range(max(2, args.warmup)):
+        qa.sage_attn_quantized(qk, vp, vs, causal=wl.causal, pv_mode=wl.pv_mode,
+                               out_dtype=q.dtype, out=out2)
+    torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(args.steps):
+        qa.sage_attn_quantized(qk, vp, vs, causal=wl.causal, pv_mode=wl.pv_mode,
+                               out_dtype=q.dtype, out=out2)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    kms = k0.elapsed_time(k1) / args.steps
+    ktops = wl.ops / (kms * 1e-3) / 1e12
+    assert torch.equal(out, out2), "attention-only path must reproduce the full pass"
+
+    traffic = traffic_from_profiles(wl.name)
+    mixed_peak = INT8_PEAK_TOPS if wl.pv_mode == "fp8" else \
+        1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / FP16_PEAK_TFLOPS)
+    res = {
+        "metric": "attention TOPS at N=16K,d=128 (1 MI355X) and % of INT8 MFMA peak",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8+f16" if wl.pv_mode == "fp16" else "i8+fp8e4m3",
+        "data": "synthetic (seeded numpy draws, see workloads/)",
+        "config": {"workload": f"{wl.name}: B={B},H={H},N={N},d={d} "
+                               f"{'causal' if wl.causal else 'non-causal'} {wl.dtype}, "
+                               f"INT8 QK^T + {wl.pv_mode.upper()} P~V",
+                   "B": B, "H": H, "N": N, "d": d, "causal": wl.causal,
+                   "pv_mode": wl.pv_mode, "in_dtype": wl.dtype},
+        "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+        "roofline": {"kernel": "attn_fwd_kernel", "bound": "mfma",
+                     "achieved": round(ktops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(ktops / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                     "kernel_ms": round(kms, 4),
+                     "ops_per_launch": wl.ops,
+                     "mixed_mfma_peak": round(mixed_peak, 1),
+                     "frac_of_mixed_peak": round(ktops / mixed_peak, 4)},
+        "prepass_ms": round(ms - kms, 4),
+        "wall_s_timed": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

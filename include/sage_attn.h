@@ -1,0 +1,185 @@
+/*
+ * sage_attn.h -- C ABI of the MI355X (gfx950) SageAttention forward pass.
+ *
+ * Pages defining the operations (cited by title and section):
+ *   [SA]    "SageAttention: Accurate 8-Bit Attention for Plug-and-Play Inference
+ *           Acceleration", paper detail page (arXiv 2410.02367).
+ *   [SA2pp] "SageAttention2++: A More Efficient Implementation of
+ *           SageAttention2", paper review page (arXiv 2505.21136).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are caller-owned DEVICE pointers (HIP device memory of the current
+ * device).  The library never allocates, frees or retains memory and keeps no
+ * global mutable state; calls on different streams may run concurrently.
+ *
+ * q, k, v, o are contiguous [B, H, N, d] tensors ("HND": batch, head, token,
+ * channel) of 16-bit elements (dtype SAGE_DT_F16 or SAGE_DT_BF16); element
+ * offsets are 64-bit.  Base pointers must be 16-byte aligned and o must not
+ * alias an input.  Supported: d in {64, 128}; 1 <= N <= 2^24; B, H >= 1;
+ * causal in {0, 1} (key j visible to query i iff j <= i); the softmax scale
+ * is fixed at 1/sqrt(d).  Inputs must be finite; for SAGE_PV_FP16 every V
+ * value must also be finite in FP16 (|v| <= 65504).
+ *
+ * `stream` is a hipStream_t (NULL = the default stream).  All work is
+ * enqueued on it; no call synchronises the host.  Every call validates all of
+ * its arguments before it enqueues anything, so a call that returns an error
+ * enqueued nothing.  A HIP launch error detected after enqueue is returned as
+ * SAGE_ERR_HIP; device faults surface at the caller's next synchronisation.
+ * No C++ exception crosses this interface.
+ */
+#ifndef SAGE_ATTN_H
+#define SAGE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_ERR_INVALID_ARG = 1,   /* a pointer, size, flag or alignment is invalid */
+  SAGE_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement (e.g. d = 96, not gfx950) */
+  SAGE_ERR_WORKSPACE = 3,     /* workspace / scratch smaller than required */
+  SAGE_ERR_HIP = 4,           /* the HIP runtime reported an error */
+  SAGE_ERR_NO_DEVICE = 5      /* no HIP device is visible */
+} sage_status;
+
+enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8 = 1 };   /* P~V precision: FP16, or FP8 E4M3 ("8+8") */
+enum { SAGE_DT_F16 = 0, SAGE_DT_BF16 = 1 };   /* element type of q, k, v and o */
+enum { SAGE_OUT_F32 = 2 };                     /* float32 output (sage_attn_fwd_quantized only) */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sage_status_str(int status);
+
+/*
+ * Blocking constants of this build, which define the numerics of the method
+ * ([SA] §3 Algorithm 1 leaves the block sizes b_q, b_kv open):
+ *   q_block    tokens per delta_Q quantisation block (128)
+ *   k_block    tokens per delta_K quantisation block (64)
+ *   kv_tile    keys per online-softmax step, visited in ascending order (64)
+ *   mean_chunk tokens per float32 partial sum of the K column mean (256)
+ * Any output pointer may be NULL.  Returns SAGE_ERR_UNSUPPORTED for d outside
+ * {64, 128} or an unknown pv_mode.
+ */
+int sage_attn_get_tiling(int d, int causal, int pv_mode, int* q_block, int* k_block,
+                         int* kv_tile, int* mean_chunk);
+
+/* Workspace bytes sage_attn_fwd needs for this shape (0 if the shape is invalid). */
+size_t sage_attn_workspace_bytes(int B, int H, int N, int d, int pv_mode);
+
+/*
+ * The SageAttention forward pass ([SA] §3 Algorithm 1, kernel "SAGEAttn-B";
+ * FP8 P~V as in [SA2pp] section 三, core formulas):
+ *   1. K~ = K - mean_t(K) per (b, h, channel)               ([SA] §4 Eq. 6)
+ *   2. Q^, delta_Q = psi(Q / sqrt(d)) per 128-token block;
+ *      K^, delta_K = psi(K~) per 64-token block, where psi gives
+ *      delta = max|X|/127 and X^ = round-to-nearest-even(X * 127/max|X|)
+ *   3. for each 64-key tile j, ascending: S = (Q^ K^_j^T as INT32) delta_Q delta_K,
+ *      online softmax (running max m, running sum l of the unquantised P~,
+ *      rescale of the accumulator by exp(m_old - m_new))      ([SA] §4 Eq. 4-5)
+ *   4. pv_mode SAGE_PV_FP16: O += fp16(P~) V'_j with V' = fp16(V);
+ *      pv_mode SAGE_PV_FP8:  O += E4M3(448 P~) V^_j with the static delta_P = 1/448
+ *      and V^ = E4M3(V * 448/colmax|V|), delta_V = colmax|V|/448 per channel;
+ *      FP32 accumulation in both modes
+ *   5. O = O / l (FP8: times delta_V / 448), rounded to the input dtype (RNE).
+ *
+ * q, k, v: inputs [B,H,N,d] of `dtype`; o: output [B,H,N,d] of `dtype`.
+ * workspace: device memory of at least sage_attn_workspace_bytes(B,H,N,d,pv_mode)
+ * bytes, 256-byte aligned; its contents on entry are irrelevant and on return
+ * hold the quantised operands (layout private).  The call is asynchronous.
+ */
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                  int B, int H, int N, int d, int causal, int pv_mode, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* As sage_attn_fwd, with o written as float32 [B,H,N,d] before the final
+ * rounding to the input dtype (same kernels and arithmetic otherwise).
+ * Used to check the forward pass at float32 output precision. */
+int sage_attn_fwd_f32out(const void* q, const void* k, const void* v, float* o,
+                         int B, int H, int N, int d, int causal, int pv_mode, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- The stages of the pass, exposed for testing and reuse -------------- */
+
+/* Scratch bytes sage_smooth_quant_qk needs (float32 partial column sums). */
+size_t sage_smooth_quant_qk_scratch_bytes(int B, int H, int N, int d);
+
+/*
+ * Steps 1-2 above.  Outputs (device, caller-owned, natural layouts):
+ *   q_i8, k_i8 int8 [B,H,N,d]; q_scale float32 [B,H,ceil(N/128)];
+ *   k_scale float32 [B,H,ceil(N/64)]; k_mean float32 [B,H,d].
+ * The column mean is a float32 sum in a fixed order: per 256-token chunk a
+ * sequential sum from 0.0f in increasing token order, then the chunk sums
+ * sequentially in increasing chunk order from 0.0f, then one IEEE division by
+ * N.  K~ = fp32(K - mean); per block a = max|X|, r = fp32(127/a),
+ * X^ = clamp(rne(fp32(X * r)), -127, 127), delta = fp32(a/127); an all-zero
+ * block gets delta = 0 and codes 0.  Q is first scaled: X = fp32(Q * fp32(1/sqrt(d))).
+ * scratch: >= sage_smooth_quant_qk_scratch_bytes(...) bytes, 16-byte aligned.
+ */
+int sage_smooth_quant_qk(const void* q, const void* k, int dtype, int B, int H, int N, int d,
+                         int8_t* q_i8, int8_t* k_i8, float* q_scale, float* k_scale,
+                         float* k_mean, void* scratch, size_t scratch_bytes, void* stream);
+
+/* Bytes of the prepared V (v_out of sage_quant_v) and of its scratch. */
+size_t sage_quant_v_bytes(int B, int H, int N, int d, int pv_mode);
+size_t sage_quant_v_scratch_bytes(int B, int H, int N, int d, int pv_mode);
+
+/*
+ * Step 4's V preparation.  v_out is written in the tiled layout the attention
+ * kernel reads: for each (b, h) and each 64-key tile t (the last one padded
+ * with zeros), d rows of 64 keys, row c holding channel c:
+ *
+ *   SAGE_PV_FP16: row = 128 bytes = eight 16-byte chunks of 8 fp16 values.
+ *     Logical chunk kk (0..7), element e (0..7) holds key
+ *       64 t + 16 (kk / 2) + 8 (e / 4) + 4 (kk % 2) + (e % 4),
+ *     stored at physical chunk kk ^ (c % 8).  Values: fp16_rne(V).
+ *   SAGE_PV_FP8: row = 64 bytes = four 16-byte chunks of 16 E4M3 codes.
+ *     Byte p (0..63) of the logical row holds key
+ *       64 t + 32 ((p / 16) % 2) + 8 ((p % 16) / 4) + 4 (p / 32) + (p % 4),
+ *     and logical chunk p / 16 is stored at physical chunk (p / 16) ^ ((c / 2) % 4).
+ *     Codes: OCP E4M3FN of fp32(V * r_c), round to nearest even, with
+ *     r_c = fp32(448 / colmax_t |V[t, c]|) (0 for an all-zero channel).
+ *
+ * Tile (b, h, t) starts at byte ((b*H + h) * ceil(N/64) + t) * d * rowbytes.
+ * v_scale (FP8 only, else may be NULL): float32 [B,H,d] = fp32(colmax / 448).
+ * scratch: >= sage_quant_v_scratch_bytes(...) bytes, 16-byte aligned
+ * (FP16 mode needs none).  v_out: >= sage_quant_v_bytes(...), 16-byte aligned.
+ */
+int sage_quant_v(const void* v, int dtype, int B, int H, int N, int d, int pv_mode,
+                 void* v_out, float* v_scale, void* scratch, size_t scratch_bytes,
+                 void* stream);
+
+/*
+ * Steps 3-5 alone: the attention kernel on operands already prepared by
+ * sage_smooth_quant_qk and sage_quant_v (e.g. K and V quantised once and
+ * reused).  q_i8, k_i8, q_scale, k_scale: as written by sage_smooth_quant_qk;
+ * v_prep (and v_scale for SAGE_PV_FP8, else may be NULL): as written by
+ * sage_quant_v with the same pv_mode.  o: [B,H,N,d] of out_dtype
+ * (SAGE_DT_F16, SAGE_DT_BF16 or SAGE_OUT_F32).  Same numerics as sage_attn_fwd.
+ */
+int sage_attn_fwd_quantized(const int8_t* q_i8, const int8_t* k_i8, const void* v_prep,
+                            const float* q_scale, const float* k_scale, const float* v_scale,
+                            void* o, int B, int H, int N, int d, int causal, int pv_mode,
+                            int out_dtype, void* stream);
+
+/*
+ * Debug: the INT32 product S = Q^ K^T of one (b, h) on the rectangle
+ * queries [q0, q0+nq) x keys [k0, k0+nk), computed by the same device code
+ * (operand staging, LDS layout, INT8 MFMA tile) as the attention kernel.
+ * q_i8, k_i8: int8 [B,H,N,d] as produced by sage_smooth_quant_qk.
+ * s_out: int32 [nq, nk] row-major.  q0, k0, nq, nk must be multiples of 32
+ * and the rectangle must lie inside [0, ceil32(N)); rows or columns >= N are
+ * written as 0.
+ */
+int sage_attn_debug_s_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
+                          int b, int h, int q0, int nq, int k0, int nk, int32_t* s_out,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_ATTN_H */

@@ -1,0 +1,9 @@
+"""MI355X (gfx950) SageAttention forward pass: smoothed per-block INT8 Q K^T,
+online softmax, FP16 or FP8 E4M3 P~V, behind a C ABI (include/sage_attn.h).
+
+Importing this package does not require a GPU; calling into it does, and it
+fails loudly (RuntimeError) when the HIP library is missing or no device is
+visible.  There is no CPU fallback.
+"""
+from .api import (debug_s_i32, quant_v, sage_attn, sage_attn_quantized,  # noqa: F401
+                  smooth_quant_qk, tiling, untile_v, workspace_bytes)

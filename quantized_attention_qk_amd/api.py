@@ -1,0 +1,168 @@
+"""Python entry points over the C ABI (argument marshalling only).
+
+Every step of the forward pass runs in the HIP kernels of libsage_attn.so;
+torch provides device memory (outputs, workspace) and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import SAGE_DT, SAGE_PV, check, lib
+
+__all__ = ["sage_attn", "sage_attn_quantized", "smooth_quant_qk", "quant_v", "debug_s_i32", "tiling",
+           "workspace_bytes", "untile_v"]
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_qkv(*ts):
+    q = ts[0]
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a HIP device")
+        if t.dtype not in SAGE_DT:
+            raise ValueError(f"dtype {t.dtype} not supported (float16 or bfloat16)")
+        if t.dtype != q.dtype or t.shape != q.shape or t.device != q.device:
+            raise ValueError("q, k, v must share dtype, shape and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+    return tuple(q.shape)
+
+
+def tiling(d: int = 128, causal: bool = False, pv_mode: str = "fp16") -> dict:
+    vals = [ctypes.c_int() for _ in range(4)]
+    check(lib().sage_attn_get_tiling(d, int(causal), SAGE_PV[pv_mode], *[ctypes.byref(v) for v in vals]),
+          "sage_attn_get_tiling")
+    return dict(zip(("q_block", "k_block", "kv_tile", "mean_chunk"), (v.value for v in vals)))
+
+
+def workspace_bytes(B: int, H: int, N: int, d: int, pv_mode: str = "fp16") -> int:
+    return int(lib().sage_attn_workspace_bytes(B, H, N, d, SAGE_PV[pv_mode]))
+
+
+def sage_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+              pv_mode: str = "fp16", out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None, out_f32: bool = False) -> torch.Tensor:
+    """SageAttention forward: O = softmax(Q K^T / sqrt(d)) V with smoothed INT8
+    Q K^T and FP16 or FP8 P~V.  q, k, v: contiguous [B, H, N, d] fp16/bf16.
+
+    Returns O in the input dtype, or float32 when `out_f32`.  `workspace` may
+    be a preallocated uint8 device tensor of workspace_bytes(...) bytes.
+    """
+    B, H, N, d = _check_qkv(q, k, v)
+    mode = SAGE_PV[pv_mode]
+    need = workspace_bytes(B, H, N, d, pv_mode)
+    if need == 0:
+        raise ValueError(f"unsupported shape {(B, H, N, d)}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    odt = torch.float32 if out_f32 else q.dtype
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    elif out.dtype != odt or tuple(out.shape) != (B, H, N, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, N, d] tensor of the output dtype")
+    fn = lib().sage_attn_fwd_f32out if out_f32 else lib().sage_attn_fwd
+    check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d, int(causal),
+             mode, SAGE_DT[q.dtype], workspace.data_ptr(), workspace.numel(),
+             _stream_ptr(q.device)), "sage_attn_fwd")
+    return out
+
+
+def smooth_quant_qk(q: torch.Tensor, k: torch.Tensor) -> dict:
+    """Smooth K and quantise Q/sqrt(d), K to INT8 per block (the prepass)."""
+    B, H, N, d = _check_qkv(q, k)
+    dev = q.device
+    nqb, nkb = -(-N // 128), -(-N // 64)
+    res = dict(q_i8=torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
+               k_i8=torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
+               q_scale=torch.empty((B, H, nqb), dtype=torch.float32, device=dev),
+               k_scale=torch.empty((B, H, nkb), dtype=torch.float32, device=dev),
+               k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev))
+    nscr = int(lib().sage_smooth_quant_qk_scratch_bytes(B, H, N, d))
+    scratch = torch.empty(max(nscr, 16), dtype=torch.uint8, device=dev)
+    check(lib().sage_smooth_quant_qk(
+        q.data_ptr(), k.data_ptr(), SAGE_DT[q.dtype], B, H, N, d, res["q_i8"].data_ptr(),
+        res["k_i8"].data_ptr(), res["q_scale"].data_ptr(), res["k_scale"].data_ptr(),
+        res["k_mean"].data_ptr(), scratch.data_ptr(), scratch.numel(), _stream_ptr(dev)),
+        "sage_smooth_quant_qk")
+    return res
+
+
+def quant_v(v: torch.Tensor, pv_mode: str = "fp16"):
+    """Prepare V for P~V: (tiled uint8 tensor, per-channel scale or None)."""
+    B, H, N, d = _check_qkv(v)
+    dev = v.device
+    mode = SAGE_PV[pv_mode]
+    v_out = torch.empty(int(lib().sage_quant_v_bytes(B, H, N, d, mode)), dtype=torch.uint8,
+                        device=dev)
+    v_scale = torch.empty((B, H, d), dtype=torch.float32, device=dev) if mode == 1 else None
+    nscr = int(lib().sage_quant_v_scratch_bytes(B, H, N, d, mode))
+    scratch = torch.empty(max(nscr, 16), dtype=torch.uint8, device=dev)
+    check(lib().sage_quant_v(v.data_ptr(), SAGE_DT[v.dtype], B, H, N, d, mode, v_out.data_ptr(),
+                             v_scale.data_ptr() if v_scale is not None else None,
+                             scratch.data_ptr(), scratch.numel(), _stream_ptr(dev)),
+          "sage_quant_v")
+    return v_out, v_scale
+
+
+def sage_attn_quantized(qk: dict, v_prep: torch.Tensor, v_scale: torch.Tensor | None,
+                        causal: bool = False, pv_mode: str = "fp16",
+                        out_dtype: torch.dtype = torch.bfloat16,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """The attention kernel alone, on the outputs of smooth_quant_qk/quant_v."""
+    q_i8 = qk["q_i8"]
+    B, H, N, d = q_i8.shape
+    odt = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}[out_dtype]
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
+    check(lib().sage_attn_fwd_quantized(
+        q_i8.data_ptr(), qk["k_i8"].data_ptr(), v_prep.data_ptr(), qk["q_scale"].data_ptr(),
+        qk["k_scale"].data_ptr(), v_scale.data_ptr() if v_scale is not None else None,
+        out.data_ptr(), B, H, N, d, int(causal), SAGE_PV[pv_mode], odt,
+        _stream_ptr(q_i8.device)), "sage_attn_fwd_quantized")
+    return out
+
+
+def debug_s_i32(q_i8: torch.Tensor, k_i8: torch.Tensor, b: int, h: int, q0: int, nq: int,
+                k0: int, nk: int) -> torch.Tensor:
+    """INT32 S = Q^ K^T on a rectangle, by the attention kernel's MFMA code."""
+    B, H, N, d = q_i8.shape
+    if q_i8.dtype != torch.int8 or k_i8.dtype != torch.int8 or k_i8.shape != q_i8.shape:
+        raise ValueError("q_i8, k_i8 must be int8 [B, H, N, d]")
+    s = torch.empty((nq, nk), dtype=torch.int32, device=q_i8.device)
+    check(lib().sage_attn_debug_s_i32(q_i8.data_ptr(), k_i8.data_ptr(), B, H, N, d, b, h, q0, nq,
+                                      k0, nk, s.data_ptr(), _stream_ptr(q_i8.device)),
+          "sage_attn_debug_s_i32")
+    return s
+
+
+def untile_v(v_out, B: int, H: int, N: int, d: int, pv_mode: str = "fp16"):
+    """Inverse of the tiled V layout documented for sage_quant_v: returns a
+    numpy array [B, H, N, d] (float16 values, or uint8 E4M3 codes)."""
+    import numpy as np
+    raw = v_out.cpu().numpy() if hasattr(v_out, "cpu") else np.asarray(v_out)
+    nt = -(-N // 64)
+    c = np.arange(d)[:, None]
+    if pv_mode == "fp16":
+        t = raw.view(np.float16).reshape(B, H, nt, d, 8, 8)      # [.., c, phys chunk, e]
+        kk = np.arange(8)[None, :] ^ (c % 8)                     # logical chunk of each phys chunk
+        e = np.arange(8)
+        key = 16 * (kk[:, :, None] // 2) + 8 * (e // 4) + 4 * (kk[:, :, None] % 2) + e % 4
+        out = np.zeros((B, H, nt, 64, d), np.float16)
+        cc = np.broadcast_to(c[:, :, None], key.shape)
+        out[:, :, :, key, cc] = t
+    else:
+        t = raw.reshape(B, H, nt, d, 4, 16)
+        lq = np.arange(4)[None, :] ^ ((c // 2) % 4)
+        p = 16 * lq[:, :, None] + np.arange(16)
+        key = 32 * ((p // 16) % 2) + 8 * ((p % 16) // 4) + 4 * (p // 32) + p % 4
+        out = np.zeros((B, H, nt, 64, d), np.uint8)
+        cc = np.broadcast_to(c[:, :, None], key.shape)
+        out[:, :, :, key, cc] = t
+    return out.reshape(B, H, nt * 64, d)[:, :, :N]

@@ -1,0 +1,289 @@
+// sage_api.cpp -- the C ABI declared in include/sage_attn.h.
+//
+// Every entry point validates all arguments before it enqueues anything, then
+// checks for a gfx950 device, then launches the kernels of prepass.hip and
+// attn_fwd.hip on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "sage_attn.h"
+#include "sage_launch.h"
+
+namespace {
+
+using sage::ceil_div;
+
+constexpr int kMaxN = 1 << 24;   // (float)N is exact; block indices fit in int
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool shape_ok(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || N > kMaxN) return false;
+  if (d != 64 && d != 128) return false;
+  // B*H*nqb workgroups must fit a 1-D grid; B*H must fit an int.
+  const long long bh = (long long)B * H;
+  if (bh > 0x7fffffffLL) return false;
+  if (bh * ceil_div(N, sage::kQBlock) > 0x7fffffffLL) return false;
+  if (bh > 65535) return false;   // grid.y of the prepass kernels
+  return true;
+}
+
+// Workspace carve-up of sage_attn_fwd (private layout).
+struct Layout {
+  size_t q_i8, k_i8, v_t, q_scale, k_scale, k_mean, v_scale, v_recip, part_sum, part_max, total;
+};
+
+Layout make_layout(int B, int H, int N, int d, int pv_mode) {
+  const size_t bh = (size_t)B * H;
+  const size_t nqb = ceil_div(N, sage::kQBlock), nkb = ceil_div(N, sage::kKBlock);
+  const size_t nt = ceil_div(N, sage::kKvTile), nch = ceil_div(N, sage::kMeanChunk);
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  L.q_i8 = take(bh * N * d);
+  L.k_i8 = take(bh * N * d);
+  L.v_t = take(bh * nt * sage::v_tile_bytes(d, pv_mode));
+  L.q_scale = take(bh * nqb * 4);
+  L.k_scale = take(bh * nkb * 4);
+  L.k_mean = take(bh * d * 4);
+  L.v_scale = take(bh * d * 4);
+  L.v_recip = take(bh * d * 4);
+  L.part_sum = take(bh * nch * d * 4);
+  L.part_max = take(pv_mode == sage::kPvFp8 ? bh * nch * d * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+// 0 = ok, else a sage_status.  The gfx950 check is cached per device.
+int device_check() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
+    (void)hipGetLastError();
+    return SAGE_ERR_NO_DEVICE;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SAGE_ERR_HIP;
+  static std::atomic<int> cache[64];   // 0 unknown, 1 gfx950, 2 other
+  if (dev < 0 || dev >= 64) return SAGE_ERR_UNSUPPORTED;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SAGE_ERR_HIP;
+    c = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    cache[dev].store(c, std::memory_order_relaxed);
+  }
+  return c == 1 ? SAGE_OK : SAGE_ERR_UNSUPPORTED;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
+
+int validate_fwd(const void* q, const void* k, const void* v, const void* o, int B, int H, int N,
+                 int d, int causal, int pv_mode, int dtype, const void* ws, size_t ws_bytes) {
+  if (!q || !k || !v || !o || !ws) return SAGE_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SAGE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return SAGE_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return SAGE_ERR_INVALID_ARG;
+  if (dtype != SAGE_DT_F16 && dtype != SAGE_DT_BF16) return SAGE_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
+  if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
+  if (o == q || o == k || o == v) return SAGE_ERR_INVALID_ARG;
+  if (ws_bytes < make_layout(B, H, N, d, pv_mode).total) return SAGE_ERR_WORKSPACE;
+  return SAGE_OK;
+}
+
+int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+            int causal, int pv_mode, int dtype, void* ws, size_t ws_bytes, void* stream,
+            int out_kind) {
+  int st = validate_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, ws, ws_bytes);
+  if (st != SAGE_OK) return st;
+  if ((st = device_check()) != SAGE_OK) return st;
+  const Layout L = make_layout(B, H, N, d, pv_mode);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+  int8_t* q_i8 = reinterpret_cast<int8_t*>(w + L.q_i8);
+  int8_t* k_i8 = reinterpret_cast<int8_t*>(w + L.k_i8);
+  uint8_t* v_t = w + L.v_t;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fp8 = pv_mode == SAGE_PV_FP8;
+  hipError_t e = sage::launch_colstats(k, fp8 ? v : nullptr, dtype, B, H, N, d, F(L.part_sum),
+                                       fp8 ? F(L.part_max) : nullptr, F(L.k_mean),
+                                       F(L.v_scale), F(L.v_recip), s);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_quant_qk(q, k, F(L.k_mean), dtype, B, H, N, d, q_i8, k_i8, F(L.q_scale),
+                            F(L.k_scale), s);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_prep_v(v, F(L.v_recip), dtype, B, H, N, d, pv_mode, v_t, s);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_attn(q_i8, k_i8, v_t, F(L.q_scale), F(L.k_scale), F(L.v_scale), B, H, N, d,
+                        causal, pv_mode, out_kind, o, s);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sage_status_str(int status) {
+  switch (status) {
+    case SAGE_OK: return "SAGE_OK";
+    case SAGE_ERR_INVALID_ARG: return "SAGE_ERR_INVALID_ARG: invalid pointer, size, flag or alignment";
+    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED: request not supported by this build (d, size or device)";
+    case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE: workspace or scratch too small";
+    case SAGE_ERR_HIP: return "SAGE_ERR_HIP: the HIP runtime reported an error";
+    case SAGE_ERR_NO_DEVICE: return "SAGE_ERR_NO_DEVICE: no HIP device visible";
+    default: return "SAGE_ERR_UNKNOWN";
+  }
+}
+
+int sage_attn_get_tiling(int d, int causal, int pv_mode, int* q_block, int* k_block,
+                         int* kv_tile, int* mean_chunk) {
+  (void)causal;
+  if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return SAGE_ERR_UNSUPPORTED;
+  if (q_block) *q_block = sage::kQBlock;
+  if (k_block) *k_block = sage::kKBlock;
+  if (kv_tile) *kv_tile = sage::kKvTile;
+  if (mean_chunk) *mean_chunk = sage::kMeanChunk;
+  return SAGE_OK;
+}
+
+size_t sage_attn_workspace_bytes(int B, int H, int N, int d, int pv_mode) {
+  if (!shape_ok(B, H, N, d)) return 0;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return 0;
+  return make_layout(B, H, N, d, pv_mode).total;
+}
+
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N,
+                  int d, int causal, int pv_mode, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return run_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, workspace, workspace_bytes,
+                 stream, dtype == SAGE_DT_BF16 ? 1 : 0);
+}
+
+int sage_attn_fwd_f32out(const void* q, const void* k, const void* v, float* o, int B, int H,
+                         int N, int d, int causal, int pv_mode, int dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return run_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, workspace, workspace_bytes,
+                 stream, 2);
+}
+
+size_t sage_smooth_quant_qk_scratch_bytes(int B, int H, int N, int d) {
+  if (!shape_ok(B, H, N, d)) return 0;
+  return (size_t)B * H * ceil_div(N, sage::kMeanChunk) * d * 4;
+}
+
+int sage_smooth_quant_qk(const void* q, const void* k, int dtype, int B, int H, int N, int d,
+                         int8_t* q_i8, int8_t* k_i8, float* q_scale, float* k_scale,
+                         float* k_mean, void* scratch, size_t scratch_bytes, void* stream) {
+  if (!q || !k || !q_i8 || !k_i8 || !q_scale || !k_scale || !k_mean || !scratch)
+    return SAGE_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8) ||
+      !aligned16(scratch) || (reinterpret_cast<uintptr_t>(k_mean) & 7u) ||
+      (reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u))
+    return SAGE_ERR_INVALID_ARG;
+  if (dtype != SAGE_DT_F16 && dtype != SAGE_DT_BF16) return SAGE_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
+  if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
+  if (scratch_bytes < sage_smooth_quant_qk_scratch_bytes(B, H, N, d)) return SAGE_ERR_WORKSPACE;
+  int st = device_check();
+  if (st != SAGE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = sage::launch_colstats(k, nullptr, dtype, B, H, N, d, static_cast<float*>(scratch),
+                                       nullptr, k_mean, nullptr, nullptr, s);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_quant_qk(q, k, k_mean, dtype, B, H, N, d, q_i8, k_i8, q_scale, k_scale, s);
+  return hip_status(e);
+}
+
+size_t sage_quant_v_bytes(int B, int H, int N, int d, int pv_mode) {
+  if (!shape_ok(B, H, N, d)) return 0;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return 0;
+  return (size_t)B * H * ceil_div(N, sage::kKvTile) * sage::v_tile_bytes(d, pv_mode);
+}
+
+size_t sage_quant_v_scratch_bytes(int B, int H, int N, int d, int pv_mode) {
+  if (!shape_ok(B, H, N, d)) return 0;
+  if (pv_mode != SAGE_PV_FP8) return 0;
+  // partial maxima + reciprocal scales
+  return align_up((size_t)B * H * ceil_div(N, sage::kMeanChunk) * d * 4) + (size_t)B * H * d * 4;
+}
+
+int sage_quant_v(const void* v, int dtype, int B, int H, int N, int d, int pv_mode, void* v_out,
+                 float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {
+  if (!v || !v_out) return SAGE_ERR_INVALID_ARG;
+  if (!aligned16(v) || !aligned16(v_out)) return SAGE_ERR_INVALID_ARG;
+  if (dtype != SAGE_DT_F16 && dtype != SAGE_DT_BF16) return SAGE_ERR_INVALID_ARG;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return SAGE_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
+  if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
+  const bool fp8 = pv_mode == SAGE_PV_FP8;
+  if (fp8 && (!v_scale || !scratch || !aligned16(scratch) ||
+              (reinterpret_cast<uintptr_t>(v_scale) & 7u)))
+    return SAGE_ERR_INVALID_ARG;
+  if (scratch_bytes < sage_quant_v_scratch_bytes(B, H, N, d, pv_mode)) return SAGE_ERR_WORKSPACE;
+  int st = device_check();
+  if (st != SAGE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* v_recip = nullptr;
+  if (fp8) {
+    float* part_max = static_cast<float*>(scratch);
+    v_recip = reinterpret_cast<float*>(
+        static_cast<uint8_t*>(scratch) +
+        align_up((size_t)B * H * ceil_div(N, sage::kMeanChunk) * d * 4));
+    hipError_t e = sage::launch_colstats(nullptr, v, dtype, B, H, N, d, nullptr, part_max, nullptr,
+                                         v_scale, v_recip, s);
+    if (e != hipSuccess) return SAGE_ERR_HIP;
+  }
+  return hip_status(sage::launch_prep_v(v, v_recip, dtype, B, H, N, d, pv_mode,
+                                        static_cast<uint8_t*>(v_out), s));
+}
+
+int sage_attn_fwd_quantized(const int8_t* q_i8, const int8_t* k_i8, const void* v_prep,
+                            const float* q_scale, const float* k_scale, const float* v_scale,
+                            void* o, int B, int H, int N, int d, int causal, int pv_mode,
+                            int out_dtype, void* stream) {
+  if (!q_i8 || !k_i8 || !v_prep || !q_scale || !k_scale || !o) return SAGE_ERR_INVALID_ARG;
+  if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_prep) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u))
+    return SAGE_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return SAGE_ERR_INVALID_ARG;
+  if (out_dtype != SAGE_DT_F16 && out_dtype != SAGE_DT_BF16 && out_dtype != SAGE_OUT_F32)
+    return SAGE_ERR_INVALID_ARG;
+  if (pv_mode == SAGE_PV_FP8 && (!v_scale || (reinterpret_cast<uintptr_t>(v_scale) & 3u)))
+    return SAGE_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
+  if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
+  int st = device_check();
+  if (st != SAGE_OK) return st;
+  return hip_status(sage::launch_attn(q_i8, k_i8, static_cast<const uint8_t*>(v_prep), q_scale,
+                                      k_scale, v_scale, B, H, N, d, causal, pv_mode, out_dtype,
+                                      o, static_cast<hipStream_t>(stream)));
+}
+
+int sage_attn_debug_s_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
+                          int b, int h, int q0, int nq, int k0, int nk, int32_t* s_out,
+                          void* stream) {
+  if (!q_i8 || !k_i8 || !s_out) return SAGE_ERR_INVALID_ARG;
+  if (!aligned16(q_i8) || !aligned16(k_i8) || (reinterpret_cast<uintptr_t>(s_out) & 3u))
+    return SAGE_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
+  if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
+  if (b < 0 || b >= B || h < 0 || h >= H) return SAGE_ERR_INVALID_ARG;
+  const int n32 = ceil_div(N, 32) * 32;
+  if (q0 < 0 || k0 < 0 || nq < 32 || nk < 32 || (q0 | k0 | nq | nk) % 32 != 0 ||
+      (long long)q0 + nq > n32 || (long long)k0 + nk > n32)
+    return SAGE_ERR_INVALID_ARG;
+  int st = device_check();
+  if (st != SAGE_OK) return st;
+  return hip_status(sage::launch_debug_s(q_i8, k_i8, B, H, N, d, b, h, q0, nq, k0, nk, s_out,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

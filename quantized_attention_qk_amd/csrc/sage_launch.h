@@ -1,0 +1,61 @@
+// sage_launch.h -- host-side launchers of the HIP kernels (internal C++ API
+// used by the C ABI in sage_api.cpp).  All arguments have been validated by
+// the caller; the launchers only size grids and enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sage {
+
+// Blocking contract (the pages leave b_q, b_kv open; see sage_attn.h).
+constexpr int kQBlock = 128;     // tokens per delta_Q block
+constexpr int kKBlock = 64;      // tokens per delta_K block
+constexpr int kKvTile = 64;      // keys per online-softmax step
+constexpr int kMeanChunk = 256;  // tokens per float32 partial column sum
+constexpr int kWaveQ = 32;       // query rows per wavefront (one 32x32 MFMA column block)
+constexpr int kWaves = 4;        // wavefronts per attention workgroup
+constexpr int kBlockQ = kWaveQ * kWaves;   // 128 query rows per workgroup
+static_assert(kBlockQ == kQBlock, "a workgroup covers exactly one delta_Q block");
+static_assert(kKvTile == kKBlock, "one delta_K per KV tile");
+
+constexpr int kPvFp16 = 0;
+constexpr int kPvFp8 = 1;
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Bytes of one 64-key tile of prepared V (d rows of 64 keys).
+inline size_t v_tile_bytes(int d, int pv_mode) {
+  return (size_t)d * (pv_mode == kPvFp16 ? 128 : 64);
+}
+
+// Prepass: column statistics of K (float32 partial sums per 256-token chunk)
+// and, if part_max != nullptr, of |V| (partial maxima), then the finalised
+// mean (and V scale / reciprocal when v_scale != nullptr).
+hipError_t launch_colstats(const void* k, const void* v, int dtype, int B, int H, int N, int d,
+                           float* part_sum, float* part_max, float* k_mean, float* v_scale,
+                           float* v_recip, hipStream_t s);
+
+// Prepass: INT8 quantisation of Q/sqrt(d) (128-token blocks) and of K - mean
+// (64-token blocks).  Either q or k may be null to skip that tensor.
+hipError_t launch_quant_qk(const void* q, const void* k, const float* k_mean, int dtype, int B,
+                           int H, int N, int d, int8_t* q_i8, int8_t* k_i8, float* q_scale,
+                           float* k_scale, hipStream_t s);
+
+// Prepass: V -> fp16 or E4M3 in the tiled layout of the attention kernel.
+hipError_t launch_prep_v(const void* v, const float* v_recip, int dtype, int B, int H, int N,
+                         int d, int pv_mode, uint8_t* v_out, hipStream_t s);
+
+// Attention kernel.  out_kind: 0 = fp16, 1 = bf16, 2 = float32.
+hipError_t launch_attn(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
+                       const float* q_scale, const float* k_scale, const float* v_scale, int B,
+                       int H, int N, int d, int causal, int pv_mode, int out_kind, void* out,
+                       hipStream_t s);
+
+// Debug: INT32 S = Q^ K^T on a rectangle of one (b, h).
+hipError_t launch_debug_s(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
+                          int b, int h, int q0, int nq, int k0, int nk, int32_t* s_out,
+                          hipStream_t s);
+
+}  // namespace sage

@@ -1,0 +1,163 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol
+declared in include/sage_attn.h, reports its tiling, sizes its workspace, and
+rejects invalid arguments (or reports a missing device) without enqueuing.
+
+Fake device pointers below are never dereferenced: every call returns before
+any launch, either from argument validation or from the device check.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from quantized_attention_qk_amd import _lib
+from quantized_attention_qk_amd._lib import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage_attn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP, NO_DEVICE = range(6)
+P = 0x10000          # an aligned, never-dereferenced fake pointer
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    h = lib()
+    for n in names:
+        assert hasattr(h, n), n
+    assert sorted(_lib.exported_symbols()) == names
+
+
+def test_status_strings():
+    for code, tag in [(OK, "SAGE_OK"), (INVALID, "INVALID_ARG"), (UNSUPPORTED, "UNSUPPORTED"),
+                      (WORKSPACE, "WORKSPACE"), (HIP, "SAGE_ERR_HIP"), (NO_DEVICE, "NO_DEVICE")]:
+        assert tag in _lib.status_str(code)
+    assert "UNKNOWN" in _lib.status_str(99)
+
+
+def test_tiling_contract_matches_oracle():
+    import oracle
+    vals = [ctypes.c_int() for _ in range(4)]
+    for d in (64, 128):
+        for pv in (0, 1):
+            assert lib().sage_attn_get_tiling(d, 0, pv, *[ctypes.byref(v) for v in vals]) == OK
+            assert [v.value for v in vals] == [oracle.Q_BLOCK, oracle.K_BLOCK, oracle.KV_TILE,
+                                               oracle.MEAN_CHUNK]
+    assert lib().sage_attn_get_tiling(96, 0, 0, None, None, None, None) == UNSUPPORTED
+    assert lib().sage_attn_get_tiling(64, 0, 7, None, None, None, None) == UNSUPPORTED
+
+
+def test_workspace_sizes():
+    h = lib()
+    B, H, N, d = 1, 24, 16384, 128
+    w16 = h.sage_attn_workspace_bytes(B, H, N, d, 0)
+    w8 = h.sage_attn_workspace_bytes(B, H, N, d, 1)
+    elems = B * H * N * d
+    # Q^ + K^ (int8) + V' (fp16) at least; V^ (e4m3) is half of V'
+    assert w16 >= 2 * elems + 2 * elems
+    assert w8 >= 2 * elems + elems and w8 < w16
+    assert h.sage_attn_workspace_bytes(1, 1, 0, 64, 0) == 0
+    assert h.sage_attn_workspace_bytes(1, 1, 10, 96, 0) == 0
+    assert h.sage_attn_workspace_bytes(1, 1, 10, 64, 3) == 0
+    assert h.sage_quant_v_bytes(1, 2, 65, 64, 0) == 2 * 2 * 64 * 128
+    assert h.sage_quant_v_bytes(1, 2, 65, 64, 1) == 2 * 2 * 64 * 64
+    assert h.sage_quant_v_scratch_bytes(1, 2, 65, 64, 0) == 0
+    assert h.sage_smooth_quant_qk_scratch_bytes(2, 3, 257, 128) == 2 * 3 * 2 * 128 * 4
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P + 0x1000, B=1, H=2, N=100, d=64, causal=0, pv=0, dtype=0,
+             ws=P + 0x100000, wsb=1 << 40)
+    a.update(kw)
+    return lib().sage_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["N"], a["d"],
+                               a["causal"], a["pv"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(ws=None), INVALID),
+    (dict(q=P + 8), INVALID), (dict(o=P + 2), INVALID), (dict(ws=P + 16), INVALID),
+    (dict(causal=2), INVALID), (dict(pv=2), INVALID), (dict(dtype=5), INVALID),
+    (dict(N=0), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(N=(1 << 24) + 1), UNSUPPORTED),
+    (dict(o=P), INVALID), (dict(wsb=1000), WORKSPACE),
+])
+def test_fwd_argument_validation(kw, code):
+    assert fwd(**kw) == code
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_no_device_reported_after_validation():
+    # valid arguments: the only failure left is the missing device
+    assert fwd() == NO_DEVICE
+    assert lib().sage_attn_fwd_f32out(P, P, P, P + 0x1000, 1, 2, 100, 64, 0, 0, 0, P + 0x100000,
+                                      1 << 40, None) == NO_DEVICE
+
+
+def test_stage_argument_validation():
+    h = lib()
+    # smooth_quant_qk: scratch too small
+    assert h.sage_smooth_quant_qk(P, P, 0, 1, 1, 300, 64, P, P, P, P, P, P, 16, None) == WORKSPACE
+    assert h.sage_smooth_quant_qk(P, P, 0, 1, 1, 300, 64, None, P, P, P, P, P, 1 << 30, None) == INVALID
+    assert h.sage_smooth_quant_qk(P, P, 0, 1, 1, 300, 96, P, P, P, P, P, P, 1 << 30, None) == UNSUPPORTED
+    # quant_v: FP8 needs v_scale and scratch
+    assert h.sage_quant_v(P, 0, 1, 1, 300, 64, 1, P, None, P, 1 << 30, None) == INVALID
+    assert h.sage_quant_v(P, 0, 1, 1, 300, 64, 1, P, P, P, 8, None) == WORKSPACE
+    assert h.sage_quant_v(P, 0, 1, 1, 300, 64, 4, P, P, P, 1 << 30, None) == INVALID
+    # debug S: rectangle must be 32-aligned and inside the padded range
+    assert h.sage_attn_debug_s_i32(P, P, 1, 1, 100, 64, 0, 0, 0, 32, 16, 32, P, None) == INVALID
+    assert h.sage_attn_debug_s_i32(P, P, 1, 1, 100, 64, 0, 0, 96, 64, 0, 32, P, None) == INVALID
+    assert h.sage_attn_debug_s_i32(P, P, 1, 1, 100, 64, 0, 1, 0, 32, 0, 32, P, None) == INVALID
+    if not torch.cuda.is_available():
+        assert h.sage_attn_debug_s_i32(P, P, 1, 1, 100, 64, 0, 0, 96, 32, 0, 128, P, None) == NO_DEVICE
+        assert h.sage_smooth_quant_qk(P, P, 0, 1, 1, 300, 64, P, P, P, P, P, P, 1 << 30, None) == NO_DEVICE
+
+
+def test_python_binding_fails_loudly_without_device():
+    import quantized_attention_qk_amd as qa
+    if torch.cuda.is_available():
+        pytest.skip("device present")
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        qa.sage_attn(q, q, q)          # CPU tensors are rejected, never computed on the CPU
+
+
+def test_untile_v_inverts_documented_layout():
+    # build a tiled buffer from the documented formulas and invert it
+    import numpy as np
+    from quantized_attention_qk_amd import untile_v
+    B, H, N, d = 1, 2, 70, 64
+    nt = 2
+    for mode, rowb in (("fp16", 128), ("fp8", 64)):
+        nat = np.arange(B * H * nt * 64 * d).reshape(B, H, nt * 64, d)
+        if mode == "fp16":
+            nat = (nat % 2000).astype(np.float16)
+            tiled = np.zeros((B, H, nt, d, 8, 8), np.float16)
+            for t in range(nt):
+                for c in range(d):
+                    for kk in range(8):
+                        for e in range(8):
+                            key = 64 * t + 16 * (kk // 2) + 8 * (e // 4) + 4 * (kk % 2) + e % 4
+                            tiled[0, :, t, c, kk ^ (c % 8), e] = nat[0, :, key, c]
+            raw = tiled.view(np.uint8).ravel()
+        else:
+            nat = (nat % 251).astype(np.uint8)
+            tiled = np.zeros((B, H, nt, d, 64), np.uint8)
+            for t in range(nt):
+                for c in range(d):
+                    for p in range(64):
+                        key = 64 * t + 32 * ((p // 16) % 2) + 8 * ((p % 16) // 4) + 4 * (p // 32) + p % 4
+                        phys = 16 * ((p // 16) ^ ((c // 2) % 4)) + p % 16
+                        tiled[0, :, t, c, phys] = nat[0, :, key, c]
+            raw = tiled.ravel()
+        assert raw.size == B * H * nt * d * rowb
+        back = untile_v(raw, B, H, N, d, mode)
+        np.testing.assert_array_equal(back, nat[:, :, :N])
