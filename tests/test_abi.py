@@ -161,3 +161,23 @@ def test_untile_v_inverts_documented_layout():
         assert raw.size == B * H * nt * d * rowb
         back = untile_v(raw, B, H, N, d, mode)
         np.testing.assert_array_equal(back, nat[:, :, :N])
+
+
+def test_quantized_entry_validation():
+    h = lib()
+    args = [P] * 7 + [1, 2, 100, 64, 0, 0, 0, None]
+    bad = list(args)
+    bad[0] = None
+    assert h.sage_attn_fwd_quantized(*bad) == INVALID
+    bad = list(args)
+    bad[13] = 3                    # out dtype
+    assert h.sage_attn_fwd_quantized(*bad) == INVALID
+    bad = list(args)
+    bad[12] = 1                    # FP8 without v_scale
+    bad[5] = None
+    assert h.sage_attn_fwd_quantized(*bad) == INVALID
+    bad = list(args)
+    bad[10] = 80                   # d
+    assert h.sage_attn_fwd_quantized(*bad) == UNSUPPORTED
+    if not torch.cuda.is_available():
+        assert h.sage_attn_fwd_quantized(*args) == NO_DEVICE
