@@ -135,11 +135,11 @@ size_t sage_quant_v_scratch_bytes(int B, int H, int N, int d, int pv_mode);
  *   SAGE_PV_FP16: row = 128 bytes = eight 16-byte chunks of 8 fp16 values.
  *     Logical chunk kk (0..7), element e (0..7) holds key
  *       64 t + 16 (kk / 2) + 8 (e / 4) + 4 (kk % 2) + (e % 4),
- *     stored at physical chunk kk ^ (c % 8).  Values: fp16_rne(V).
+ *     stored at physical chunk kk ^ ((c / 2) % 8).  Values: fp16_rne(V).
  *   SAGE_PV_FP8: row = 64 bytes = four 16-byte chunks of 16 E4M3 codes.
  *     Byte p (0..63) of the logical row holds key
  *       64 t + 32 ((p / 16) % 2) + 8 ((p % 16) / 4) + 4 (p / 32) + (p % 4),
- *     and logical chunk p / 16 is stored at physical chunk (p / 16) ^ ((c / 2) % 4).
+ *     and logical chunk p / 16 is stored at physical chunk (p / 16) ^ ((c / 4) % 4).
  *     Codes: OCP E4M3FN of fp32(V * r_c), round to nearest even, with
  *     r_c = fp32(448 / colmax_t |V[t, c]|) (0 for an all-zero channel).
  *

@@ -151,7 +151,7 @@ def untile_v(v_out, B: int, H: int, N: int, d: int, pv_mode: str = "fp16"):
     c = np.arange(d)[:, None]
     if pv_mode == "fp16":
         t = raw.view(np.float16).reshape(B, H, nt, d, 8, 8)      # [.., c, phys chunk, e]
-        kk = np.arange(8)[None, :] ^ (c % 8)                     # logical chunk of each phys chunk
+        kk = np.arange(8)[None, :] ^ ((c // 2) % 8)              # logical chunk of each phys chunk
         e = np.arange(8)
         key = 16 * (kk[:, :, None] // 2) + 8 * (e // 4) + 4 * (kk[:, :, None] % 2) + e % 4
         out = np.zeros((B, H, nt, 64, d), np.float16)
@@ -159,7 +159,7 @@ def untile_v(v_out, B: int, H: int, N: int, d: int, pv_mode: str = "fp16"):
         out[:, :, :, key, cc] = t
     else:
         t = raw.reshape(B, H, nt, d, 4, 16)
-        lq = np.arange(4)[None, :] ^ ((c // 2) % 4)
+        lq = np.arange(4)[None, :] ^ ((c // 4) % 4)
         p = 16 * lq[:, :, None] + np.arange(16)
         key = 32 * ((p // 16) % 2) + 8 * ((p % 16) // 4) + 4 * (p // 32) + p % 4
         out = np.zeros((B, H, nt, 64, d), np.uint8)

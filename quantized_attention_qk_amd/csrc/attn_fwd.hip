@@ -27,10 +27,12 @@
 //   tile: P~ = exp2(s * c_j - m) with c_j = delta_Q delta_K[j] log2(e).  For
 //   FP8, log2(448) is folded into the same subtraction so the MFMA operand is
 //   448 P~ directly, and l is kept in the same units.
-// * K^ and prepared-V tiles are staged through LDS (double buffered, XOR
-//   swizzled rows); global loads for tile j+1 are in flight during tile j.
+// * K^ and prepared-V tiles go from HBM straight into LDS (global_load_lds,
+//   double buffered, XOR-swizzled rows), one step ahead of their use.
 // * The output rescale by alpha is skipped when no row of the wavefront has a
 //   new maximum (alpha == 1 exactly), which is bit-identical.
+#include <type_traits>
+
 #include "sage_common.h"
 #include "sage_launch.h"
 
@@ -81,51 +83,58 @@ __device__ __forceinline__ v16i qk_block(const v4i (&qf)[D / 32], const uint8_t*
   return acc;
 }
 
-// Global -> register staging of one K^ tile, then register -> LDS with the
-// row swizzle.  Keys >= N are staged as zeros.
-template <int D, int NT>
-struct KStage {
-  static constexpr int PER = KTile<D>::CHUNKS / NT;
-  static_assert(PER * NT == KTile<D>::CHUNKS, "threads must tile the K^ tile");
-  uint4 r[PER];
-  __device__ __forceinline__ void load(const int8_t* __restrict__ k_bh, int key0, int N, int tid) {
+typedef __attribute__((address_space(3))) void lds_void;
+
+// HBM -> LDS copies with global_load_lds_dwordx4: every lane moves 16 bytes
+// straight into LDS (no VGPR staging); a wavefront writes 1 KiB contiguous
+// LDS bytes per instruction, so the K^ row swizzle is applied by choosing
+// each lane's source address.  NW wavefronts share the work.
+template <int D, int NW>
+struct KLoader {
+  static constexpr int PER = KTile<D>::CHUNKS / (64 * NW);
+  static_assert(PER * 64 * NW == KTile<D>::CHUNKS, "wavefronts must tile the K^ tile");
+  int row[PER], off[PER];   // per-lane source row and byte offset within the tile
+  __device__ __forceinline__ KLoader(int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int g = tid + i * NT;
-      const int key = g / KTile<D>::CPR;
-      const int kc = g % KTile<D>::CPR;
-      r[i] = (key0 + key < N)
-                 ? *reinterpret_cast<const uint4*>(k_bh + (size_t)(key0 + key) * D + kc * 16)
-                 : uint4{0u, 0u, 0u, 0u};
+      const int P = (i * NW + wave) * 64 + lane;   // LDS chunk this lane writes
+      row[i] = P / KTile<D>::CPR;
+      const int kc = (P % KTile<D>::CPR) ^ row_swizzle<D>(row[i]);
+      off[i] = row[i] * D + kc * 16;
     }
   }
-  __device__ __forceinline__ void store(uint8_t* kb, int tid) const {
+  // Rows at or beyond N re-read row N-1 (their scores are masked).
+  template <bool CLAMP>
+  __device__ __forceinline__ void issue(const int8_t* __restrict__ k_bh, int key0, int N,
+                                        uint8_t* kb, int wave) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int g = tid + i * NT;
-      const int key = g / KTile<D>::CPR;
-      const int kc = g % KTile<D>::CPR;
-      *reinterpret_cast<uint4*>(kb + KTile<D>::lds_off(key, kc)) = r[i];
+      const int8_t* src = k_bh + (size_t)key0 * D + off[i];
+      if constexpr (CLAMP)
+        if (key0 + row[i] >= N) src = k_bh + (size_t)(N - 1) * D + (off[i] - row[i] * D);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(kb + (i * NW + wave) * 1024), 16, 0, 0);
     }
   }
 };
 
-// Prepared-V tiles are stored pre-swizzled, so staging is a linear copy.
-template <int D, int PV, int NT>
-struct VStage {
-  static constexpr int PER = VTile<D, PV>::CHUNKS / NT;
-  static_assert(PER * NT == VTile<D, PV>::CHUNKS, "threads must tile the V tile");
-  uint4 r[PER];
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ vtile, int tid) {
+// Prepared-V tiles are stored pre-swizzled, so their copy is linear.
+template <int D, int PV, int NW>
+struct VLoader {
+  static constexpr int PER = VTile<D, PV>::CHUNKS / (64 * NW);
+  static_assert(PER * 64 * NW == VTile<D, PV>::CHUNKS, "wavefronts must tile the V tile");
+  __device__ __forceinline__ static void issue(const uint8_t* __restrict__ vtile, uint8_t* vb,
+                                               int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-      r[i] = *reinterpret_cast<const uint4*>(vtile + (size_t)(tid + i * NT) * 16);
-  }
-  __device__ __forceinline__ void store(uint8_t* vb, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) *reinterpret_cast<uint4*>(vb + (tid + i * NT) * 16) = r[i];
+    for (int i = 0; i < PER; ++i) {
+      const int P = (i * NW + wave) * 64 + lane;
+      __builtin_amdgcn_global_load_lds(vtile + (size_t)P * 16,
+                                       (lds_void*)(vb + (i * NW + wave) * 1024), 16, 0, 0);
+    }
   }
 };
+
+// Wait until this wavefront's HBM -> LDS copies have landed.
+__device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int OUT>
 __device__ __forceinline__ void store4(void* out, size_t idx, float a, float b, float c, float d) {
@@ -140,6 +149,185 @@ __device__ __forceinline__ void store4(void* out, size_t idx, float a, float b, 
   }
 }
 
+// P~ of one tile as the B operand of the P~V MFMA: FP16 = four 8-half steps
+// (16 keys each), FP8 = one 32-byte operand covering the 64 keys.
+template <int PV>
+struct PTile;
+template <>
+struct PTile<kPvFp16> {
+  v4i w[4];
+};
+template <>
+struct PTile<kPvFp8> {
+  v8i w;
+};
+
+// S^T = K^ Q^T for one 64-key tile: two 32x32 INT32 blocks.
+template <int D>
+__device__ __forceinline__ void qk_tile(v16i (&s)[2], const v4i (&qf)[D / 32], const uint8_t* kb,
+                                        int n, int hh) {
+  s[0] = qk_block<D>(qf, kb, 0, n, hh);
+  s[1] = qk_block<D>(qf, kb, 1, n, hh);
+}
+
+// In FP16 mode the running max used for P~ is refreshed only when a tile's max
+// exceeds it by more than this many log2 units; until then P~ may reach
+// 2^kLazyMax (far inside FP16 range) and the output rescale is skipped.  The
+// result is the same softmax up to rounding.  FP8 mode keeps the exact max
+// because P^ = 448 P~ must not exceed the E4M3 range.
+constexpr float kLazyMax = 8.0f;
+
+// Online softmax of one tile: returns alpha = exp2(m_old - m_new) and writes
+// P~ (FP8: 448 P~) into the MFMA operand.  MASK selects the variant that
+// masks keys >= N and (causal) keys > query; a fully masked tile leaves the
+// state unchanged (P~ = 0, alpha = 1).
+template <int PV, bool CAUSAL, bool MASK>
+__device__ __forceinline__ float softmax_tile(v16i (&s)[2], float& m_run, float& l_run,
+                                              PTile<PV>& pt, float cj, int key0, int N, int qrow,
+                                              int hh) {
+  uint32_t keep = 0xffffffffu;   // bit 16*blk + r: key visible
+  if constexpr (MASK) {
+    keep = 0u;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * blk + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const bool ok = key < N && (!CAUSAL || key <= qrow);
+        keep |= (uint32_t)ok << (16 * blk + r);
+        if (!ok) s[blk][r] = INT32_MIN;
+      }
+  }
+  // row max: chain of 3-input maxima over the lane's 32 scores, then the pair
+  int mx = max(s[0][0], s[0][1]);
+#pragma unroll
+  for (int i = 2; i < 32; i += 2) mx = max(mx, max(s[i >> 4][i & 15], s[i >> 4][(i & 15) + 1]));
+  mx = pair_max_i32(mx);
+  const float mt = (float)mx * cj;
+  float m_new;
+  if constexpr (PV == kPvFp16) m_new = mt > m_run + kLazyMax ? mt : m_run;
+  else m_new = fmaxf(m_run, mt);
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  const float negm = PV == kPvFp8 ? kLog2_448 - m_new : -m_new;
+
+  float p[2][16];
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float e = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[blk][r], cj, negm));
+      if constexpr (MASK) e = ((keep >> (16 * blk + r)) & 1u) ? e : 0.f;
+      p[blk][r] = e;
+      if constexpr (PV == kPvFp8) ls[r & 3] += e;
+    }
+
+  if constexpr (PV == kPvFp16) {
+    // step S (16 keys) = registers 8*(S%2) .. +7 of block S/2; the row sum
+    // adds the fp16 values the MFMA consumes (v_dot2 with (1, 1): two keys
+    // per instruction, float32 accumulation).
+    const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int S = 0; S < 4; ++S) {
+      const int blk = S >> 1, r0 = 8 * (S & 1);
+      pt.w[S] = v4i{(int)pack_f16x2(p[blk][r0 + 0], p[blk][r0 + 1]),
+                    (int)pack_f16x2(p[blk][r0 + 2], p[blk][r0 + 3]),
+                    (int)pack_f16x2(p[blk][r0 + 4], p[blk][r0 + 5]),
+                    (int)pack_f16x2(p[blk][r0 + 6], p[blk][r0 + 7])};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // copy the element to a scalar first: clang mis-lowers a bit_cast
+        // whose operand is an ext_vector element (it reads element 0)
+        const int pair = pt.w[S][i];
+        ls[i] = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, pair), one, ls[i], false);
+      }
+    }
+  } else {
+    // byte 16*blk + r <-> register r of block blk
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int blk = w >> 2, r0 = 4 * (w & 3);
+      pt.w[w] = (int)pack_fp8x4(p[blk][r0], p[blk][r0 + 1], p[blk][r0 + 2], p[blk][r0 + 3]);
+    }
+  }
+  l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
+  m_run = m_new;
+  return alpha;
+}
+
+// O^T += V^T P~^T for one tile, V from LDS.
+template <int D, int PV>
+__device__ __forceinline__ void pv_tile(v16f (&o)[D / 32], const PTile<PV>& pt,
+                                        const uint8_t* vb, int n, int hh) {
+  constexpr int NCB = D / 32;
+  if constexpr (PV == kPvFp16) {
+#pragma unroll
+    for (int S = 0; S < 4; ++S) {
+      const v8h pb = __builtin_bit_cast(v8h, pt.w[S]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int row = 32 * cb + n;
+        const v4i a = *reinterpret_cast<const v4i*>(
+            vb + row * 128 + (((2 * S + hh) ^ row_swizzle<128>(row)) << 4));
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), pb, o[cb], 0,
+                                                       0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int row = 32 * cb + n;
+      const int sw = row_swizzle<64>(row);
+      const v4i a0 = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh) ^ sw) << 4));
+      const v4i a1 = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh + 1) ^ sw) << 4));
+      const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      // scale operands 127 = E8M0 exponent of 1.0 (no block scaling)
+      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pt.w, o[cb], 0, 0, 0, 127, 0, 127);
+    }
+  }
+}
+
+// Instruction order for one pipelined step: each MFMA (with its LDS operand
+// read) is followed by a slice of the softmax's vector instructions, so a
+// wavefront keeps issuing VALU work while its MFMAs execute.  The softmax
+// inputs were computed one step earlier, so the slices have no pending
+// dependency on these MFMAs.  Scheduling hints only; results are unchanged.
+template <int D, int PV>
+__device__ __forceinline__ void interleave_hint() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008, kValu = 0x002;
+  constexpr int QK_MFMA = 2 * (D / 32);
+  constexpr int PV_MFMA = PV == kPvFp16 ? 4 * (D / 32) : (D / 32);
+  constexpr int PV_READS = PV == kPvFp16 ? PV_MFMA : 2 * PV_MFMA;
+  constexpr int MF = QK_MFMA + PV_MFMA;
+  constexpr int RD = QK_MFMA + PV_READS;
+  constexpr int VALU_PER = (PV == kPvFp16 ? 150 : 130) / MF;
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kDsRead, (RD + MF - 1) / MF, 0);
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kValu, VALU_PER, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void rescale(v16f (&o)[D / 32], float alpha) {
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) o[cb] *= alpha;
+  }
+}
+
+// Software pipeline over the KV tiles of one workgroup (4 wavefronts), two
+// tiles deep.  Entering step j a wavefront holds P~(j) (MFMA operand) and the
+// INT32 scores S(j+1); step j issues
+//     S(j+2) = K^(j+2) Q^T          [INT8 MFMA]
+//     O     += P~(j) V(j)           [FP16/FP8 MFMA]
+//     softmax(S(j+1)) -> P~(j+1)    [VALU, independent of both]
+// then rescales O by alpha(j+1).  K^ tile j+3 and V tile j+1 are loaded from
+// HBM during step j and written to LDS after its compute (double buffers,
+// one barrier per step).  All wavefronts run every step of the workgroup; a
+// causal tile beyond a wavefront's last row is fully masked and changes
+// nothing.
 template <int D, int PV, int OUT, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__ k_i8,
@@ -149,7 +337,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   constexpr int KB = KTile<D>::BYTES;
   constexpr int VB = VTile<D, PV>::BYTES;
   constexpr int NCB = D / 32;   // 32-channel blocks of the output
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][KB + VB];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KB];
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][VB];
 
   // Workgroup -> (b*h, query block).
   int wg = blockIdx.x;
@@ -174,143 +363,97 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   const int lane = tid & 63;
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int qw0 = qb * kBlockQ + wave * kWaveQ;   // first query row of this wavefront
-  const int qrow = qw0 + n;                        // this lane's query row
+  const int qrow = qb * kBlockQ + wave * kWaveQ + n;   // this lane's query row
 
   const int8_t* q_bh = q_i8 + (size_t)bh * N * D;
   const int8_t* k_bh = k_i8 + (size_t)bh * N * D;
   const uint8_t* v_bh = v_t + (size_t)bh * ntiles * VB;
-  const int nkb = ntiles;   // delta_K blocks == KV tiles
-  const float* ks_bh = k_scale + (size_t)bh * nkb;
+  const float* ks_bh = k_scale + (size_t)bh * ntiles;   // one delta_K per KV tile
 
   v4i qf[D / 32];
   load_q_frag<D>(qf, q_bh, qrow, N, hh);
   const float cq = q_scale[(size_t)bh * nqb + qb] * kLog2e;
 
+  // Tiles of the workgroup; tiles [0, nt_full) need no mask for any row, the
+  // rest (ragged tail, causal diagonal) run the masked softmax.
   const int kv_end = CAUSAL ? min(N, (qb + 1) * kBlockQ) : N;
   const int nt = (kv_end + kKvTile - 1) / kKvTile;
+  const int nt_full = CAUSAL ? min(2 * qb, N / kKvTile) : N / kKvTile;
 
-  KStage<D, 256> kst;
-  VStage<D, PV, 256> vst;
-  kst.load(k_bh, 0, N, tid);
-  vst.load(v_bh, tid);
-  kst.store(smem[0], tid);
-  vst.store(smem[0] + KB, tid);
-  __syncthreads();
-
+  const KLoader<D, kWaves> kld(wave, lane);
+  using VL = VLoader<D, PV, kWaves>;
   float m_run = -__builtin_inff();
   float l_run = 0.f;
   v16f o[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) o[cb] = v16f{};
+  v16i sA[2], sB[2];
+  PTile<PV> pA, pB;
 
-  for (int j = 0; j < nt; ++j) {
-    const int key0 = j * kKvTile;
-    const bool has_next = j + 1 < nt;
-    if (has_next) {
-      kst.load(k_bh, key0 + kKvTile, N, tid);
-      vst.load(v_bh + (size_t)(j + 1) * VB, tid);
+  auto softmax_any = [&](v16i (&sc)[2], PTile<PV>& pn, int t) __attribute__((always_inline)) {
+    const float cj = cq * ks_bh[t];
+    return t < nt_full
+               ? softmax_tile<PV, CAUSAL, false>(sc, m_run, l_run, pn, cj, t * kKvTile, N, qrow, hh)
+               : softmax_tile<PV, CAUSAL, true>(sc, m_run, l_run, pn, cj, t * kKvTile, N, qrow, hh);
+  };
+
+  // Prologue: S(0), S(1), P~(0); then K^(2) into the slot of K^(0).
+  kld.template issue<true>(k_bh, 0, N, kbuf[0], wave);
+  VL::issue(v_bh, vbuf[0], wave, lane);
+  if (nt > 1) kld.template issue<true>(k_bh, kKvTile, N, kbuf[1], wave);
+  wait_lds_loads();
+  __syncthreads();
+  qk_tile<D>(sA, qf, kbuf[0], n, hh);
+  if (nt > 1) qk_tile<D>(sB, qf, kbuf[1], n, hh);
+  softmax_any(sA, pA, 0);   // alpha irrelevant: O is still zero
+  __syncthreads();          // every wave has read K^(0)
+  if (nt > 2) kld.template issue<true>(k_bh, 2 * kKvTile, N, kbuf[0], wave);
+  wait_lds_loads();
+  __syncthreads();
+
+  // Steady state: two steps per trip (static LDS slots and register roles),
+  // no masking, every load and MFMA present.  Step j writes K^(j+3) and
+  // V(j+1) into the slots read during step j-1.
+  int j = 0;
+  for (; j + 4 < nt && j + 2 < nt_full; j += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int jj = j + u;
+      kld.template issue<false>(k_bh, (jj + 3) * kKvTile, N, kbuf[1 - u], wave);
+      VL::issue(v_bh + (size_t)(jj + 1) * VB, vbuf[1 - u], wave, lane);
+      v16i(&s_cur)[2] = u == 0 ? sB : sA;
+      v16i(&s_new)[2] = u == 0 ? sA : sB;
+      PTile<PV>& p_cur = u == 0 ? pA : pB;
+      PTile<PV>& p_new = u == 0 ? pB : pA;
+      qk_tile<D>(s_new, qf, kbuf[u], n, hh);
+      pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh);
+      const float alpha = softmax_tile<PV, CAUSAL, false>(
+          s_cur, m_run, l_run, p_new, cq * ks_bh[jj + 1], (jj + 1) * kKvTile, N, qrow, hh);
+      interleave_hint<D, PV>();
+      rescale<D>(o, alpha);
+      wait_lds_loads();
+      __syncthreads();
     }
-    const uint8_t* kb = smem[j & 1];
-    const uint8_t* vb = kb + KB;
-    const bool active = !CAUSAL || key0 <= qw0 + (kWaveQ - 1);
-    if (active) {
-      const float cj = cq * ks_bh[j];
-      v16i s[2];
-      s[0] = qk_block<D>(qf, kb, 0, n, hh);
-      s[1] = qk_block<D>(qf, kb, 1, n, hh);
-
-      // Mask keys past N and, when causal, keys after the query.
-      const bool need_mask = (CAUSAL && key0 + kKvTile - 1 > qw0) || (key0 + kKvTile > N);
-      uint32_t keep = 0xffffffffu;   // bit 16*blk + r
-      if (need_mask) {
-        keep = 0u;
+  }
+  // Tail: the last steps, with masking and missing tiles handled explicitly.
+  for (; j < nt; j += 2) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * blk + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = key < N && (!CAUSAL || key <= qrow);
-            keep |= (uint32_t)ok << (16 * blk + r);
-            if (!ok) s[blk][r] = INT32_MIN;
-          }
-      }
-      int mx = INT32_MIN;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = max(mx, max(s[blk][r], s[blk][r + 1]));
-      mx = pair_max_i32(mx);
-      const float m_new = fmaxf(m_run, (float)mx * cj);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      const float negm = PV == kPvFp8 ? kLog2_448 - m_new : -m_new;
-
-      float p[2][16];
-      float lsum = 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[blk][r], cj, negm));
-          if (need_mask && !((keep >> (16 * blk + r)) & 1u)) e = 0.f;
-          p[blk][r] = e;
-          lsum += e;
-        }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
-      }
-
-      if constexpr (PV == kPvFp16) {
-        // B operand of step S (16 keys): registers 8*(S%2) .. +7 of block S/2.
-#pragma unroll
-        for (int S = 0; S < 4; ++S) {
-          const int blk = S >> 1, r0 = 8 * (S & 1);
-          const v4i pw = {(int)pack_f16x2(p[blk][r0 + 0], p[blk][r0 + 1]),
-                          (int)pack_f16x2(p[blk][r0 + 2], p[blk][r0 + 3]),
-                          (int)pack_f16x2(p[blk][r0 + 4], p[blk][r0 + 5]),
-                          (int)pack_f16x2(p[blk][r0 + 6], p[blk][r0 + 7])};
-          const v8h pb = __builtin_bit_cast(v8h, pw);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            const int row = 32 * cb + n;
-            const v4i a = *reinterpret_cast<const v4i*>(
-                vb + row * 128 + (((2 * S + hh) ^ row_swizzle<128>(row)) << 4));
-            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), pb, o[cb],
-                                                           0, 0, 0);
-          }
-        }
-      } else {
-        // B operand: 32 E4M3 codes, byte 16*blk + r <-> register r of block blk.
-        v8i pb;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int blk = w >> 2, r0 = 4 * (w & 3);
-          pb[w] = (int)pack_fp8x4(p[blk][r0], p[blk][r0 + 1], p[blk][r0 + 2], p[blk][r0 + 3]);
-        }
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const int row = 32 * cb + n;
-          const int sw = row_swizzle<64>(row);
-          const v4i a0 = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh) ^ sw) << 4));
-          const v4i a1 =
-              *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh + 1) ^ sw) << 4));
-          const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          // scale operands 127 = E8M0 exponent of 1.0 (no block scaling)
-          o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[cb], 0, 0, 0, 127, 0,
-                                                                  127);
-        }
+    for (int u = 0; u < 2; ++u) {
+      const int jj = j + u;
+      if (jj < nt) {
+        if (jj + 3 < nt) kld.template issue<true>(k_bh, (jj + 3) * kKvTile, N, kbuf[1 - u], wave);
+        if (jj + 1 < nt) VL::issue(v_bh + (size_t)(jj + 1) * VB, vbuf[1 - u], wave, lane);
+        v16i(&s_cur)[2] = u == 0 ? sB : sA;
+        v16i(&s_new)[2] = u == 0 ? sA : sB;
+        PTile<PV>& p_cur = u == 0 ? pA : pB;
+        PTile<PV>& p_new = u == 0 ? pB : pA;
+        if (jj + 2 < nt) qk_tile<D>(s_new, qf, kbuf[u], n, hh);
+        pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh);
+        if (jj + 1 < nt) rescale<D>(o, softmax_any(s_cur, p_new, jj + 1));
+        wait_lds_loads();
+        __syncthreads();
       }
     }
-    if (has_next) {
-      uint8_t* nb = smem[(j + 1) & 1];
-      kst.store(nb, tid);
-      vst.store(nb + KB, tid);
-    }
-    __syncthreads();
   }
 
   // Epilogue: O = O / l (FP8: l is in units of 448 P~, and delta_V per channel).
@@ -349,9 +492,9 @@ __global__ __launch_bounds__(64) void debug_s_kernel(const int8_t* __restrict__ 
   const int kbase = k0 + 64 * blockIdx.y;
   v4i qf[D / 32];
   load_q_frag<D>(qf, q_bh, qbase + n, N, hh);
-  KStage<D, 64> kst;
-  kst.load(k_bh, kbase, N, lane);
-  kst.store(kb, lane);
+  const KLoader<D, 1> kld(0, lane);
+  kld.template issue<true>(k_bh, kbase, N, kb, 0);
+  wait_lds_loads();
   __syncthreads();
   const int query = qbase + n;
 #pragma unroll

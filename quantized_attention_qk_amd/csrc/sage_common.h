@@ -50,13 +50,16 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return (uint32_t)w;
 }
 
-// LDS swizzles: the 16-byte chunk `k` of row `r` is stored at chunk k ^ swz(r),
-// so that the 8 lanes served together by a ds_read_b128 (consecutive rows,
-// same logical chunk) hit distinct bank groups.
+// LDS swizzles.  gfx950's LDS serves a ds_read_b128 sixteen lanes at a time
+// (256 bytes = all 64 banks).  The 16-byte chunk `k` of row `r` is stored at
+// chunk k ^ swz(r): for 128-byte rows, rows r and r+1 share a 256-byte bank
+// window, so swz(r) = (r / 2) % 8 makes the 16 lanes of a group (16
+// consecutive rows, same logical chunk) hit 16 distinct 16-byte bank groups;
+// for 64-byte rows, four rows share a window and swz(r) = (r / 4) % 4.
 template <int ROW_BYTES>
 __device__ __forceinline__ int row_swizzle(int r) {
-  if constexpr (ROW_BYTES >= 128) return r & 7;
-  else if constexpr (ROW_BYTES == 64) return (r >> 1) & 3;
+  if constexpr (ROW_BYTES >= 128) return (r >> 1) & 7;
+  else if constexpr (ROW_BYTES == 64) return (r >> 2) & 3;
   else return 0;
 }
 

@@ -146,7 +146,7 @@ def test_untile_v_inverts_documented_layout():
                     for kk in range(8):
                         for e in range(8):
                             key = 64 * t + 16 * (kk // 2) + 8 * (e // 4) + 4 * (kk % 2) + e % 4
-                            tiled[0, :, t, c, kk ^ (c % 8), e] = nat[0, :, key, c]
+                            tiled[0, :, t, c, kk ^ ((c // 2) % 8), e] = nat[0, :, key, c]
             raw = tiled.view(np.uint8).ravel()
         else:
             nat = (nat % 251).astype(np.uint8)
@@ -155,7 +155,7 @@ def test_untile_v_inverts_documented_layout():
                 for c in range(d):
                     for p in range(64):
                         key = 64 * t + 32 * ((p // 16) % 2) + 8 * ((p % 16) // 4) + 4 * (p // 32) + p % 4
-                        phys = 16 * ((p // 16) ^ ((c // 2) % 4)) + p % 16
+                        phys = 16 * ((p // 16) ^ ((c // 4) % 4)) + p % 16
                         tiled[0, :, t, c, phys] = nat[0, :, key, c]
             raw = tiled.ravel()
         assert raw.size == B * H * nt * d * rowb
