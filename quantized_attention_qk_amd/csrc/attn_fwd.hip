@@ -32,6 +32,7 @@
 // * The output rescale by alpha is skipped when no row of the wavefront has a
 //   new maximum (alpha == 1 exactly), which is bit-identical.
 #include <type_traits>
+#include <utility>
 
 #include "sage_common.h"
 #include "sage_launch.h"
@@ -85,10 +86,23 @@ __device__ __forceinline__ v16i qk_block(const v4i (&qf)[D / 32], const uint8_t*
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// HBM -> LDS copies with global_load_lds_dwordx4: every lane moves 16 bytes
-// straight into LDS (no VGPR staging); a wavefront writes 1 KiB contiguous
-// LDS bytes per instruction, so the K^ row swizzle is applied by choosing
-// each lane's source address.  NW wavefronts share the work.
+// Raw buffer resource for gfx9: base address, stride 0, byte-addressed
+// records, default data format word.
+constexpr int kBufferFlags = 0x00020000;
+__device__ __forceinline__ v4i buffer_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+             __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)), bytes, kBufferFlags};
+}
+// buffer_load_dword* ... lds (the LLVM intrinsic, with a v4i32 resource).
+__device__ void raw_buffer_load_lds(v4i rsrc, lds_void* lds, int size, int voffset, int soffset,
+                                    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// HBM -> LDS copies with buffer_load_dwordx4 ... lds: every lane moves 16
+// bytes straight into LDS (no VGPR staging, scalar base and LDS address, one
+// 32-bit lane offset); a wavefront writes 1 KiB of contiguous LDS per
+// instruction, so the K^ row swizzle is applied by choosing each lane's
+// source offset.  NW wavefronts share the work; `wave` must be uniform.
 template <int D, int NW>
 struct KLoader {
   static constexpr int PER = KTile<D>::CHUNKS / (64 * NW);
@@ -103,16 +117,22 @@ struct KLoader {
       off[i] = row[i] * D + kc * 16;
     }
   }
-  // Rows at or beyond N re-read row N-1 (their scores are masked).
+  // k_bh: the head's K^ (N*D bytes).  Rows at or beyond N re-read row N-1
+  // (their scores are masked).
   template <bool CLAMP>
-  __device__ __forceinline__ void issue(const int8_t* __restrict__ k_bh, int key0, int N,
-                                        uint8_t* kb, int wave) const {
+  __device__ __forceinline__ void issue(const int8_t* k_bh, int key0, int N, uint8_t* kb,
+                                        int wave) const {
+    const v4i rs = buffer_rsrc(k_bh, N * D);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int8_t* src = k_bh + (size_t)key0 * D + off[i];
-      if constexpr (CLAMP)
-        if (key0 + row[i] >= N) src = k_bh + (size_t)(N - 1) * D + (off[i] - row[i] * D);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(kb + (i * NW + wave) * 1024), 16, 0, 0);
+      lds_void* dst = (lds_void*)(kb + (i * NW + wave) * 1024);
+      if constexpr (CLAMP) {
+        const int r = min(key0 + row[i], N - 1);
+        raw_buffer_load_lds(rs, dst, 16, r * D + (off[i] - row[i] * D), 0,
+                                                 0, 0);
+      } else {
+        raw_buffer_load_lds(rs, dst, 16, off[i], key0 * D, 0, 0);
+      }
     }
   }
 };
@@ -122,13 +142,15 @@ template <int D, int PV, int NW>
 struct VLoader {
   static constexpr int PER = VTile<D, PV>::CHUNKS / (64 * NW);
   static_assert(PER * 64 * NW == VTile<D, PV>::CHUNKS, "wavefronts must tile the V tile");
-  __device__ __forceinline__ static void issue(const uint8_t* __restrict__ vtile, uint8_t* vb,
-                                               int wave, int lane) {
+  // v_bh: the head's prepared V (ntiles tiles); tile t starts at t * VTile::BYTES.
+  __device__ __forceinline__ static void issue(const uint8_t* v_bh, int ntiles, int tile,
+                                               uint8_t* vb, int wave, int lane) {
+    const v4i rs = buffer_rsrc(v_bh, ntiles * VTile<D, PV>::BYTES);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int P = (i * NW + wave) * 64 + lane;
-      __builtin_amdgcn_global_load_lds(vtile + (size_t)P * 16,
-                                       (lds_void*)(vb + (i * NW + wave) * 1024), 16, 0, 0);
+      raw_buffer_load_lds(rs, (lds_void*)(vb + (i * NW + wave) * 1024), 16,
+                                               P * 16, tile * VTile<D, PV>::BYTES, 0, 0);
     }
   }
 };
@@ -287,26 +309,185 @@ __device__ __forceinline__ void pv_tile(v16f (&o)[D / 32], const PTile<PV>& pt,
   }
 }
 
-// Instruction order for one pipelined step: each MFMA (with its LDS operand
-// read) is followed by a slice of the softmax's vector instructions, so a
-// wavefront keeps issuing VALU work while its MFMAs execute.  The softmax
-// inputs were computed one step earlier, so the slices have no pending
-// dependency on these MFMAs.  Scheduling hints only; results are unchanged.
+// ---------------------------------------------------------------------------
+// The steady-state step as an explicit instruction schedule.
+//
+// A step issues NQK INT8 MFMAs (S(j+2)) and NPV P~V MFMAs (tile j), and runs
+// the softmax of S(j+1), whose scores were produced one step earlier.  The
+// MFMAs are spread over "slots"; every slot issues one MFMA (its LDS operand
+// was read two slots earlier) followed by a slice of the softmax's vector
+// micro-ops, and slots are separated by scheduling barriers.  Each wavefront
+// thus alternates MFMA and VALU issue, keeping both units busy.  The order
+// only affects timing: the arithmetic is the same as softmax_tile/qk_tile/
+// pv_tile (unmasked tiles only).
 template <int D, int PV>
-__device__ __forceinline__ void interleave_hint() {
-  constexpr int kDsRead = 0x100, kMfma = 0x008, kValu = 0x002;
-  constexpr int QK_MFMA = 2 * (D / 32);
-  constexpr int PV_MFMA = PV == kPvFp16 ? 4 * (D / 32) : (D / 32);
-  constexpr int PV_READS = PV == kPvFp16 ? PV_MFMA : 2 * PV_MFMA;
-  constexpr int MF = QK_MFMA + PV_MFMA;
-  constexpr int RD = QK_MFMA + PV_READS;
-  constexpr int VALU_PER = (PV == kPvFp16 ? 150 : 130) / MF;
-#pragma unroll
-  for (int i = 0; i < MF; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kDsRead, (RD + MF - 1) / MF, 0);
-    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kValu, VALU_PER, 0);
+struct StepPlan {
+  static constexpr int TD = D / 32;                              // d-steps per QK block
+  static constexpr int NCB = D / 32;                             // output channel blocks
+  static constexpr int NQK = 2 * TD;
+  static constexpr int NPV = PV == kPvFp16 ? 4 * NCB : NCB;
+  static constexpr int NM = NQK + NPV;                           // MFMA slots
+  // slot k issues a P~V MFMA iff the running PV quota steps up at k
+  static constexpr bool is_pv(int k) { return ((k + 1) * NPV) / NM > (k * NPV) / NM; }
+  static constexpr int index(int k) {   // index of the MFMA among its kind
+    int c = 0;
+    for (int i = 0; i < k; ++i) c += is_pv(i) == is_pv(k);
+    return c;
   }
+  // softmax micro-ops: 0..47 max/convert, 48 combine, then exp and pack, then finish
+  static constexpr int NPACK = PV == kPvFp16 ? 16 : 8;
+  static constexpr int NU = 48 + 1 + 32 + NPACK + 1;
+  // first micro-op of slot k (cumulative instruction weight, spread evenly)
+  static constexpr int weight(int u) {
+    return u < 48 ? 1 : u == 48 ? 10 : u < 49 + 32 + NPACK ? 2 : 3;
+  }
+  static constexpr int total_weight() {
+    int w = 0;
+    for (int u = 0; u < NU; ++u) w += weight(u);
+    return w;
+  }
+  static constexpr int first_uop(int k) {
+    const int target = (k * total_weight()) / NM;
+    int w = 0, u = 0;
+    while (u < NU && w + weight(u) / 2 < target) w += weight(u++);
+    return u;
+  }
+};
+
+template <int D, int PV>
+using OpReg = std::conditional_t<PV == kPvFp16, v4i, v8i>;
+
+template <int D, int PV>
+__device__ __forceinline__ float fused_step(v16f (&o)[D / 32], const v4i (&qf)[D / 32],
+                                            v16i (&s_cur)[2], v16i (&s_new)[2],
+                                            const PTile<PV>& p_cur, PTile<PV>& p_new,
+                                            const uint8_t* kb, const uint8_t* vb, float& m_run,
+                                            float& l_run, float cj, int n, int hh) {
+  using Plan = StepPlan<D, PV>;
+  using Op = OpReg<D, PV>;
+  constexpr int LA = 2;   // operand read lookahead (slots)
+  Op ops[LA + 1];
+
+  // ---- MFMA side
+  auto read_op = [&]<int K>() __attribute__((always_inline)) {
+    Op& r = ops[K % (LA + 1)];
+    constexpr int i = Plan::index(K);
+    if constexpr (!Plan::is_pv(K)) {
+      constexpr int blk = i % 2, t = i / 2;
+      const v4i a = *reinterpret_cast<const v4i*>(kb + KTile<D>::lds_off(32 * blk + n, 2 * t + hh));
+      if constexpr (PV == kPvFp16) r = a;
+      else r = Op{a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+    } else if constexpr (PV == kPvFp16) {
+      constexpr int S = i / Plan::NCB, cb = i % Plan::NCB;
+      const int row = 32 * cb + n;
+      r = *reinterpret_cast<const v4i*>(vb + row * 128 +
+                                        (((2 * S + hh) ^ row_swizzle<128>(row)) << 4));
+    } else {
+      constexpr int cb = i;
+      const int row = 32 * cb + n;
+      const int sw = row_swizzle<64>(row);
+      const v4i a0 = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh) ^ sw) << 4));
+      const v4i a1 = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh + 1) ^ sw) << 4));
+      r = Op{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    }
+  };
+  auto do_mfma = [&]<int K>() __attribute__((always_inline)) {
+    const Op& r = ops[K % (LA + 1)];
+    constexpr int i = Plan::index(K);
+    if constexpr (!Plan::is_pv(K)) {
+      constexpr int blk = i % 2, t = i / 2;
+      v4i a;
+      if constexpr (PV == kPvFp16) a = r;
+      else a = v4i{r[0], r[1], r[2], r[3]};
+      s_new[blk] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[t], t == 0 ? v16i{} : s_new[blk],
+                                                          0, 0, 0);
+    } else if constexpr (PV == kPvFp16) {
+      constexpr int S = i / Plan::NCB, cb = i % Plan::NCB;
+      o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, r),
+                                                     __builtin_bit_cast(v8h, p_cur.w[S]), o[cb],
+                                                     0, 0, 0);
+    } else {
+      constexpr int cb = i;
+      // scale operands 127 = E8M0 exponent of 1.0 (no block scaling)
+      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(r, p_cur.w, o[cb], 0, 0, 0, 127,
+                                                              0, 127);
+    }
+  };
+
+  // ---- softmax side (same arithmetic as softmax_tile, unmasked)
+  int mpart[4];
+  float f[32], e[32];
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+  float m_new = 0.f, alpha = 1.f, negm = 0.f;
+  auto sc = [&](int i) __attribute__((always_inline)) -> int { return s_cur[i >> 4][i & 15]; };
+  auto uop = [&]<int U>() __attribute__((always_inline)) {
+    if constexpr (U < 48) {
+      // triples: max of two scores into one of 4 partial maxima, and a convert
+      constexpr int g = U / 3, r = U % 3;
+      if constexpr (r == 0) {
+        const int v = max(sc(2 * g), sc(2 * g + 1));
+        mpart[g & 3] = g < 4 ? v : max(mpart[g & 3], v);
+      } else {
+        f[2 * g + r - 1] = (float)sc(2 * g + r - 1);
+      }
+    } else if constexpr (U == 48) {
+      int mx = max(max(mpart[0], mpart[1]), max(mpart[2], mpart[3]));
+      mx = pair_max_i32(mx);
+      const float mt = (float)mx * cj;
+      if constexpr (PV == kPvFp16) m_new = mt > m_run + kLazyMax ? mt : m_run;
+      else m_new = fmaxf(m_run, mt);
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      negm = PV == kPvFp8 ? kLog2_448 - m_new : -m_new;
+    } else if constexpr (U < 49 + 32 + Plan::NPACK) {
+      // exp of score i, and after every 2 (FP16) / 4 (FP8) scores their pack
+      constexpr int v = U - 49;
+      constexpr int per = PV == kPvFp16 ? 3 : 5;   // 2 exps + pack, or 4 exps + pack
+      constexpr int grp = v / per, pos = v % per;
+      constexpr int nper = per - 1;
+      if constexpr (pos < nper) {
+        constexpr int i = grp * nper + pos;
+        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[i], cj, negm));
+        if constexpr (PV == kPvFp8) ls[i & 3] += e[i];
+      } else if constexpr (PV == kPvFp16) {
+        constexpr int w = grp;   // pair (2w, 2w+1) -> step w/4, element w%4
+        uint32_t pk = pack_f16x2(e[2 * w], e[2 * w + 1]);
+        // pin: keep this micro-op in its slot (otherwise the backend sinks
+        // the softmax below the rescale branch, out of the MFMA slots)
+        asm volatile("" : "+v"(pk));
+        p_new.w[w >> 2][w & 3] = (int)pk;
+        const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
+        ls[w & 3] = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, pk), one, ls[w & 3], false);
+      } else {
+        constexpr int w = grp;
+        uint32_t pk = pack_fp8x4(e[4 * w], e[4 * w + 1], e[4 * w + 2], e[4 * w + 3]);
+        asm volatile("" : "+v"(pk));
+        p_new.w[w] = (int)pk;
+      }
+    } else {
+      l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
+      m_run = m_new;
+      asm volatile("" : "+v"(l_run));
+    }
+  };
+  auto uops = [&]<int U0, int U1>() __attribute__((always_inline)) {
+    [&]<int... U>(std::integer_sequence<int, U...>) __attribute__((always_inline)) {
+      (uop.template operator()<U0 + U>(), ...);
+    }(std::make_integer_sequence<int, U1 - U0>{});
+  };
+
+  // ---- the schedule
+  read_op.template operator()<0>();
+  read_op.template operator()<1>();
+  [&]<int... K>(std::integer_sequence<int, K...>) __attribute__((always_inline)) {
+    ([&]() __attribute__((always_inline)) {
+      if constexpr (K + LA < Plan::NM) read_op.template operator()<K + LA>();
+      do_mfma.template operator()<K>();
+      uops.template operator()<Plan::first_uop(K), Plan::first_uop(K + 1)>();
+      __builtin_amdgcn_sched_barrier(0);
+    }(), ...);
+  }(std::make_integer_sequence<int, Plan::NM>{});
+  uops.template operator()<Plan::first_uop(Plan::NM), Plan::NU>();
+  return alpha;
 }
 
 template <int D>
@@ -359,7 +540,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   }
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
   const int lane = tid & 63;
   const int n = lane & 31;
   const int hh = lane >> 5;
@@ -399,7 +580,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
 
   // Prologue: S(0), S(1), P~(0); then K^(2) into the slot of K^(0).
   kld.template issue<true>(k_bh, 0, N, kbuf[0], wave);
-  VL::issue(v_bh, vbuf[0], wave, lane);
+  VL::issue(v_bh, ntiles, 0, vbuf[0], wave, lane);
   if (nt > 1) kld.template issue<true>(k_bh, kKvTile, N, kbuf[1], wave);
   wait_lds_loads();
   __syncthreads();
@@ -420,16 +601,13 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     for (int u = 0; u < 2; ++u) {
       const int jj = j + u;
       kld.template issue<false>(k_bh, (jj + 3) * kKvTile, N, kbuf[1 - u], wave);
-      VL::issue(v_bh + (size_t)(jj + 1) * VB, vbuf[1 - u], wave, lane);
+      VL::issue(v_bh, ntiles, jj + 1, vbuf[1 - u], wave, lane);
       v16i(&s_cur)[2] = u == 0 ? sB : sA;
       v16i(&s_new)[2] = u == 0 ? sA : sB;
       PTile<PV>& p_cur = u == 0 ? pA : pB;
       PTile<PV>& p_new = u == 0 ? pB : pA;
-      qk_tile<D>(s_new, qf, kbuf[u], n, hh);
-      pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh);
-      const float alpha = softmax_tile<PV, CAUSAL, false>(
-          s_cur, m_run, l_run, p_new, cq * ks_bh[jj + 1], (jj + 1) * kKvTile, N, qrow, hh);
-      interleave_hint<D, PV>();
+      const float alpha = fused_step<D, PV>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[u], vbuf[u],
+                                            m_run, l_run, cq * ks_bh[jj + 1], n, hh);
       rescale<D>(o, alpha);
       wait_lds_loads();
       __syncthreads();
@@ -442,7 +620,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
       const int jj = j + u;
       if (jj < nt) {
         if (jj + 3 < nt) kld.template issue<true>(k_bh, (jj + 3) * kKvTile, N, kbuf[1 - u], wave);
-        if (jj + 1 < nt) VL::issue(v_bh + (size_t)(jj + 1) * VB, vbuf[1 - u], wave, lane);
+        if (jj + 1 < nt) VL::issue(v_bh, ntiles, jj + 1, vbuf[1 - u], wave, lane);
         v16i(&s_cur)[2] = u == 0 ? sB : sA;
         v16i(&s_new)[2] = u == 0 ? sA : sB;
         PTile<PV>& p_cur = u == 0 ? pA : pB;
