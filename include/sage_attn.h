@@ -166,6 +166,20 @@ int sage_attn_fwd_quantized(const int8_t* q_i8, const int8_t* k_i8, const void* 
                             int out_dtype, void* stream);
 
 /*
+ * Full-precision reference for selected query rows: float32 softmax
+ * attention O[b,h,i,:] = softmax(q_i K^T / sqrt(d)) V (causal: keys <= i) with
+ * no quantisation, for every (b, h) and every row index in `rows` (device
+ * int32 [nrows]).  o: float32 [B,H,nrows,d].  A row index outside [0, N)
+ * yields NaN outputs for that row (nothing is read for it).  This is the
+ * reference against which a layer's quantised output is profiled when the
+ * P~V precision is chosen per layer by cosine similarity ([SA] §2 Q2 item 3:
+ * layers above 99.8% use the faster kernel).
+ */
+int sage_attn_ref_rows_f32(const void* q, const void* k, const void* v, int dtype, int B, int H,
+                           int N, int d, int causal, const int32_t* rows, int nrows, float* o,
+                           void* stream);
+
+/*
  * Debug: the INT32 product S = Q^ K^T of one (b, h) on the rectangle
  * queries [q0, q0+nq) x keys [k0, k0+nk), computed by the same device code
  * (operand staging, LDS layout, INT8 MFMA tile) as the attention kernel.

@@ -31,6 +31,7 @@ _SIGNATURES = {
     "sage_quant_v_scratch_bytes": (_c_size, [_c_int] * 5),
     "sage_quant_v": (_c_int, [_vp] + [_c_int] * 6 + [_vp, _vp, _vp, _c_size, _vp]),
     "sage_attn_fwd_quantized": (_c_int, [_vp] * 7 + [_c_int] * 7 + [_vp]),
+    "sage_attn_ref_rows_f32": (_c_int, [_vp] * 3 + [_c_int] * 6 + [_vp, _c_int, _vp, _vp]),
     "sage_attn_debug_s_i32": (_c_int, [_vp, _vp] + [_c_int] * 10 + [_vp, _vp]),
 }
 

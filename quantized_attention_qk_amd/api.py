@@ -11,7 +11,7 @@ import torch
 
 from ._lib import SAGE_DT, SAGE_PV, check, lib
 
-__all__ = ["sage_attn", "sage_attn_quantized", "smooth_quant_qk", "quant_v", "debug_s_i32", "tiling",
+__all__ = ["sage_attn", "sage_attn_quantized", "ref_rows", "smooth_quant_qk", "quant_v", "debug_s_i32", "tiling",
            "workspace_bytes", "untile_v"]
 
 
@@ -126,6 +126,20 @@ def sage_attn_quantized(qk: dict, v_prep: torch.Tensor, v_scale: torch.Tensor | 
         qk["k_scale"].data_ptr(), v_scale.data_ptr() if v_scale is not None else None,
         out.data_ptr(), B, H, N, d, int(causal), SAGE_PV[pv_mode], odt,
         _stream_ptr(q_i8.device)), "sage_attn_fwd_quantized")
+    return out
+
+
+def ref_rows(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rows: torch.Tensor,
+             causal: bool = False) -> torch.Tensor:
+    """Float32 softmax attention (no quantisation) on the query rows `rows`
+    of every (b, h): returns [B, H, len(rows), d] float32."""
+    B, H, N, d = _check_qkv(q, k, v)
+    rows = rows.to(device=q.device, dtype=torch.int32).contiguous()
+    out = torch.empty((B, H, rows.numel(), d), dtype=torch.float32, device=q.device)
+    check(lib().sage_attn_ref_rows_f32(q.data_ptr(), k.data_ptr(), v.data_ptr(), SAGE_DT[q.dtype],
+                                       B, H, N, d, int(causal), rows.data_ptr(), rows.numel(),
+                                       out.data_ptr(), _stream_ptr(q.device)),
+          "sage_attn_ref_rows_f32")
     return out
 
 

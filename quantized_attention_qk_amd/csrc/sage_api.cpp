@@ -267,6 +267,23 @@ int sage_attn_fwd_quantized(const int8_t* q_i8, const int8_t* k_i8, const void* 
                                       o, static_cast<hipStream_t>(stream)));
 }
 
+int sage_attn_ref_rows_f32(const void* q, const void* k, const void* v, int dtype, int B, int H,
+                           int N, int d, int causal, const int32_t* rows, int nrows, float* o,
+                           void* stream) {
+  if (!q || !k || !v || !rows || !o) return SAGE_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (reinterpret_cast<uintptr_t>(rows) & 3u) ||
+      (reinterpret_cast<uintptr_t>(o) & 3u))
+    return SAGE_ERR_INVALID_ARG;
+  if (dtype != SAGE_DT_F16 && dtype != SAGE_DT_BF16) return SAGE_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || nrows < 1) return SAGE_ERR_INVALID_ARG;
+  if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
+  int st = device_check();
+  if (st != SAGE_OK) return st;
+  return hip_status(sage::launch_ref_rows(q, k, v, dtype, B, H, N, d, causal, rows, nrows, o,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int sage_attn_debug_s_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
                           int b, int h, int q0, int nq, int k0, int nk, int32_t* s_out,
                           void* stream) {

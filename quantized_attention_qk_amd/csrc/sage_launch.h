@@ -53,6 +53,11 @@ hipError_t launch_attn(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_
                        int H, int N, int d, int causal, int pv_mode, int out_kind, void* out,
                        hipStream_t s);
 
+// Float32 softmax attention on selected query rows (reference for profiling).
+hipError_t launch_ref_rows(const void* q, const void* k, const void* v, int dtype, int B, int H,
+                           int N, int d, int causal, const int32_t* rows, int nrows, float* out,
+                           hipStream_t s);
+
 // Debug: INT32 S = Q^ K^T on a rectangle of one (b, h).
 hipError_t launch_debug_s(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
                           int b, int h, int q0, int nq, int k0, int nk, int32_t* s_out,

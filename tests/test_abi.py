@@ -181,3 +181,20 @@ def test_quantized_entry_validation():
     assert h.sage_attn_fwd_quantized(*bad) == UNSUPPORTED
     if not torch.cuda.is_available():
         assert h.sage_attn_fwd_quantized(*args) == NO_DEVICE
+
+
+def test_ref_rows_validation():
+    h = lib()
+    args = [P, P, P, 0, 1, 2, 100, 64, 0, P, 5, P, None]
+    assert h.sage_attn_ref_rows_f32(*args[:9], None, *args[10:]) == INVALID    # no rows
+    bad = list(args)
+    bad[3] = 2                     # dtype
+    assert h.sage_attn_ref_rows_f32(*bad) == INVALID
+    bad = list(args)
+    bad[10] = 0                    # nrows
+    assert h.sage_attn_ref_rows_f32(*bad) == INVALID
+    bad = list(args)
+    bad[7] = 96                    # d
+    assert h.sage_attn_ref_rows_f32(*bad) == UNSUPPORTED
+    if not torch.cuda.is_available():
+        assert h.sage_attn_ref_rows_f32(*args) == NO_DEVICE

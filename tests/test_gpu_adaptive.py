@@ -1,0 +1,56 @@
+"""GPU checks of the float32 reference rows and the per-layer P~V choice.
+
+* sage_attn_ref_rows_f32 against the oracle's exact softmax attention
+  (brute_attention, float64) on the same rows: max |diff| <= 1e-5.
+* select_pv_modes keeps FP8 P~V on a benign layer (cosine above 99.8%) and
+  falls back to FP16 on the "vout" layer, whose single huge V token pushes
+  the other V values into E4M3's subnormal range (the oracle puts that
+  layer's FP8 cosine at about 0.996, its FP16 cosine at 0.999).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import make_inputs, small
+
+pytestmark = pytest.mark.gpu
+
+
+def note(msg):
+    print(f"[gpu-adaptive] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("wl", [small("r200", N=200, d=64), small("r333c", N=333, d=128, causal=True,
+                                                                  dtype="bf16", H=3)])
+def test_ref_rows_match_exact_attention(wl):
+    import quantized_attention_qk_amd as qa
+    note(f"ref rows {wl}")
+    inp = make_inputs(wl)
+    q, k, v = inp.torch_tensors("cuda")
+    rows = [0, 1, 63, 64, wl.N // 2, wl.N - 1, wl.N + 5, -1]
+    out = qa.ref_rows(q, k, v, torch.tensor(rows, dtype=torch.int32), causal=wl.causal)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    exact = oracle.brute_attention(inp.qf, inp.kf, inp.vf, causal=wl.causal)
+    for j, r in enumerate(rows):
+        if 0 <= r < wl.N:
+            np.testing.assert_allclose(got[:, :, j], exact[:, :, r], rtol=0, atol=1e-5)
+        else:
+            assert np.isnan(got[:, :, j]).all()
+
+
+def test_adaptive_choice():
+    import quantized_attention_qk_amd as qa
+    layers = {}
+    for name, extras in (("benign", "kbias4"), ("vout", "vout")):
+        wl = small(name, B=1, H=2, N=2048, d=128, dtype="bf16", extras=extras, seed=5)
+        layers[name] = make_inputs(wl).torch_tensors("cuda")
+    note("select_pv_modes benign/vout")
+    table = qa.select_pv_modes(layers, rows=256, seed=0)
+    note(f"table {table}")
+    assert table["benign"]["pv_mode"] == "fp8" and table["benign"]["cos_fp8"] > 0.9985
+    assert table["vout"]["pv_mode"] == "fp16" and table["vout"]["cos_fp8"] < 0.998

@@ -128,11 +128,16 @@ def _apply_extras(wl: Workload, rng, q, k, v):
         q[..., qch] *= np.float32(8.0)
         k += (rng.standard_normal((B, H, 1, d), dtype=np.float32) * np.float32(5.0))
     elif e == "vout":
-        # one outlier token per channel in V (~3e4): most channel values then
-        # fall far below the per-channel FP8 scale.
+        # one V token per (b, h) with value 6e4 in every channel, which queries
+        # avoid (a shared query-channel bias against a large negative key
+        # component): the per-channel FP8 V scale then pushes every other V
+        # value into E4M3's coarse subnormal range.
         N = v.shape[2]
-        tok = rng.integers(0, N, size=(B, H, 1, d))
-        np.put_along_axis(v, tok, np.float32(3.0e4), axis=2)
+        c0 = int(rng.integers(0, d))
+        t0 = int(rng.integers(0, N))
+        q[..., c0] += np.float32(5.0)
+        k[..., t0, c0] -= np.float32(60.0)
+        v[..., t0, :] = np.float32(6.0e4)
     else:
         raise ValueError(f"unknown extras recipe {e!r}")
 
