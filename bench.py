@@ -40,7 +40,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a device-to-device copy of BYTES (3 launches), to calibrate "
+                         "the HBM byte counters against a known traffic")
     return ap.parse_args()
+
+
+def copy_probe(nbytes: int):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter readings
+    give the factor between those counters and true HBM bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": src.numel() * 4, "launches": 3}), flush=True)
 
 
 def kernel_src_hash() -> str:
@@ -94,6 +109,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": args.gpus}), flush=True)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
 
