@@ -27,8 +27,10 @@
 //   tile: P~ = exp2(s * c_j - m) with c_j = delta_Q delta_K[j] log2(e).  For
 //   FP8, log2(448) is folded into the same subtraction so the MFMA operand is
 //   448 P~ directly, and l is kept in the same units.
-// * K^ and prepared-V tiles go from HBM straight into LDS (global_load_lds,
-//   double buffered, XOR-swizzled rows), one step ahead of their use.
+// * K^ and prepared-V tiles go from HBM straight into LDS (buffer_load ...
+//   lds, double buffered, XOR-swizzled rows), one step ahead of their use.
+//   The copies are issued from inline assembly: the compiler would otherwise
+//   make every LDS read of the current tiles wait for them.
 // * The output rescale by alpha is skipped when no row of the wavefront has a
 //   new maximum (alpha == 1 exactly), which is bit-identical.
 #include <type_traits>
@@ -94,9 +96,63 @@ __device__ __forceinline__ v4i buffer_rsrc(const void* base, int bytes) {
   return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
              __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)), bytes, kBufferFlags};
 }
-// buffer_load_dword* ... lds (the LLVM intrinsic, with a v4i32 resource).
-__device__ void raw_buffer_load_lds(v4i rsrc, lds_void* lds, int size, int voffset, int soffset,
-                                    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+
+// PER buffer_load_dwordx4 ... lds copies in one block: copy i writes 1 KiB
+// of LDS at m0[i] (64 lanes x 16 bytes) from byte offset voff[i] + soff of
+// the buffer rsrc.  The compiler only sees opaque code with no register
+// outputs: it does not count these loads, so a later LDS read of a
+// different tile does not wait for them; the caller waits explicitly
+// (wait_lds_loads) before the barrier that publishes the tile.  Hazards
+// handled here: an SGPR written by a vector instruction must not be read
+// by a buffer load within 5 wait states, and M0 written by a scalar move
+// must not be read by an LDS copy in the next wait state.
+// M0 is a reserved register; these kernels use it only for LDS copies, each
+// of which sets it right before use, so clobbering it here is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int PER>
+__device__ __forceinline__ void lds_copy_x4(v4i rsrc, int soff, const uint32_t (&m0)[PER],
+                                            const int (&voff)[PER]) {
+  static_assert(PER == 1 || PER == 2 || PER % 4 == 0, "copies per block");
+  if constexpr (PER > 4) {
+#pragma unroll
+    for (int g = 0; g < PER; g += 4) {
+      const uint32_t m4[4] = {m0[g], m0[g + 1], m0[g + 2], m0[g + 3]};
+      const int v4[4] = {voff[g], voff[g + 1], voff[g + 2], voff[g + 3]};
+      lds_copy_x4<4>(rsrc, soff, m4, v4);
+    }
+  } else if constexpr (PER == 1) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(m0[0]), "v"(voff[0]), "s"(rsrc), "s"(soff)
+        : "memory", "m0");
+  } else if constexpr (PER == 2) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %4, %5 offen lds\n\t"
+        "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %3, %4, %5 offen lds"
+        :
+        : "s"(m0[0]), "s"(m0[1]), "v"(voff[0]), "v"(voff[1]), "s"(rsrc), "s"(soff)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %4, %8, %9 offen lds\n\t"
+        "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %5, %8, %9 offen lds\n\t"
+        "s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %6, %8, %9 offen lds\n\t"
+        "s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %7, %8, %9 offen lds"
+        :
+        : "s"(m0[0]), "s"(m0[1]), "s"(m0[2]), "s"(m0[3]), "v"(voff[0]), "v"(voff[1]),
+          "v"(voff[2]), "v"(voff[3]), "s"(rsrc), "s"(soff)
+        : "memory", "m0");
+  }
+}
+#pragma clang diagnostic pop
 
 // HBM -> LDS copies with buffer_load_dwordx4 ... lds: every lane moves 16
 // bytes straight into LDS (no VGPR staging, scalar base and LDS address, one
@@ -123,17 +179,14 @@ struct KLoader {
   __device__ __forceinline__ void issue(const int8_t* k_bh, int key0, int N, uint8_t* kb,
                                         int wave) const {
     const v4i rs = buffer_rsrc(k_bh, N * D);
+    uint32_t m0[PER];
+    int vo[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      lds_void* dst = (lds_void*)(kb + (i * NW + wave) * 1024);
-      if constexpr (CLAMP) {
-        const int r = min(key0 + row[i], N - 1);
-        raw_buffer_load_lds(rs, dst, 16, r * D + (off[i] - row[i] * D), 0,
-                                                 0, 0);
-      } else {
-        raw_buffer_load_lds(rs, dst, 16, off[i], key0 * D, 0, 0);
-      }
+      m0[i] = __builtin_amdgcn_readfirstlane(lds_addr(kb + (i * NW + wave) * 1024));
+      vo[i] = CLAMP ? min(key0 + row[i], N - 1) * D + (off[i] - row[i] * D) : off[i];
     }
+    lds_copy_x4<PER>(rs, CLAMP ? 0 : key0 * D, m0, vo);
   }
 };
 
@@ -146,12 +199,14 @@ struct VLoader {
   __device__ __forceinline__ static void issue(const uint8_t* v_bh, int ntiles, int tile,
                                                uint8_t* vb, int wave, int lane) {
     const v4i rs = buffer_rsrc(v_bh, ntiles * VTile<D, PV>::BYTES);
+    uint32_t m0[PER];
+    int vo[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int P = (i * NW + wave) * 64 + lane;
-      raw_buffer_load_lds(rs, (lds_void*)(vb + (i * NW + wave) * 1024), 16,
-                                               P * 16, tile * VTile<D, PV>::BYTES, 0, 0);
+      m0[i] = __builtin_amdgcn_readfirstlane(lds_addr(vb + (i * NW + wave) * 1024));
+      vo[i] = ((i * NW + wave) * 64 + lane) * 16;
     }
+    lds_copy_x4<PER>(rs, tile * VTile<D, PV>::BYTES, m0, vo);
   }
 };
 
