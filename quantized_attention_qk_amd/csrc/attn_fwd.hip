@@ -72,11 +72,12 @@ __device__ __forceinline__ void load_q_frag(v4i (&qf)[D / 32], const int8_t* __r
     qf[t] = qrow < N ? *reinterpret_cast<const v4i*>(qp + 32 * t) : v4i{0, 0, 0, 0};
 }
 
-// One 32-key x 32-query block of S^T (INT32) from the K^ tile in LDS.
+// One 32-key x 32-query block of S^T (INT32) from the K^ tile in LDS,
+// accumulated onto `init` (zero, or the magic bias of FP16 mode).
 template <int D>
 __device__ __forceinline__ v16i qk_block(const v4i (&qf)[D / 32], const uint8_t* kb, int blk,
-                                         int n, int hh) {
-  v16i acc = {};
+                                         int n, int hh, const v16i& init) {
+  v16i acc = init;
   const int row = 32 * blk + n;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
@@ -173,17 +174,16 @@ struct KLoader {
       off[i] = row[i] * D + kc * 16;
     }
   }
-  // k_bh: the head's K^ (N*D bytes).  Rows at or beyond N re-read row N-1
-  // (their scores are masked).
+  // rs: buffer resource of the head's K^ (N*D bytes); kb: LDS byte address of
+  // the tile slot.  Rows at or beyond N re-read row N-1 (their scores are
+  // masked).
   template <bool CLAMP>
-  __device__ __forceinline__ void issue(const int8_t* k_bh, int key0, int N, uint8_t* kb,
-                                        int wave) const {
-    const v4i rs = buffer_rsrc(k_bh, N * D);
+  __device__ __forceinline__ void issue(v4i rs, int key0, int N, uint32_t kb, int wave) const {
     uint32_t m0[PER];
     int vo[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      m0[i] = __builtin_amdgcn_readfirstlane(lds_addr(kb + (i * NW + wave) * 1024));
+      m0[i] = kb + (i * NW + wave) * 1024;
       vo[i] = CLAMP ? min(key0 + row[i], N - 1) * D + (off[i] - row[i] * D) : off[i];
     }
     lds_copy_x4<PER>(rs, CLAMP ? 0 : key0 * D, m0, vo);
@@ -195,15 +195,14 @@ template <int D, int PV, int NW>
 struct VLoader {
   static constexpr int PER = VTile<D, PV>::CHUNKS / (64 * NW);
   static_assert(PER * 64 * NW == VTile<D, PV>::CHUNKS, "wavefronts must tile the V tile");
-  // v_bh: the head's prepared V (ntiles tiles); tile t starts at t * VTile::BYTES.
-  __device__ __forceinline__ static void issue(const uint8_t* v_bh, int ntiles, int tile,
-                                               uint8_t* vb, int wave, int lane) {
-    const v4i rs = buffer_rsrc(v_bh, ntiles * VTile<D, PV>::BYTES);
+  // rs: buffer resource of the head's prepared V (tile t starts at
+  // t * VTile::BYTES); vb: LDS byte address of the tile slot.
+  __device__ __forceinline__ static void issue(v4i rs, int tile, uint32_t vb, int wave, int lane) {
     uint32_t m0[PER];
     int vo[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      m0[i] = __builtin_amdgcn_readfirstlane(lds_addr(vb + (i * NW + wave) * 1024));
+      m0[i] = vb + (i * NW + wave) * 1024;
       vo[i] = ((i * NW + wave) * 64 + lane) * 16;
     }
     lds_copy_x4<PER>(rs, tile * VTile<D, PV>::BYTES, m0, vo);
@@ -242,9 +241,41 @@ struct PTile<kPvFp8> {
 // S^T = K^ Q^T for one 64-key tile: two 32x32 INT32 blocks.
 template <int D>
 __device__ __forceinline__ void qk_tile(v16i (&s)[2], const v4i (&qf)[D / 32], const uint8_t* kb,
-                                        int n, int hh) {
-  s[0] = qk_block<D>(qf, kb, 0, n, hh);
-  s[1] = qk_block<D>(qf, kb, 1, n, hh);
+                                        int n, int hh, const v16i& init) {
+  s[0] = qk_block<D>(qf, kb, 0, n, hh, init);
+  s[1] = qk_block<D>(qf, kb, 1, n, hh, init);
+}
+
+// FP16 mode converts scores to float without an instruction: the INT32
+// accumulation starts from the bit pattern of 1.5 * 2^23, so the accumulator
+// read as a float is exactly 1.5 * 2^23 + s (|s| <= 127^2 d < 2^22 keeps it in
+// the binade where the float spacing is 1).  With c = delta_Q delta_K log2(e)
+// rounded to 21 significant bits, K0 = 1.5 * 2^23 * c is exact, and the
+// exponent argument s c - m becomes one fused multiply-add
+// fma(x, c, -(K0 + m)); the running max m is kept on a grid of twice the
+// float spacing at the workgroup's largest K0, which makes K0 + m exact, so
+// the argument is the correctly rounded s c - m as before.
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+
+// Grid of the FP16-mode running max: step (a power of two) and 1/step.
+struct MaxGrid {
+  float step, inv;
+};
+
+struct TileScale {
+  float c;    // delta_Q delta_K log2(e) (FP16 mode: rounded to 21 significant bits)
+  float k0;   // FP16 mode: kMagic * c (exact); unused in FP8 mode
+};
+
+template <int PV>
+__device__ __forceinline__ TileScale tile_scale(float cq, float dk) {
+  if constexpr (PV == kPvFp16) {
+    const float c = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, cq * dk) & ~7u);
+    return TileScale{c, kMagic * c};
+  } else {
+    return TileScale{cq * dk, 0.f};
+  }
 }
 
 // In FP16 mode the running max used for P~ is refreshed only when a tile's max
@@ -260,8 +291,9 @@ constexpr float kLazyMax = 8.0f;
 // state unchanged (P~ = 0, alpha = 1).
 template <int PV, bool CAUSAL, bool MASK>
 __device__ __forceinline__ float softmax_tile(v16i (&s)[2], float& m_run, float& l_run,
-                                              PTile<PV>& pt, float cj, int key0, int N, int qrow,
-                                              int hh) {
+                                              PTile<PV>& pt, TileScale ts, MaxGrid grid, int key0,
+                                              int N, int qrow, int hh) {
+  constexpr bool F16 = PV == kPvFp16;
   uint32_t keep = 0xffffffffu;   // bit 16*blk + r: key visible
   if constexpr (MASK) {
     keep = 0u;
@@ -272,20 +304,27 @@ __device__ __forceinline__ float softmax_tile(v16i (&s)[2], float& m_run, float&
         const int key = key0 + 32 * blk + 8 * (r >> 2) + 4 * hh + (r & 3);
         const bool ok = key < N && (!CAUSAL || key <= qrow);
         keep |= (uint32_t)ok << (16 * blk + r);
-        if (!ok) s[blk][r] = INT32_MIN;
+        // FP16: the biased scores are positive floats, 0 is below all of them
+        if (!ok) s[blk][r] = F16 ? 0 : INT32_MIN;
       }
   }
   // row max: chain of 3-input maxima over the lane's 32 scores, then the pair
+  // (in FP16 mode on the bit patterns of positive floats, which order alike)
   int mx = max(s[0][0], s[0][1]);
 #pragma unroll
   for (int i = 2; i < 32; i += 2) mx = max(mx, max(s[i >> 4][i & 15], s[i >> 4][(i & 15) + 1]));
   mx = pair_max_i32(mx);
-  const float mt = (float)mx * cj;
-  float m_new;
-  if constexpr (PV == kPvFp16) m_new = mt > m_run + kLazyMax ? mt : m_run;
-  else m_new = fmaxf(m_run, mt);
+  float m_new, nb;
+  if constexpr (F16) {
+    const float mt = (__builtin_bit_cast(float, mx) - kMagic) * ts.c;
+    m_new = mt > m_run + kLazyMax ? __builtin_ceilf(mt * grid.inv) * grid.step : m_run;
+    nb = -(ts.k0 + m_new);
+  } else {
+    const float mt = (float)mx * ts.c;
+    m_new = fmaxf(m_run, mt);
+    nb = kLog2_448 - m_new;
+  }
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-  const float negm = PV == kPvFp8 ? kLog2_448 - m_new : -m_new;
 
   float p[2][16];
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
@@ -293,13 +332,17 @@ __device__ __forceinline__ float softmax_tile(v16i (&s)[2], float& m_run, float&
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float e = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[blk][r], cj, negm));
+      // copy the element to a scalar first: clang mis-lowers a bit_cast
+      // whose operand is an ext_vector element (it reads element 0)
+      const int si = s[blk][r];
+      const float x = F16 ? __builtin_bit_cast(float, si) : (float)si;
+      float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x, ts.c, nb));
       if constexpr (MASK) e = ((keep >> (16 * blk + r)) & 1u) ? e : 0.f;
       p[blk][r] = e;
-      if constexpr (PV == kPvFp8) ls[r & 3] += e;
+      if constexpr (!F16) ls[r & 3] += e;
     }
 
-  if constexpr (PV == kPvFp16) {
+  if constexpr (F16) {
     // step S (16 keys) = registers 8*(S%2) .. +7 of block S/2; the row sum
     // adds the fp16 values the MFMA consumes (v_dot2 with (1, 1): two keys
     // per instruction, float32 accumulation).
@@ -389,12 +432,14 @@ struct StepPlan {
     for (int i = 0; i < k; ++i) c += is_pv(i) == is_pv(k);
     return c;
   }
-  // softmax micro-ops: 0..47 max/convert, 48 combine, then exp and pack, then finish
+  // softmax micro-ops: NPRE maxima (FP8: with the conversions), one combine,
+  // then the exps and packs, then the finish
+  static constexpr int NPRE = PV == kPvFp16 ? 16 : 48;
   static constexpr int NPACK = PV == kPvFp16 ? 16 : 8;
-  static constexpr int NU = 48 + 1 + 32 + NPACK + 1;
+  static constexpr int NU = NPRE + 1 + 32 + NPACK + 1;
   // first micro-op of slot k (cumulative instruction weight, spread evenly)
   static constexpr int weight(int u) {
-    return u < 48 ? 1 : u == 48 ? 10 : u < 49 + 32 + NPACK ? 2 : 3;
+    return u < NPRE ? 1 : u == NPRE ? 10 : u < NPRE + 1 + 32 + NPACK ? 2 : 3;
   }
   static constexpr int total_weight() {
     int w = 0;
@@ -417,7 +462,8 @@ __device__ __forceinline__ float fused_step(v16f (&o)[D / 32], const v4i (&qf)[D
                                             v16i (&s_cur)[2], v16i (&s_new)[2],
                                             const PTile<PV>& p_cur, PTile<PV>& p_new,
                                             const uint8_t* kb, const uint8_t* vb, float& m_run,
-                                            float& l_run, float cj, int n, int hh) {
+                                            float& l_run, TileScale ts, MaxGrid grid,
+                                            const v16i& init, int n, int hh) {
   using Plan = StepPlan<D, PV>;
   using Op = OpReg<D, PV>;
   constexpr int LA = 2;   // operand read lookahead (slots)
@@ -454,7 +500,7 @@ __device__ __forceinline__ float fused_step(v16f (&o)[D / 32], const v4i (&qf)[D
       v4i a;
       if constexpr (PV == kPvFp16) a = r;
       else a = v4i{r[0], r[1], r[2], r[3]};
-      s_new[blk] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[t], t == 0 ? v16i{} : s_new[blk],
+      s_new[blk] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[t], t == 0 ? init : s_new[blk],
                                                           0, 0, 0);
     } else if constexpr (PV == kPvFp16) {
       constexpr int S = i / Plan::NCB, cb = i % Plan::NCB;
@@ -470,40 +516,49 @@ __device__ __forceinline__ float fused_step(v16f (&o)[D / 32], const v4i (&qf)[D
   };
 
   // ---- softmax side (same arithmetic as softmax_tile, unmasked)
+  constexpr bool F16 = PV == kPvFp16;
+  constexpr int NPRE = Plan::NPRE;
   int mpart[4];
   float f[32], e[32];
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
-  float m_new = 0.f, alpha = 1.f, negm = 0.f;
+  float m_new = 0.f, alpha = 1.f, nb = 0.f;
   auto sc = [&](int i) __attribute__((always_inline)) -> int { return s_cur[i >> 4][i & 15]; };
   auto uop = [&]<int U>() __attribute__((always_inline)) {
-    if constexpr (U < 48) {
-      // triples: max of two scores into one of 4 partial maxima, and a convert
-      constexpr int g = U / 3, r = U % 3;
+    if constexpr (U < NPRE) {
+      // FP16: max of two scores into one of 4 partial maxima.  FP8: triples
+      // of that max and two conversions.
+      constexpr int g = F16 ? U : U / 3, r = F16 ? 0 : U % 3;
       if constexpr (r == 0) {
         const int v = max(sc(2 * g), sc(2 * g + 1));
         mpart[g & 3] = g < 4 ? v : max(mpart[g & 3], v);
       } else {
         f[2 * g + r - 1] = (float)sc(2 * g + r - 1);
       }
-    } else if constexpr (U == 48) {
+    } else if constexpr (U == NPRE) {
       int mx = max(max(mpart[0], mpart[1]), max(mpart[2], mpart[3]));
       mx = pair_max_i32(mx);
-      const float mt = (float)mx * cj;
-      if constexpr (PV == kPvFp16) m_new = mt > m_run + kLazyMax ? mt : m_run;
-      else m_new = fmaxf(m_run, mt);
+      if constexpr (F16) {
+        const float mt = (__builtin_bit_cast(float, mx) - kMagic) * ts.c;
+        m_new = mt > m_run + kLazyMax ? __builtin_ceilf(mt * grid.inv) * grid.step : m_run;
+        nb = -(ts.k0 + m_new);
+      } else {
+        const float mt = (float)mx * ts.c;
+        m_new = fmaxf(m_run, mt);
+        nb = kLog2_448 - m_new;
+      }
       alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      negm = PV == kPvFp8 ? kLog2_448 - m_new : -m_new;
-    } else if constexpr (U < 49 + 32 + Plan::NPACK) {
+    } else if constexpr (U < NPRE + 1 + 32 + Plan::NPACK) {
       // exp of score i, and after every 2 (FP16) / 4 (FP8) scores their pack
-      constexpr int v = U - 49;
-      constexpr int per = PV == kPvFp16 ? 3 : 5;   // 2 exps + pack, or 4 exps + pack
+      constexpr int v = U - NPRE - 1;
+      constexpr int per = F16 ? 3 : 5;   // 2 exps + pack, or 4 exps + pack
       constexpr int grp = v / per, pos = v % per;
       constexpr int nper = per - 1;
       if constexpr (pos < nper) {
         constexpr int i = grp * nper + pos;
-        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[i], cj, negm));
-        if constexpr (PV == kPvFp8) ls[i & 3] += e[i];
-      } else if constexpr (PV == kPvFp16) {
+        const float x = F16 ? __builtin_bit_cast(float, sc(i)) : f[i];
+        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, ts.c, nb));
+        if constexpr (!F16) ls[i & 3] += e[i];
+      } else if constexpr (F16) {
         constexpr int w = grp;   // pair (2w, 2w+1) -> step w/4, element w%4
         uint32_t pk = pack_f16x2(e[2 * w], e[2 * w + 1]);
         // pin: keep this micro-op in its slot (otherwise the backend sinks
@@ -610,6 +665,23 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   load_q_frag<D>(qf, q_bh, qrow, N, hh);
   const float cq = q_scale[(size_t)bh * nqb + qb] * kLog2e;
 
+  // FP16 mode: the accumulator start value (magic bias) and the grid of the
+  // running max, twice the float spacing at the largest K0 of the head.
+  v16i init = {};
+  MaxGrid grid = {1.f, 1.f};
+  if constexpr (PV == kPvFp16) {
+    const int mb = __builtin_amdgcn_readfirstlane(kMagicBits + (N & 0x80000000));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) init[r] = mb;
+    float kmax = 0.f;
+    for (int i = lane; i < ntiles; i += 64) kmax = fmaxf(kmax, ks_bh[i]);
+    kmax = wave_max(kmax);
+    const int e = (int)(__builtin_bit_cast(uint32_t, kMagic * (cq * kmax)) >> 23);
+    const int ge = max(e - 22, 2);   // biased exponent of the grid step
+    grid = MaxGrid{__builtin_bit_cast(float, (uint32_t)ge << 23),
+                   __builtin_bit_cast(float, (uint32_t)(254 - ge) << 23)};
+  }
+
   // Tiles of the workgroup; tiles [0, nt_full) need no mask for any row, the
   // rest (ragged tail, causal diagonal) run the masked softmax.
   const int kv_end = CAUSAL ? min(N, (qb + 1) * kBlockQ) : N;
@@ -618,6 +690,10 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
 
   const KLoader<D, kWaves> kld(wave, lane);
   using VL = VLoader<D, PV, kWaves>;
+  const v4i krs = buffer_rsrc(k_bh, N * D);
+  const v4i vrs = buffer_rsrc(v_bh, ntiles * VB);
+  const uint32_t kl[2] = {lds_addr(kbuf[0]), lds_addr(kbuf[1])};
+  const uint32_t vl[2] = {lds_addr(vbuf[0]), lds_addr(vbuf[1])};
   float m_run = -__builtin_inff();
   float l_run = 0.f;
   v16f o[NCB];
@@ -627,23 +703,24 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   PTile<PV> pA, pB;
 
   auto softmax_any = [&](v16i (&sc)[2], PTile<PV>& pn, int t) __attribute__((always_inline)) {
-    const float cj = cq * ks_bh[t];
-    return t < nt_full
-               ? softmax_tile<PV, CAUSAL, false>(sc, m_run, l_run, pn, cj, t * kKvTile, N, qrow, hh)
-               : softmax_tile<PV, CAUSAL, true>(sc, m_run, l_run, pn, cj, t * kKvTile, N, qrow, hh);
+    const TileScale ts = tile_scale<PV>(cq, ks_bh[t]);
+    return t < nt_full ? softmax_tile<PV, CAUSAL, false>(sc, m_run, l_run, pn, ts, grid,
+                                                         t * kKvTile, N, qrow, hh)
+                       : softmax_tile<PV, CAUSAL, true>(sc, m_run, l_run, pn, ts, grid,
+                                                        t * kKvTile, N, qrow, hh);
   };
 
   // Prologue: S(0), S(1), P~(0); then K^(2) into the slot of K^(0).
-  kld.template issue<true>(k_bh, 0, N, kbuf[0], wave);
-  VL::issue(v_bh, ntiles, 0, vbuf[0], wave, lane);
-  if (nt > 1) kld.template issue<true>(k_bh, kKvTile, N, kbuf[1], wave);
+  kld.template issue<true>(krs, 0, N, kl[0], wave);
+  VL::issue(vrs, 0, vl[0], wave, lane);
+  if (nt > 1) kld.template issue<true>(krs, kKvTile, N, kl[1], wave);
   wait_lds_loads();
   __syncthreads();
-  qk_tile<D>(sA, qf, kbuf[0], n, hh);
-  if (nt > 1) qk_tile<D>(sB, qf, kbuf[1], n, hh);
+  qk_tile<D>(sA, qf, kbuf[0], n, hh, init);
+  if (nt > 1) qk_tile<D>(sB, qf, kbuf[1], n, hh, init);
   softmax_any(sA, pA, 0);   // alpha irrelevant: O is still zero
   __syncthreads();          // every wave has read K^(0)
-  if (nt > 2) kld.template issue<true>(k_bh, 2 * kKvTile, N, kbuf[0], wave);
+  if (nt > 2) kld.template issue<true>(krs, 2 * kKvTile, N, kl[0], wave);
   wait_lds_loads();
   __syncthreads();
 
@@ -655,14 +732,15 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int jj = j + u;
-      kld.template issue<false>(k_bh, (jj + 3) * kKvTile, N, kbuf[1 - u], wave);
-      VL::issue(v_bh, ntiles, jj + 1, vbuf[1 - u], wave, lane);
+      kld.template issue<false>(krs, (jj + 3) * kKvTile, N, kl[1 - u], wave);
+      VL::issue(vrs, jj + 1, vl[1 - u], wave, lane);
       v16i(&s_cur)[2] = u == 0 ? sB : sA;
       v16i(&s_new)[2] = u == 0 ? sA : sB;
       PTile<PV>& p_cur = u == 0 ? pA : pB;
       PTile<PV>& p_new = u == 0 ? pB : pA;
-      const float alpha = fused_step<D, PV>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[u], vbuf[u],
-                                            m_run, l_run, cq * ks_bh[jj + 1], n, hh);
+      const float alpha =
+          fused_step<D, PV>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[u], vbuf[u], m_run, l_run,
+                            tile_scale<PV>(cq, ks_bh[jj + 1]), grid, init, n, hh);
       rescale<D>(o, alpha);
       wait_lds_loads();
       __syncthreads();
@@ -674,13 +752,13 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     for (int u = 0; u < 2; ++u) {
       const int jj = j + u;
       if (jj < nt) {
-        if (jj + 3 < nt) kld.template issue<true>(k_bh, (jj + 3) * kKvTile, N, kbuf[1 - u], wave);
-        if (jj + 1 < nt) VL::issue(v_bh, ntiles, jj + 1, vbuf[1 - u], wave, lane);
+        if (jj + 3 < nt) kld.template issue<true>(krs, (jj + 3) * kKvTile, N, kl[1 - u], wave);
+        if (jj + 1 < nt) VL::issue(vrs, jj + 1, vl[1 - u], wave, lane);
         v16i(&s_cur)[2] = u == 0 ? sB : sA;
         v16i(&s_new)[2] = u == 0 ? sA : sB;
         PTile<PV>& p_cur = u == 0 ? pA : pB;
         PTile<PV>& p_new = u == 0 ? pB : pA;
-        if (jj + 2 < nt) qk_tile<D>(s_new, qf, kbuf[u], n, hh);
+        if (jj + 2 < nt) qk_tile<D>(s_new, qf, kbuf[u], n, hh, init);
         pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh);
         if (jj + 1 < nt) rescale<D>(o, softmax_any(s_cur, p_new, jj + 1));
         wait_lds_loads();
@@ -726,13 +804,13 @@ __global__ __launch_bounds__(64) void debug_s_kernel(const int8_t* __restrict__ 
   v4i qf[D / 32];
   load_q_frag<D>(qf, q_bh, qbase + n, N, hh);
   const KLoader<D, 1> kld(0, lane);
-  kld.template issue<true>(k_bh, kbase, N, kb, 0);
+  kld.template issue<true>(buffer_rsrc(k_bh, N * D), kbase, N, lds_addr(kb), 0);
   wait_lds_loads();
   __syncthreads();
   const int query = qbase + n;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    const v16i s = qk_block<D>(qf, kb, blk, n, hh);
+    const v16i s = qk_block<D>(qf, kb, blk, n, hh, v16i{});
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kbase + 32 * blk + 8 * (r >> 2) + 4 * hh + (r & 3);
