@@ -586,8 +586,9 @@ __device__ __forceinline__ float fused_step(v16f (&o)[D / 32], const v4i (&qf)[D
   };
 
   // ---- the schedule
-  read_op.template operator()<0>();
-  read_op.template operator()<1>();
+  [&]<int... K>(std::integer_sequence<int, K...>) __attribute__((always_inline)) {
+    (read_op.template operator()<K>(), ...);
+  }(std::make_integer_sequence<int, LA>{});
   [&]<int... K>(std::integer_sequence<int, K...>) __attribute__((always_inline)) {
     ([&]() __attribute__((always_inline)) {
       if constexpr (K + LA < Plan::NM) read_op.template operator()<K + LA>();

@@ -77,11 +77,13 @@ __global__ __launch_bounds__(128) void finalize_kernel(const float* __restrict__
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
     if constexpr (DO_K) {
       float tot = 0.f;
+#pragma unroll 16
       for (int j = 0; j < nchunks; ++j) tot += part_sum[((size_t)bh * nchunks + j) * D + c];
       k_mean[(size_t)bh * D + c] = tot / (float)N;
     }
     if constexpr (DO_V) {
       float cm = 0.f;
+#pragma unroll 16
       for (int j = 0; j < nchunks; ++j) cm = fmaxf(cm, part_max[((size_t)bh * nchunks + j) * D + c]);
       v_scale[(size_t)bh * D + c] = cm / 448.f;
       v_recip[(size_t)bh * D + c] = cm > 0.f ? 448.f / cm : 0.f;
@@ -114,25 +116,40 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
   const uint16_t* src = (isq ? q : k) + base;
   const float* mean = k_mean + (size_t)bh * D;
 
+  // Every chunk of this thread covers the same 8 channels (256 * 8 is a
+  // multiple of d); Q is scaled by 1/sqrt(d) and K has its mean subtracted,
+  // each with one rounding: x = f * sc - mu with (sc, mu) = (1/sqrt(d), 0) for
+  // Q and (1, mean) for K (multiplying by 1 and subtracting 0 are exact).
+  const int ch0 = (threadIdx.x * 8) % D;
+  const float sc = isq ? inv_sqrt_d : 1.0f;
+  float mu[8];
+  if (isq) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mu[e] = 0.f;
+  } else {
+    const v4f m0 = *reinterpret_cast<const v4f*>(mean + ch0);
+    const v4f m1 = *reinterpret_cast<const v4f*>(mean + ch0 + 4);
+    mu[0] = m0[0]; mu[1] = m0[1]; mu[2] = m0[2]; mu[3] = m0[3];
+    mu[4] = m1[0]; mu[5] = m1[1]; mu[6] = m1[2]; mu[7] = m1[3];
+  }
+  uint4 raw[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = threadIdx.x + i * 256;
+    raw[i] = c < nchunk ? *reinterpret_cast<const uint4*>(src + (size_t)c * 8) : uint4{0u, 0u, 0u, 0u};
+  }
   float x[MAXC][8];
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
-    const int c = threadIdx.x + i * 256;
-    if (c < nchunk) {
-      const uint4 w = *reinterpret_cast<const uint4*>(src + (size_t)c * 8);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-      const int ch0 = (c * 8) % D;
+    const uint32_t ww[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    const bool live = threadIdx.x + i * 256 < nchunk;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float f = in_to_f32<DT>((uint16_t)(ww[e >> 1] >> ((e & 1) * 16)));
-        f = isq ? f * inv_sqrt_d : f - mean[ch0 + e];
-        x[i][e] = f;
-        amax = fmaxf(amax, fabsf(f));
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+    for (int e = 0; e < 8; ++e) {
+      const float f = in_to_f32<DT>((uint16_t)(ww[e >> 1] >> ((e & 1) * 16)));
+      const float v = live ? f * sc - mu[e] : 0.f;
+      x[i][e] = v;
+      amax = fmaxf(amax, fabsf(v));
     }
   }
   amax = wave_max(amax);
