@@ -9,6 +9,6 @@ from .sage_oracle import (  # noqa: F401
     Q_BLOCK, K_BLOCK, KV_TILE, MEAN_CHUNK, P_STATIC_FP8, P_STATIC_INT8,
     column_mean, quantize_int8_blocks, smooth_quant_qk, prep_v, attention,
     sage_attention, brute_attention, cos_sim, rel_l1, rmse, s_int32_tile,
-    inv_sqrt_d,
+    inv_sqrt_d, rope_rotate_half,
 )
 from .codecs import e4m3_encode, e4m3_decode, fp16_round  # noqa: F401

@@ -159,6 +159,30 @@ def smooth_quant_qk(qf: np.ndarray, kf: np.ndarray, smooth: bool = True):
 
 
 # ---------------------------------------------------------------------------
+# Rotary position embedding ahead of the quantisation.  [SA] §7 (key
+# implementation details, item 1): Q and K are quantised right after the RoPE
+# computation, in the same kernel, with 1/sqrt(d) folded into Q's
+# quantisation.  The pages do not print RoPE itself; the reading here is the
+# common "rotate half" form: channel i (< d/2) pairs with channel i + d/2,
+# and with c = cos[t, i], s = sin[t, i] of token t
+#     y_i       = x_i c - x_{i+d/2} s
+#     y_{i+d/2} = x_{i+d/2} c + x_i s,
+# each product and each sum rounded to float32 in that order.  The tables are
+# inputs (float32 [N, d/2]); smoothing and quantisation then see y.
+def rope_rotate_half(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """x: float32 [B, H, N, d]; cos, sin: float32 [N, d/2]. Returns float32."""
+    x = np.asarray(x, dtype=np.float32)
+    h = x.shape[-1] // 2
+    c = np.asarray(cos, dtype=np.float32)[None, None]
+    sn = np.asarray(sin, dtype=np.float32)[None, None]
+    lo, hi = x[..., :h], x[..., h:]
+    y = np.empty_like(x)
+    y[..., :h] = (lo * c).astype(np.float32) - (hi * sn).astype(np.float32)
+    y[..., h:] = (hi * c).astype(np.float32) + (lo * sn).astype(np.float32)
+    return y
+
+
+# ---------------------------------------------------------------------------
 # V preparation: FP16 P~V keeps V in FP16 ([SA] §3 Algorithm 1, FP16 matmul);
 # FP8 P~V quantises V per channel, delta_V = colmax|V|/448 ([SA2pp] "三").
 def prep_v(vf: np.ndarray, pv_mode: str):

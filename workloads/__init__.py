@@ -29,7 +29,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "round_to_bf16_bits",
-           "round_to_fp16", "bf16_bits_to_f32", "Inputs"]
+           "round_to_fp16", "bf16_bits_to_f32", "Inputs", "rope_tables", "to_nhd"]
 
 
 @dataclass(frozen=True)
@@ -169,3 +169,18 @@ def small(name="t", B=1, H=2, N=200, d=64, dtype="fp16", causal=False, pv_mode="
           seed=11, extras="kbias4") -> Workload:
     """A small ad-hoc workload for tests."""
     return Workload(name, B, H, N, d, dtype, causal, pv_mode, seed, extras)
+
+
+def rope_tables(N: int, d: int, base: float = 10000.0, offset: int = 0):
+    """Rotary tables as a model would pass them: angle(t, i) = (t + offset) *
+    base^(-2i/d) for token t and pair i < d/2, evaluated in float64 and
+    rounded to float32.  Returns (cos, sin), each float32 [N, d/2]."""
+    i = np.arange(d // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * i / d)
+    ang = (np.arange(N, dtype=np.float64) + offset)[:, None] * inv_freq[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def to_nhd(x: np.ndarray) -> np.ndarray:
+    """[B, H, N, d] -> contiguous [B, N, H, d] (the token-major layout)."""
+    return np.ascontiguousarray(np.swapaxes(x, 1, 2))
