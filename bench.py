@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle sample")
+    ap.add_argument("--layout", default="HND", choices=["HND", "NHD"],
+                    help="q, k, v, o layout: [B,H,N,d] or token-major [B,N,H,d]")
+    ap.add_argument("--rope", action="store_true",
+                    help="apply rotary embeddings to Q and K inside the quantisation prepass")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES (3 launches), to calibrate "
                          "the HBM byte counters against a known traffic")
@@ -125,11 +129,18 @@ def main():
     B, H, N, d = wl.B, wl.H, wl.N, wl.d
     inp = make_inputs(wl)
     q, k, v = inp.torch_tensors("cuda")
+    if args.layout == "NHD":
+        q, k, v = (t.transpose(1, 2).contiguous() for t in (q, k, v))
+    rope = None
+    if args.rope:
+        from workloads import rope_tables
+        rope = tuple(torch.from_numpy(t).cuda() for t in rope_tables(N, d))
     out = torch.empty_like(q)
     ws = torch.empty(qa.workspace_bytes(B, H, N, d, wl.pv_mode), dtype=torch.uint8, device="cuda")
 
     def step():
-        qa.sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out=out, workspace=ws)
+        qa.sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out=out, workspace=ws,
+                     layout=args.layout, rope=rope)
 
     for _ in range(args.warmup):
         step()
@@ -147,9 +158,9 @@ def main():
     tops = wl.ops / (ms * 1e-3) / 1e12
 
     # The attention kernel alone, on prepared operands, on the same stream.
-    qk = qa.smooth_quant_qk(q, k)
-    vp, vs = qa.quant_v(v, wl.pv_mode)
-    out2 = torch.empty_like(q)
+    qk = qa.smooth_quant_qk(q, k, layout=args.layout, rope=rope)
+    vp, vs = qa.quant_v(v, wl.pv_mode, layout=args.layout)
+    out2 = torch.empty((B, H, N, d), dtype=q.dtype, device="cuda")
     for _ in range(max(2, args.warmup)):
         qa.sage_attn_quantized(qk, vp, vs, causal=wl.causal, pv_mode=wl.pv_mode,
                                out_dtype=q.dtype, out=out2)
@@ -163,7 +174,8 @@ def main():
     torch.cuda.synchronize()
     kms = k0.elapsed_time(k1) / args.steps
     ktops = wl.ops / (kms * 1e-3) / 1e12
-    assert torch.equal(out, out2), "attention-only path must reproduce the full pass"
+    o_hnd = out.transpose(1, 2) if args.layout == "NHD" else out
+    assert torch.equal(o_hnd, out2), "attention-only path must reproduce the full pass"
 
     traffic = traffic_from_profiles(wl.name)
     mixed_peak = INT8_PEAK_TOPS if wl.pv_mode == "fp8" else \
@@ -185,7 +197,8 @@ def main():
                                f"{'causal' if wl.causal else 'non-causal'} {wl.dtype}, "
                                f"INT8 QK^T + {wl.pv_mode.upper()} P~V",
                    "B": B, "H": H, "N": N, "d": d, "causal": wl.causal,
-                   "pv_mode": wl.pv_mode, "in_dtype": wl.dtype},
+                   "pv_mode": wl.pv_mode, "in_dtype": wl.dtype, "layout": args.layout,
+                   "rope": bool(args.rope)},
         "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
         "roofline": {"kernel": "attn_fwd_kernel", "bound": "mfma",
                      "achieved": round(ktops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",

@@ -50,6 +50,8 @@ typedef enum {
 enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8 = 1 };   /* P~V precision: FP16, or FP8 E4M3 ("8+8") */
 enum { SAGE_DT_F16 = 0, SAGE_DT_BF16 = 1 };   /* element type of q, k, v and o */
 enum { SAGE_OUT_F32 = 2 };                     /* float32 output (sage_attn_fwd_quantized only) */
+enum { SAGE_LAYOUT_HND = 0,                    /* q, k, v, o as [B,H,N,d] */
+       SAGE_LAYOUT_NHD = 1 };                  /* token-major [B,N,H,d] */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* sage_status_str(int status);
@@ -102,6 +104,27 @@ int sage_attn_fwd_f32out(const void* q, const void* k, const void* v, float* o,
                          int B, int H, int N, int d, int causal, int pv_mode, int dtype,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sage_attn_fwd with two options of the inputs:
+ *   layout   SAGE_LAYOUT_HND ([B,H,N,d]) or SAGE_LAYOUT_NHD (token-major
+ *            [B,N,H,d], contiguous); o is written in the same layout.
+ *   rope_cos, rope_sin  NULL, or float32 device tables [N, d/2] (16-byte
+ *            aligned): Q and K are rotated before smoothing and quantisation,
+ *            in the same kernels that quantise them ([SA] §7 key implementation
+ *            details, item 1: RoPE fused with the quantisation).  Rotate-half
+ *            form: channel i < d/2 pairs with i + d/2, and with c = cos[t][i],
+ *            s = sin[t][i] of token t, (x_i, x_{i+d/2}) -> (x_i c - x_{i+d/2} s,
+ *            x_{i+d/2} c + x_i s), each product and sum rounded to float32.
+ *            V is not rotated.  Both tables or neither.
+ *   out_f32  0: o in `dtype`; 1: o float32 (as sage_attn_fwd_f32out).
+ * Same workspace as sage_attn_fwd.  SAGE_ERR_INVALID_ARG for an unknown
+ * layout, one table without the other, or a misaligned table.
+ */
+int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
+                     int B, int H, int N, int d, int causal, int pv_mode, int dtype,
+                     int layout, const float* rope_cos, const float* rope_sin, int out_f32,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- The stages of the pass, exposed for testing and reuse -------------- */
 
 /* Scratch bytes sage_smooth_quant_qk needs (float32 partial column sums). */
@@ -122,6 +145,14 @@ size_t sage_smooth_quant_qk_scratch_bytes(int B, int H, int N, int d);
 int sage_smooth_quant_qk(const void* q, const void* k, int dtype, int B, int H, int N, int d,
                          int8_t* q_i8, int8_t* k_i8, float* q_scale, float* k_scale,
                          float* k_mean, void* scratch, size_t scratch_bytes, void* stream);
+
+/* sage_smooth_quant_qk with the input layout and the optional RoPE tables of
+ * sage_attn_fwd_ex (the mean is then the mean of the rotated K).  Outputs are
+ * in the [B,H,N,d] layout whatever the input layout. */
+int sage_smooth_quant_qk_ex(const void* q, const void* k, int dtype, int layout,
+                            const float* rope_cos, const float* rope_sin, int B, int H, int N,
+                            int d, int8_t* q_i8, int8_t* k_i8, float* q_scale, float* k_scale,
+                            float* k_mean, void* scratch, size_t scratch_bytes, void* stream);
 
 /* Bytes of the prepared V (v_out of sage_quant_v) and of its scratch. */
 size_t sage_quant_v_bytes(int B, int H, int N, int d, int pv_mode);
@@ -151,6 +182,12 @@ size_t sage_quant_v_scratch_bytes(int B, int H, int N, int d, int pv_mode);
 int sage_quant_v(const void* v, int dtype, int B, int H, int N, int d, int pv_mode,
                  void* v_out, float* v_scale, void* scratch, size_t scratch_bytes,
                  void* stream);
+
+/* sage_quant_v reading v in `layout` (SAGE_LAYOUT_HND or SAGE_LAYOUT_NHD);
+ * the output layout is unchanged. */
+int sage_quant_v_ex(const void* v, int dtype, int layout, int B, int H, int N, int d,
+                    int pv_mode, void* v_out, float* v_scale, void* scratch,
+                    size_t scratch_bytes, void* stream);
 
 /*
  * Steps 3-5 alone: the attention kernel on operands already prepared by

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_att
 SAGE_OK = 0
 SAGE_PV = {"fp16": 0, "fp8": 1}
 SAGE_DT = {torch.float16: 0, torch.bfloat16: 1}
+SAGE_LAYOUT = {"HND": 0, "NHD": 1}
 
 _c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
@@ -26,7 +27,11 @@ _SIGNATURES = {
     "sage_attn_fwd": (_c_int, [_vp] * 4 + [_c_int] * 7 + [_vp, _c_size, _vp]),
     "sage_attn_fwd_f32out": (_c_int, [_vp] * 4 + [_c_int] * 7 + [_vp, _c_size, _vp]),
     "sage_smooth_quant_qk_scratch_bytes": (_c_size, [_c_int] * 4),
+    "sage_attn_fwd_ex": (_c_int, [_vp] * 4 + [_c_int] * 8 + [_vp, _vp, _c_int, _vp, _c_size, _vp]),
     "sage_smooth_quant_qk": (_c_int, [_vp, _vp] + [_c_int] * 5 + [_vp] * 6 + [_c_size, _vp]),
+    "sage_smooth_quant_qk_ex": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp] + [_c_int] * 4 +
+                                [_vp] * 6 + [_c_size, _vp]),
+    "sage_quant_v_ex": (_c_int, [_vp] + [_c_int] * 7 + [_vp, _vp, _vp, _c_size, _vp]),
     "sage_quant_v_bytes": (_c_size, [_c_int] * 5),
     "sage_quant_v_scratch_bytes": (_c_size, [_c_int] * 5),
     "sage_quant_v": (_c_int, [_vp] + [_c_int] * 6 + [_vp, _vp, _vp, _c_size, _vp]),

@@ -9,7 +9,7 @@ import ctypes
 
 import torch
 
-from ._lib import SAGE_DT, SAGE_PV, check, lib
+from ._lib import SAGE_DT, SAGE_LAYOUT, SAGE_PV, check, lib
 
 __all__ = ["sage_attn", "sage_attn_quantized", "ref_rows", "smooth_quant_qk", "quant_v", "debug_s_i32", "tiling",
            "workspace_bytes", "untile_v"]
@@ -19,10 +19,14 @@ def _stream_ptr(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _check_qkv(*ts):
+def _check_qkv(*ts, layout: str = "HND"):
+    """(B, H, N, d) of contiguous 16-bit device tensors in `layout`
+    ("HND": [B, H, N, d]; "NHD": [B, N, H, d])."""
+    if layout not in SAGE_LAYOUT:
+        raise ValueError(f"layout {layout!r} (HND or NHD)")
     q = ts[0]
     if q.dim() != 4:
-        raise ValueError("expected [B, H, N, d] tensors")
+        raise ValueError("expected 4-d tensors")
     for t in ts:
         if not t.is_cuda:
             raise ValueError("tensors must be on a HIP device")
@@ -31,8 +35,23 @@ def _check_qkv(*ts):
         if t.dtype != q.dtype or t.shape != q.shape or t.device != q.device:
             raise ValueError("q, k, v must share dtype, shape and device")
         if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous [B, H, N, d]")
-    return tuple(q.shape)
+            raise ValueError("tensors must be contiguous")
+    if layout == "HND":
+        return tuple(q.shape)
+    B, N, H, d = q.shape
+    return B, H, N, d
+
+
+def _rope_ptrs(rope, N, d, dev):
+    """Device pointers of float32 [N, d/2] cos/sin tables, or (None, None)."""
+    if rope is None:
+        return None, None, ()
+    cos, sin = rope
+    for t in (cos, sin):
+        if (not t.is_cuda or t.device != dev or t.dtype != torch.float32 or
+                tuple(t.shape) != (N, d // 2) or not t.is_contiguous()):
+            raise ValueError("rope tables must be contiguous float32 [N, d/2] on the device")
+    return cos.data_ptr(), sin.data_ptr(), (cos, sin)
 
 
 def tiling(d: int = 128, causal: bool = False, pv_mode: str = "fp16") -> dict:
@@ -48,14 +67,18 @@ def workspace_bytes(B: int, H: int, N: int, d: int, pv_mode: str = "fp16") -> in
 
 def sage_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
               pv_mode: str = "fp16", out: torch.Tensor | None = None,
-              workspace: torch.Tensor | None = None, out_f32: bool = False) -> torch.Tensor:
+              workspace: torch.Tensor | None = None, out_f32: bool = False,
+              layout: str = "HND", rope=None) -> torch.Tensor:
     """SageAttention forward: O = softmax(Q K^T / sqrt(d)) V with smoothed INT8
-    Q K^T and FP16 or FP8 P~V.  q, k, v: contiguous [B, H, N, d] fp16/bf16.
+    Q K^T and FP16 or FP8 P~V.  q, k, v: contiguous fp16/bf16 tensors, [B, H, N,
+    d] (layout "HND") or [B, N, H, d] ("NHD"); O has the same layout.
 
+    rope: optional (cos, sin) float32 [N, d/2] device tables; Q and K are then
+    rotated (rotate-half form) inside the quantisation prepass.
     Returns O in the input dtype, or float32 when `out_f32`.  `workspace` may
     be a preallocated uint8 device tensor of workspace_bytes(...) bytes.
     """
-    B, H, N, d = _check_qkv(q, k, v)
+    B, H, N, d = _check_qkv(q, k, v, layout=layout)
     mode = SAGE_PV[pv_mode]
     need = workspace_bytes(B, H, N, d, pv_mode)
     if need == 0:
@@ -64,19 +87,29 @@ def sage_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     odt = torch.float32 if out_f32 else q.dtype
     if out is None:
-        out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
-    elif out.dtype != odt or tuple(out.shape) != (B, H, N, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, H, N, d] tensor of the output dtype")
-    fn = lib().sage_attn_fwd_f32out if out_f32 else lib().sage_attn_fwd
-    check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d, int(causal),
-             mode, SAGE_DT[q.dtype], workspace.data_ptr(), workspace.numel(),
-             _stream_ptr(q.device)), "sage_attn_fwd")
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
+    elif out.dtype != odt or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape and the output dtype")
+    pc, ps, keep = _rope_ptrs(rope, N, d, q.device)
+    if layout == "HND" and rope is None:
+        fn = lib().sage_attn_fwd_f32out if out_f32 else lib().sage_attn_fwd
+        check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
+                 int(causal), mode, SAGE_DT[q.dtype], workspace.data_ptr(), workspace.numel(),
+                 _stream_ptr(q.device)), "sage_attn_fwd")
+    else:
+        check(lib().sage_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B,
+                                     H, N, d, int(causal), mode, SAGE_DT[q.dtype],
+                                     SAGE_LAYOUT[layout], pc, ps, int(out_f32),
+                                     workspace.data_ptr(), workspace.numel(),
+                                     _stream_ptr(q.device)), "sage_attn_fwd_ex")
+    del keep
     return out
 
 
-def smooth_quant_qk(q: torch.Tensor, k: torch.Tensor) -> dict:
-    """Smooth K and quantise Q/sqrt(d), K to INT8 per block (the prepass)."""
-    B, H, N, d = _check_qkv(q, k)
+def smooth_quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND", rope=None) -> dict:
+    """Smooth K and quantise Q/sqrt(d), K to INT8 per block (the prepass), with
+    optional RoPE applied first.  Outputs are [B, H, N, d]-ordered."""
+    B, H, N, d = _check_qkv(q, k, layout=layout)
     dev = q.device
     nqb, nkb = -(-N // 128), -(-N // 64)
     res = dict(q_i8=torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
@@ -86,17 +119,19 @@ def smooth_quant_qk(q: torch.Tensor, k: torch.Tensor) -> dict:
                k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev))
     nscr = int(lib().sage_smooth_quant_qk_scratch_bytes(B, H, N, d))
     scratch = torch.empty(max(nscr, 16), dtype=torch.uint8, device=dev)
-    check(lib().sage_smooth_quant_qk(
-        q.data_ptr(), k.data_ptr(), SAGE_DT[q.dtype], B, H, N, d, res["q_i8"].data_ptr(),
-        res["k_i8"].data_ptr(), res["q_scale"].data_ptr(), res["k_scale"].data_ptr(),
-        res["k_mean"].data_ptr(), scratch.data_ptr(), scratch.numel(), _stream_ptr(dev)),
-        "sage_smooth_quant_qk")
+    pc, ps, keep = _rope_ptrs(rope, N, d, dev)
+    check(lib().sage_smooth_quant_qk_ex(
+        q.data_ptr(), k.data_ptr(), SAGE_DT[q.dtype], SAGE_LAYOUT[layout], pc, ps, B, H, N, d,
+        res["q_i8"].data_ptr(), res["k_i8"].data_ptr(), res["q_scale"].data_ptr(),
+        res["k_scale"].data_ptr(), res["k_mean"].data_ptr(), scratch.data_ptr(), scratch.numel(),
+        _stream_ptr(dev)), "sage_smooth_quant_qk_ex")
+    del keep
     return res
 
 
-def quant_v(v: torch.Tensor, pv_mode: str = "fp16"):
+def quant_v(v: torch.Tensor, pv_mode: str = "fp16", layout: str = "HND"):
     """Prepare V for P~V: (tiled uint8 tensor, per-channel scale or None)."""
-    B, H, N, d = _check_qkv(v)
+    B, H, N, d = _check_qkv(v, layout=layout)
     dev = v.device
     mode = SAGE_PV[pv_mode]
     v_out = torch.empty(int(lib().sage_quant_v_bytes(B, H, N, d, mode)), dtype=torch.uint8,
@@ -104,10 +139,11 @@ def quant_v(v: torch.Tensor, pv_mode: str = "fp16"):
     v_scale = torch.empty((B, H, d), dtype=torch.float32, device=dev) if mode == 1 else None
     nscr = int(lib().sage_quant_v_scratch_bytes(B, H, N, d, mode))
     scratch = torch.empty(max(nscr, 16), dtype=torch.uint8, device=dev)
-    check(lib().sage_quant_v(v.data_ptr(), SAGE_DT[v.dtype], B, H, N, d, mode, v_out.data_ptr(),
-                             v_scale.data_ptr() if v_scale is not None else None,
-                             scratch.data_ptr(), scratch.numel(), _stream_ptr(dev)),
-          "sage_quant_v")
+    check(lib().sage_quant_v_ex(v.data_ptr(), SAGE_DT[v.dtype], SAGE_LAYOUT[layout], B, H, N, d,
+                                mode, v_out.data_ptr(),
+                                v_scale.data_ptr() if v_scale is not None else None,
+                                scratch.data_ptr(), scratch.numel(), _stream_ptr(dev)),
+          "sage_quant_v_ex")
     return v_out, v_scale
 
 

@@ -625,7 +625,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__ k_i8,
                      const uint8_t* __restrict__ v_t, const float* __restrict__ q_scale,
                      const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-                     int BH, int N, int nqb, int ntiles, int xcd_remap, void* __restrict__ out) {
+                     int BH, int N, int nqb, int ntiles, int xcd_remap, int H, int nhd,
+                     void* __restrict__ out) {
   constexpr int KB = KTile<D>::BYTES;
   constexpr int VB = VTile<D, PV>::BYTES;
   constexpr int NCB = D / 32;   // 32-channel blocks of the output
@@ -772,7 +773,9 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   const float l_tot = pair_sum_f32(l_run);
   const float inv = 1.0f / l_tot;
   if (qrow < N) {
-    const size_t orow = ((size_t)bh * N + qrow) * D;
+    // O row of (b, h, qrow): [B,H,N,d] or token-major [B,N,H,d]
+    const size_t orow = nhd ? (((size_t)(bh / H) * N + qrow) * H + bh % H) * D
+                            : ((size_t)bh * N + qrow) * D;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -827,7 +830,7 @@ __global__ __launch_bounds__(64) void debug_s_kernel(const int8_t* __restrict__ 
 template <int D, int PV, int OUT, bool CAUSAL>
 static hipError_t attn_dispatch(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
                                 const float* q_scale, const float* k_scale,
-                                const float* v_scale, int B, int H, int N, void* out,
+                                const float* v_scale, int B, int H, int N, int nhd, void* out,
                                 hipStream_t s) {
   const int nqb = ceil_div(N, kBlockQ);
   const int ntiles = ceil_div(N, kKvTile);
@@ -835,29 +838,30 @@ static hipError_t attn_dispatch(const int8_t* q_i8, const int8_t* k_i8, const ui
   const long long grid = (long long)BH * nqb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   attn_fwd_kernel<D, PV, OUT, CAUSAL><<<dim3((unsigned)grid), 256, 0, s>>>(
-      q_i8, k_i8, v_t, q_scale, k_scale, v_scale, BH, N, nqb, ntiles, CAUSAL ? 0 : 1, out);
+      q_i8, k_i8, v_t, q_scale, k_scale, v_scale, BH, N, nqb, ntiles, CAUSAL ? 0 : 1, H, nhd,
+      out);
   return hipGetLastError();
 }
 
 template <int D, int PV, int OUT>
 static hipError_t attn_dispatch_c(int causal, const int8_t* q_i8, const int8_t* k_i8,
                                   const uint8_t* v_t, const float* q_scale, const float* k_scale,
-                                  const float* v_scale, int B, int H, int N, void* out,
+                                  const float* v_scale, int B, int H, int N, int nhd, void* out,
                                   hipStream_t s) {
   return causal ? attn_dispatch<D, PV, OUT, true>(q_i8, k_i8, v_t, q_scale, k_scale, v_scale, B,
-                                                  H, N, out, s)
+                                                  H, N, nhd, out, s)
                 : attn_dispatch<D, PV, OUT, false>(q_i8, k_i8, v_t, q_scale, k_scale, v_scale,
-                                                   B, H, N, out, s);
+                                                   B, H, N, nhd, out, s);
 }
 
 hipError_t launch_attn(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
                        const float* q_scale, const float* k_scale, const float* v_scale, int B,
-                       int H, int N, int d, int causal, int pv_mode, int out_kind, void* out,
-                       hipStream_t s) {
+                       int H, int N, int d, int causal, int pv_mode, int out_kind, int nhd,
+                       void* out, hipStream_t s) {
 #define SAGE_ATTN_CASE(D, PV, OUT)                                                          \
   if (d == D && pv_mode == PV && out_kind == OUT)                                          \
     return attn_dispatch_c<D, PV, OUT>(causal, q_i8, k_i8, v_t, q_scale, k_scale, v_scale, \
-                                       B, H, N, out, s);
+                                       B, H, N, nhd, out, s);
   SAGE_ATTN_CASE(64, 0, 0) SAGE_ATTN_CASE(64, 0, 1) SAGE_ATTN_CASE(64, 0, 2)
   SAGE_ATTN_CASE(64, 1, 0) SAGE_ATTN_CASE(64, 1, 1) SAGE_ATTN_CASE(64, 1, 2)
   SAGE_ATTN_CASE(128, 0, 0) SAGE_ATTN_CASE(128, 0, 1) SAGE_ATTN_CASE(128, 0, 2)

@@ -15,15 +15,39 @@
 namespace sage {
 
 // ---------------------------------------------------------------------------
-// Column statistics.  One thread owns a pair of channels of one 256-token
-// chunk of one (b, h) and adds the tokens in increasing order from 0.0f.
-// Workgroups of 256 threads cover 256/(d/2) chunks.
-template <int DT, int D, bool DO_K, bool DO_V>
+// Element offset of token t of head bh = b*H + h in a [B,H,N,d] tensor
+// (nhd = 0) or a token-major [B,N,H,d] tensor (nhd = 1).
+template <int D>
+__device__ __forceinline__ size_t row_off(int bh, int t, int H, int N, int nhd) {
+  if (!nhd) return ((size_t)bh * N + t) * D;
+  const int b = bh / H, h = bh - b * H;
+  return (((size_t)b * N + t) * H + h) * D;
+}
+
+// Rotate-half RoPE of one channel pair (x_i, x_{i+d/2}) with c = cos, s = sin:
+// (x_i c - x_{i+d/2} s, x_{i+d/2} c + x_i s), every product and sum rounded
+// to float32 (this file is compiled without FP contraction).
+__device__ __forceinline__ void rope_pair(float lo, float hi, float c, float s, float& rlo,
+                                          float& rhi) {
+  rlo = lo * c - hi * s;
+  rhi = hi * c + lo * s;
+}
+
+// Column statistics.  Without RoPE one thread owns a pair of channels of one
+// 256-token chunk of one (b, h) and adds the tokens in increasing order from
+// 0.0f; with RoPE it owns the two channel pairs (c, c+1) and (c+d/2, c+1+d/2)
+// and adds the rotated values.  Workgroups of 256 threads cover several
+// chunks.
+template <int DT, int D, bool DO_K, bool DO_V, bool ROPE>
 __global__ __launch_bounds__(256) void colstats_kernel(const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v, int N,
-                                                       int nchunks, float* __restrict__ part_sum,
+                                                       int H, int nhd, int nchunks,
+                                                       const float* __restrict__ rope_cos,
+                                                       const float* __restrict__ rope_sin,
+                                                       float* __restrict__ part_sum,
                                                        float* __restrict__ part_max) {
-  constexpr int P = D / 2;
+  constexpr int HD = D / 2;
+  constexpr int P = ROPE ? D / 4 : D / 2;   // threads per chunk
   constexpr int CPW = 256 / P;
   const int bh = blockIdx.y;
   const int p = threadIdx.x % P;
@@ -31,37 +55,80 @@ __global__ __launch_bounds__(256) void colstats_kernel(const uint16_t* __restric
   if (chunk >= nchunks) return;
   const int t0 = chunk * kMeanChunk;
   const int cnt = min(kMeanChunk, N - t0);
-  const size_t base = ((size_t)bh * N + t0) * D + 2 * p;
+  const size_t ts = nhd ? (size_t)H * D : (size_t)D;   // token stride (elements)
+  const size_t base = row_off<D>(bh, t0, H, N, nhd) + 2 * p;
   const size_t out = ((size_t)bh * nchunks + chunk) * D + 2 * p;
-  if constexpr (DO_K) {
-    const uint32_t* kp = reinterpret_cast<const uint32_t*>(k + base);
-    float s0 = 0.f, s1 = 0.f;
-    if (cnt == kMeanChunk) {
+  if constexpr (!ROPE) {
+    if constexpr (DO_K) {
+      const uint16_t* kp = k + base;
+      float s0 = 0.f, s1 = 0.f;
+      if (cnt == kMeanChunk) {
 #pragma unroll 16
-      for (int t = 0; t < kMeanChunk; ++t) {
-        const uint32_t w = kp[(size_t)t * P];
-        s0 += in_to_f32<DT>((uint16_t)(w & 0xffffu));
-        s1 += in_to_f32<DT>((uint16_t)(w >> 16));
+        for (int t = 0; t < kMeanChunk; ++t) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(kp + t * ts);
+          s0 += in_to_f32<DT>((uint16_t)(w & 0xffffu));
+          s1 += in_to_f32<DT>((uint16_t)(w >> 16));
+        }
+      } else {
+        for (int t = 0; t < cnt; ++t) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(kp + t * ts);
+          s0 += in_to_f32<DT>((uint16_t)(w & 0xffffu));
+          s1 += in_to_f32<DT>((uint16_t)(w >> 16));
+        }
       }
-    } else {
+      *reinterpret_cast<v2f*>(part_sum + out) = v2f{s0, s1};
+    }
+    if constexpr (DO_V) {
+      const uint16_t* vp = v + base;
+      float m0 = 0.f, m1 = 0.f;
+#pragma unroll 16
       for (int t = 0; t < cnt; ++t) {
-        const uint32_t w = kp[(size_t)t * P];
-        s0 += in_to_f32<DT>((uint16_t)(w & 0xffffu));
-        s1 += in_to_f32<DT>((uint16_t)(w >> 16));
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(vp + t * ts);
+        m0 = fmaxf(m0, fabsf(in_to_f32<DT>((uint16_t)(w & 0xffffu))));
+        m1 = fmaxf(m1, fabsf(in_to_f32<DT>((uint16_t)(w >> 16))));
       }
+      *reinterpret_cast<v2f*>(part_max + out) = v2f{m0, m1};
     }
-    *reinterpret_cast<v2f*>(part_sum + out) = v2f{s0, s1};
-  }
-  if constexpr (DO_V) {
-    const uint32_t* vp = reinterpret_cast<const uint32_t*>(v + base);
-    float m0 = 0.f, m1 = 0.f;
-#pragma unroll 16
-    for (int t = 0; t < cnt; ++t) {
-      const uint32_t w = vp[(size_t)t * P];
-      m0 = fmaxf(m0, fabsf(in_to_f32<DT>((uint16_t)(w & 0xffffu))));
-      m1 = fmaxf(m1, fabsf(in_to_f32<DT>((uint16_t)(w >> 16))));
+  } else {
+    if constexpr (DO_K) {
+      const uint16_t* kp = k + base;
+      const float* cp = rope_cos + (size_t)t0 * HD + 2 * p;
+      const float* sp = rope_sin + (size_t)t0 * HD + 2 * p;
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll 8
+      for (int t = 0; t < cnt; ++t) {
+        const uint32_t lo = *reinterpret_cast<const uint32_t*>(kp + t * ts);
+        const uint32_t hi = *reinterpret_cast<const uint32_t*>(kp + t * ts + HD);
+        const v2f c = *reinterpret_cast<const v2f*>(cp + (size_t)t * HD);
+        const v2f sn = *reinterpret_cast<const v2f*>(sp + (size_t)t * HD);
+        float r0, r1, r2, r3;
+        rope_pair(in_to_f32<DT>((uint16_t)(lo & 0xffffu)), in_to_f32<DT>((uint16_t)(hi & 0xffffu)),
+                  c[0], sn[0], r0, r2);
+        rope_pair(in_to_f32<DT>((uint16_t)(lo >> 16)), in_to_f32<DT>((uint16_t)(hi >> 16)), c[1],
+                  sn[1], r1, r3);
+        s0 += r0;
+        s1 += r1;
+        s2 += r2;
+        s3 += r3;
+      }
+      *reinterpret_cast<v2f*>(part_sum + out) = v2f{s0, s1};
+      *reinterpret_cast<v2f*>(part_sum + out + HD) = v2f{s2, s3};
     }
-    *reinterpret_cast<v2f*>(part_max + out) = v2f{m0, m1};
+    if constexpr (DO_V) {
+      const uint16_t* vp = v + base;
+      float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+#pragma unroll 8
+      for (int t = 0; t < cnt; ++t) {
+        const uint32_t lo = *reinterpret_cast<const uint32_t*>(vp + t * ts);
+        const uint32_t hi = *reinterpret_cast<const uint32_t*>(vp + t * ts + HD);
+        m0 = fmaxf(m0, fabsf(in_to_f32<DT>((uint16_t)(lo & 0xffffu))));
+        m1 = fmaxf(m1, fabsf(in_to_f32<DT>((uint16_t)(lo >> 16))));
+        m2 = fmaxf(m2, fabsf(in_to_f32<DT>((uint16_t)(hi & 0xffffu))));
+        m3 = fmaxf(m3, fabsf(in_to_f32<DT>((uint16_t)(hi >> 16))));
+      }
+      *reinterpret_cast<v2f*>(part_max + out) = v2f{m0, m1};
+      *reinterpret_cast<v2f*>(part_max + out + HD) = v2f{m2, m3};
+    }
   }
 }
 
@@ -96,10 +163,11 @@ __global__ __launch_bounds__(128) void finalize_kernel(const float* __restrict__
 // tokens) of one (b, h); a block is a contiguous run of ntok*d elements read
 // as 16-byte chunks.  Values stay in registers between the absmax reduction
 // and the encoding.
-template <int DT, int D>
+template <int DT, int D, bool ROPE>
 __global__ __launch_bounds__(256) void quant_qk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const float* __restrict__ k_mean, int N, int nqb, int nkb, int first_blk, float inv_sqrt_d,
+    const float* __restrict__ k_mean, int N, int H, int nhd, int nqb, int nkb, int first_blk,
+    float inv_sqrt_d, const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
     int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8, float* __restrict__ q_scale,
     float* __restrict__ k_scale) {
   constexpr int MAXC = kQBlock * D / 8 / 256;   // 16-byte chunks per thread (Q block)
@@ -112,9 +180,10 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
   const int tok0 = blk * btok;
   const int ntok = min(btok, N - tok0);
   const int nchunk = ntok * (D / 8);
-  const size_t base = ((size_t)bh * N + tok0) * D;
-  const uint16_t* src = (isq ? q : k) + base;
+  const size_t base = ((size_t)bh * N + tok0) * D;   // of the INT8 output ([B,H,N,d])
+  const uint16_t* src = isq ? q : k;
   const float* mean = k_mean + (size_t)bh * D;
+  constexpr int CPR = D / 8;   // chunks per token row
 
   // Every chunk of this thread covers the same 8 channels (256 * 8 is a
   // multiple of d); Q is scaled by 1/sqrt(d) and K has its mean subtracted,
@@ -132,21 +201,45 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
     mu[0] = m0[0]; mu[1] = m0[1]; mu[2] = m0[2]; mu[3] = m0[3];
     mu[4] = m1[0]; mu[5] = m1[1]; mu[6] = m1[2]; mu[7] = m1[3];
   }
-  uint4 raw[MAXC];
+  // With RoPE every chunk also needs the chunk d/2 channels away in the same
+  // row (its rotation partner) and 8 entries of the cos/sin tables.
+  constexpr int HD = D / 2;
+  const int pch = (ch0 + HD) % D;
+  uint4 raw[MAXC], par[MAXC];
+  v4f cs[MAXC][2], sn[MAXC][2];
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int c = threadIdx.x + i * 256;
-    raw[i] = c < nchunk ? *reinterpret_cast<const uint4*>(src + (size_t)c * 8) : uint4{0u, 0u, 0u, 0u};
+    const int tok = tok0 + c / CPR;
+    const uint16_t* row = src + row_off<D>(bh, tok, H, N, nhd);
+    raw[i] = c < nchunk ? *reinterpret_cast<const uint4*>(row + ch0) : uint4{0u, 0u, 0u, 0u};
+    if constexpr (ROPE) {
+      par[i] = c < nchunk ? *reinterpret_cast<const uint4*>(row + pch) : uint4{0u, 0u, 0u, 0u};
+      const size_t toff = (size_t)(c < nchunk ? tok : tok0) * HD + (ch0 % HD);
+      cs[i][0] = *reinterpret_cast<const v4f*>(rope_cos + toff);
+      cs[i][1] = *reinterpret_cast<const v4f*>(rope_cos + toff + 4);
+      sn[i][0] = *reinterpret_cast<const v4f*>(rope_sin + toff);
+      sn[i][1] = *reinterpret_cast<const v4f*>(rope_sin + toff + 4);
+    }
   }
   float x[MAXC][8];
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const uint32_t ww[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    const uint32_t pp[4] = {par[i].x, par[i].y, par[i].z, par[i].w};
     const bool live = threadIdx.x + i * 256 < nchunk;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float f = in_to_f32<DT>((uint16_t)(ww[e >> 1] >> ((e & 1) * 16)));
+      float f = in_to_f32<DT>((uint16_t)(ww[e >> 1] >> ((e & 1) * 16)));
+      if constexpr (ROPE) {
+        const float g = in_to_f32<DT>((uint16_t)(pp[e >> 1] >> ((e & 1) * 16)));
+        const float c = cs[i][e >> 2][e & 3], sv = sn[i][e >> 2][e & 3];
+        const bool low = ch0 < HD;   // own channel in the low half of the pair
+        float rl, rh;
+        rope_pair(low ? f : g, low ? g : f, c, sv, rl, rh);
+        f = low ? rl : rh;
+      }
       const float v = live ? f * sc - mu[e] : 0.f;
       x[i][e] = v;
       amax = fmaxf(amax, fabsf(v));
@@ -186,7 +279,8 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
 template <int DT, int D, int PV>
 __global__ __launch_bounds__(256) void prep_v_kernel(const uint16_t* __restrict__ v,
                                                      const float* __restrict__ v_recip, int N,
-                                                     int ntiles, uint8_t* __restrict__ v_out) {
+                                                     int H, int nhd, int ntiles,
+                                                     uint8_t* __restrict__ v_out) {
   constexpr int LD = D + 8;   // halves per LDS row (16-byte aligned, rotated banks)
   __shared__ __attribute__((aligned(16))) uint16_t tile[kKvTile * LD];
   const int bh = blockIdx.y;
@@ -198,7 +292,7 @@ __global__ __launch_bounds__(256) void prep_v_kernel(const uint16_t* __restrict_
     const int col = (c % (D / 8)) * 8;
     uint4 w = {0u, 0u, 0u, 0u};
     if (key0 + key < N)
-      w = *reinterpret_cast<const uint4*>(v + ((size_t)bh * N + key0 + key) * D + col);
+      w = *reinterpret_cast<const uint4*>(v + row_off<D>(bh, key0 + key, H, N, nhd) + col);
     *reinterpret_cast<uint4*>(&tile[key * LD + col]) = w;
   }
   __syncthreads();
@@ -244,83 +338,96 @@ __global__ __launch_bounds__(256) void prep_v_kernel(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // Launchers.
-template <int DT, int D>
+template <int DT, int D, bool ROPE>
 static hipError_t colstats_dispatch(const void* k, const void* v, int B, int H, int N,
-                                    float* part_sum, float* part_max, float* k_mean,
-                                    float* v_scale, float* v_recip, hipStream_t s) {
+                                    const InLayout& in, float* part_sum, float* part_max,
+                                    float* k_mean, float* v_scale, float* v_recip,
+                                    hipStream_t s) {
   const int nch = ceil_div(N, kMeanChunk);
-  const int cpw = 256 / (D / 2);
+  const int cpw = 256 / (ROPE ? D / 4 : D / 2);
   dim3 grid(ceil_div(nch, cpw), B * H);
   const bool dk = k != nullptr, dv = v != nullptr;
   auto kp = static_cast<const uint16_t*>(k);
   auto vp = static_cast<const uint16_t*>(v);
+#define SAGE_COLSTATS(DK, DV)                                                                 \
+  colstats_kernel<DT, D, DK, DV, ROPE><<<grid, 256, 0, s>>>(kp, vp, N, H, in.nhd, nch,         \
+                                                            in.rope_cos, in.rope_sin, part_sum, \
+                                                            part_max);                          \
+  finalize_kernel<D, DK, DV><<<B * H, 128, 0, s>>>(part_sum, part_max, N, nch, k_mean, v_scale, \
+                                                   v_recip);
   if (dk && dv) {
-    colstats_kernel<DT, D, true, true><<<grid, 256, 0, s>>>(kp, vp, N, nch, part_sum, part_max);
-    finalize_kernel<D, true, true><<<B * H, 128, 0, s>>>(part_sum, part_max, N, nch, k_mean,
-                                                         v_scale, v_recip);
+    SAGE_COLSTATS(true, true)
   } else if (dk) {
-    colstats_kernel<DT, D, true, false><<<grid, 256, 0, s>>>(kp, vp, N, nch, part_sum, part_max);
-    finalize_kernel<D, true, false><<<B * H, 128, 0, s>>>(part_sum, part_max, N, nch, k_mean,
-                                                          v_scale, v_recip);
+    SAGE_COLSTATS(true, false)
   } else if (dv) {
-    colstats_kernel<DT, D, false, true><<<grid, 256, 0, s>>>(kp, vp, N, nch, part_sum, part_max);
-    finalize_kernel<D, false, true><<<B * H, 128, 0, s>>>(part_sum, part_max, N, nch, k_mean,
-                                                          v_scale, v_recip);
+    SAGE_COLSTATS(false, true)
   }
+#undef SAGE_COLSTATS
   return hipGetLastError();
 }
 
 hipError_t launch_colstats(const void* k, const void* v, int dtype, int B, int H, int N, int d,
-                           float* part_sum, float* part_max, float* k_mean, float* v_scale,
-                           float* v_recip, hipStream_t s) {
-  if (dtype == 0 && d == 64) return colstats_dispatch<0, 64>(k, v, B, H, N, part_sum, part_max, k_mean, v_scale, v_recip, s);
-  if (dtype == 0 && d == 128) return colstats_dispatch<0, 128>(k, v, B, H, N, part_sum, part_max, k_mean, v_scale, v_recip, s);
-  if (dtype == 1 && d == 64) return colstats_dispatch<1, 64>(k, v, B, H, N, part_sum, part_max, k_mean, v_scale, v_recip, s);
-  if (dtype == 1 && d == 128) return colstats_dispatch<1, 128>(k, v, B, H, N, part_sum, part_max, k_mean, v_scale, v_recip, s);
+                           const InLayout& in, float* part_sum, float* part_max, float* k_mean,
+                           float* v_scale, float* v_recip, hipStream_t s) {
+  // RoPE rotates K only; V statistics never see it
+  const bool rope = in.rope_cos != nullptr && k != nullptr;
+#define SAGE_CS(DT, D)                                                                        \
+  if (dtype == DT && d == D)                                                                  \
+    return rope ? colstats_dispatch<DT, D, true>(k, v, B, H, N, in, part_sum, part_max, k_mean, \
+                                                 v_scale, v_recip, s)                            \
+                : colstats_dispatch<DT, D, false>(k, v, B, H, N, in, part_sum, part_max,        \
+                                                  k_mean, v_scale, v_recip, s);
+  SAGE_CS(0, 64) SAGE_CS(0, 128) SAGE_CS(1, 64) SAGE_CS(1, 128)
+#undef SAGE_CS
   return hipErrorInvalidValue;
 }
 
-template <int DT, int D>
+template <int DT, int D, bool ROPE>
 static hipError_t quant_qk_dispatch(const void* q, const void* k, const float* k_mean, int B,
-                                    int H, int N, int8_t* q_i8, int8_t* k_i8, float* q_scale,
-                                    float* k_scale, hipStream_t s) {
+                                    int H, int N, const InLayout& in, int8_t* q_i8, int8_t* k_i8,
+                                    float* q_scale, float* k_scale, hipStream_t s) {
   const int nqb = ceil_div(N, kQBlock), nkb = ceil_div(N, kKBlock);
   const float isd = (float)(1.0 / __builtin_sqrt((double)D));
   const int first = q ? 0 : nqb;
   const int count = (q ? nqb : 0) + (k ? nkb : 0);
   dim3 grid(count, B * H);
-  quant_qk_kernel<DT, D><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(q),
-                                              static_cast<const uint16_t*>(k), k_mean, N, nqb,
-                                              nkb, first, isd, q_i8, k_i8, q_scale, k_scale);
+  quant_qk_kernel<DT, D, ROPE><<<grid, 256, 0, s>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), k_mean, N, H, in.nhd, nqb,
+      nkb, first, isd, in.rope_cos, in.rope_sin, q_i8, k_i8, q_scale, k_scale);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_qk(const void* q, const void* k, const float* k_mean, int dtype, int B,
-                           int H, int N, int d, int8_t* q_i8, int8_t* k_i8, float* q_scale,
-                           float* k_scale, hipStream_t s) {
+                           int H, int N, int d, const InLayout& in, int8_t* q_i8, int8_t* k_i8,
+                           float* q_scale, float* k_scale, hipStream_t s) {
   if (!q && !k) return hipSuccess;
-  if (dtype == 0 && d == 64) return quant_qk_dispatch<0, 64>(q, k, k_mean, B, H, N, q_i8, k_i8, q_scale, k_scale, s);
-  if (dtype == 0 && d == 128) return quant_qk_dispatch<0, 128>(q, k, k_mean, B, H, N, q_i8, k_i8, q_scale, k_scale, s);
-  if (dtype == 1 && d == 64) return quant_qk_dispatch<1, 64>(q, k, k_mean, B, H, N, q_i8, k_i8, q_scale, k_scale, s);
-  if (dtype == 1 && d == 128) return quant_qk_dispatch<1, 128>(q, k, k_mean, B, H, N, q_i8, k_i8, q_scale, k_scale, s);
+  const bool rope = in.rope_cos != nullptr;
+#define SAGE_QQ(DT, D)                                                                      \
+  if (dtype == DT && d == D)                                                                \
+    return rope ? quant_qk_dispatch<DT, D, true>(q, k, k_mean, B, H, N, in, q_i8, k_i8,      \
+                                                 q_scale, k_scale, s)                        \
+                : quant_qk_dispatch<DT, D, false>(q, k, k_mean, B, H, N, in, q_i8, k_i8,     \
+                                                  q_scale, k_scale, s);
+  SAGE_QQ(0, 64) SAGE_QQ(0, 128) SAGE_QQ(1, 64) SAGE_QQ(1, 128)
+#undef SAGE_QQ
   return hipErrorInvalidValue;
 }
 
 template <int DT, int D, int PV>
 static hipError_t prep_v_dispatch(const void* v, const float* v_recip, int B, int H, int N,
-                                  uint8_t* v_out, hipStream_t s) {
+                                  int nhd, uint8_t* v_out, hipStream_t s) {
   const int nt = ceil_div(N, kKvTile);
   dim3 grid(nt, B * H);
-  prep_v_kernel<DT, D, PV><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), v_recip, N, nt,
-                                                v_out);
+  prep_v_kernel<DT, D, PV><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), v_recip, N, H,
+                                                nhd, nt, v_out);
   return hipGetLastError();
 }
 
 hipError_t launch_prep_v(const void* v, const float* v_recip, int dtype, int B, int H, int N,
-                         int d, int pv_mode, uint8_t* v_out, hipStream_t s) {
+                         int d, int pv_mode, int nhd, uint8_t* v_out, hipStream_t s) {
 #define SAGE_PV_CASE(DT, D, PV)                                              \
   if (dtype == DT && d == D && pv_mode == PV)                                \
-    return prep_v_dispatch<DT, D, PV>(v, v_recip, B, H, N, v_out, s);
+    return prep_v_dispatch<DT, D, PV>(v, v_recip, B, H, N, nhd, v_out, s);
   SAGE_PV_CASE(0, 64, 0) SAGE_PV_CASE(0, 64, 1) SAGE_PV_CASE(0, 128, 0) SAGE_PV_CASE(0, 128, 1)
   SAGE_PV_CASE(1, 64, 0) SAGE_PV_CASE(1, 64, 1) SAGE_PV_CASE(1, 128, 0) SAGE_PV_CASE(1, 128, 1)
 #undef SAGE_PV_CASE

@@ -81,6 +81,14 @@ int device_check() {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
 
+// Layout flag and RoPE tables: both tables or neither, 16-byte aligned.
+int validate_in(int layout, const float* rope_cos, const float* rope_sin) {
+  if (layout != SAGE_LAYOUT_HND && layout != SAGE_LAYOUT_NHD) return SAGE_ERR_INVALID_ARG;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return SAGE_ERR_INVALID_ARG;
+  if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) return SAGE_ERR_INVALID_ARG;
+  return SAGE_OK;
+}
+
 int validate_fwd(const void* q, const void* k, const void* v, const void* o, int B, int H, int N,
                  int d, int causal, int pv_mode, int dtype, const void* ws, size_t ws_bytes) {
   if (!q || !k || !v || !o || !ws) return SAGE_ERR_INVALID_ARG;
@@ -98,10 +106,12 @@ int validate_fwd(const void* q, const void* k, const void* v, const void* o, int
 }
 
 int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
-            int causal, int pv_mode, int dtype, void* ws, size_t ws_bytes, void* stream,
-            int out_kind) {
+            int causal, int pv_mode, int dtype, int layout, const float* rope_cos,
+            const float* rope_sin, void* ws, size_t ws_bytes, void* stream, int out_kind) {
   int st = validate_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, ws, ws_bytes);
   if (st != SAGE_OK) return st;
+  if ((st = validate_in(layout, rope_cos, rope_sin)) != SAGE_OK) return st;
+  const sage::InLayout in{layout, rope_cos, rope_sin};
   if ((st = device_check()) != SAGE_OK) return st;
   const Layout L = make_layout(B, H, N, d, pv_mode);
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -111,17 +121,17 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, 
   uint8_t* v_t = w + L.v_t;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fp8 = pv_mode == SAGE_PV_FP8;
-  hipError_t e = sage::launch_colstats(k, fp8 ? v : nullptr, dtype, B, H, N, d, F(L.part_sum),
-                                       fp8 ? F(L.part_max) : nullptr, F(L.k_mean),
+  hipError_t e = sage::launch_colstats(k, fp8 ? v : nullptr, dtype, B, H, N, d, in,
+                                       F(L.part_sum), fp8 ? F(L.part_max) : nullptr, F(L.k_mean),
                                        F(L.v_scale), F(L.v_recip), s);
   if (e != hipSuccess) return SAGE_ERR_HIP;
-  e = sage::launch_quant_qk(q, k, F(L.k_mean), dtype, B, H, N, d, q_i8, k_i8, F(L.q_scale),
+  e = sage::launch_quant_qk(q, k, F(L.k_mean), dtype, B, H, N, d, in, q_i8, k_i8, F(L.q_scale),
                             F(L.k_scale), s);
   if (e != hipSuccess) return SAGE_ERR_HIP;
-  e = sage::launch_prep_v(v, F(L.v_recip), dtype, B, H, N, d, pv_mode, v_t, s);
+  e = sage::launch_prep_v(v, F(L.v_recip), dtype, B, H, N, d, pv_mode, layout, v_t, s);
   if (e != hipSuccess) return SAGE_ERR_HIP;
   e = sage::launch_attn(q_i8, k_i8, v_t, F(L.q_scale), F(L.k_scale), F(L.v_scale), B, H, N, d,
-                        causal, pv_mode, out_kind, o, s);
+                        causal, pv_mode, out_kind, layout, o, s);
   return hip_status(e);
 }
 
@@ -162,15 +172,25 @@ size_t sage_attn_workspace_bytes(int B, int H, int N, int d, int pv_mode) {
 int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N,
                   int d, int causal, int pv_mode, int dtype, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  return run_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, workspace, workspace_bytes,
-                 stream, dtype == SAGE_DT_BF16 ? 1 : 0);
+  return run_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, SAGE_LAYOUT_HND, nullptr,
+                 nullptr, workspace, workspace_bytes, stream, dtype == SAGE_DT_BF16 ? 1 : 0);
 }
 
 int sage_attn_fwd_f32out(const void* q, const void* k, const void* v, float* o, int B, int H,
                          int N, int d, int causal, int pv_mode, int dtype, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  return run_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, workspace, workspace_bytes,
-                 stream, 2);
+  return run_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, SAGE_LAYOUT_HND, nullptr,
+                 nullptr, workspace, workspace_bytes, stream, 2);
+}
+
+int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int H, int N,
+                     int d, int causal, int pv_mode, int dtype, int layout,
+                     const float* rope_cos, const float* rope_sin, int out_f32, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (out_f32 != 0 && out_f32 != 1) return SAGE_ERR_INVALID_ARG;
+  return run_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, layout, rope_cos, rope_sin,
+                 workspace, workspace_bytes, stream,
+                 out_f32 ? 2 : (dtype == SAGE_DT_BF16 ? 1 : 0));
 }
 
 size_t sage_smooth_quant_qk_scratch_bytes(int B, int H, int N, int d) {
@@ -181,6 +201,14 @@ size_t sage_smooth_quant_qk_scratch_bytes(int B, int H, int N, int d) {
 int sage_smooth_quant_qk(const void* q, const void* k, int dtype, int B, int H, int N, int d,
                          int8_t* q_i8, int8_t* k_i8, float* q_scale, float* k_scale,
                          float* k_mean, void* scratch, size_t scratch_bytes, void* stream) {
+  return sage_smooth_quant_qk_ex(q, k, dtype, SAGE_LAYOUT_HND, nullptr, nullptr, B, H, N, d, q_i8,
+                                 k_i8, q_scale, k_scale, k_mean, scratch, scratch_bytes, stream);
+}
+
+int sage_smooth_quant_qk_ex(const void* q, const void* k, int dtype, int layout,
+                            const float* rope_cos, const float* rope_sin, int B, int H, int N,
+                            int d, int8_t* q_i8, int8_t* k_i8, float* q_scale, float* k_scale,
+                            float* k_mean, void* scratch, size_t scratch_bytes, void* stream) {
   if (!q || !k || !q_i8 || !k_i8 || !q_scale || !k_scale || !k_mean || !scratch)
     return SAGE_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8) ||
@@ -190,14 +218,17 @@ int sage_smooth_quant_qk(const void* q, const void* k, int dtype, int B, int H, 
   if (dtype != SAGE_DT_F16 && dtype != SAGE_DT_BF16) return SAGE_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
   if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
-  if (scratch_bytes < sage_smooth_quant_qk_scratch_bytes(B, H, N, d)) return SAGE_ERR_WORKSPACE;
-  int st = device_check();
+  int st = validate_in(layout, rope_cos, rope_sin);
   if (st != SAGE_OK) return st;
+  if (scratch_bytes < sage_smooth_quant_qk_scratch_bytes(B, H, N, d)) return SAGE_ERR_WORKSPACE;
+  if ((st = device_check()) != SAGE_OK) return st;
+  const sage::InLayout in{layout, rope_cos, rope_sin};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = sage::launch_colstats(k, nullptr, dtype, B, H, N, d, static_cast<float*>(scratch),
-                                       nullptr, k_mean, nullptr, nullptr, s);
+  hipError_t e = sage::launch_colstats(k, nullptr, dtype, B, H, N, d, in,
+                                       static_cast<float*>(scratch), nullptr, k_mean, nullptr,
+                                       nullptr, s);
   if (e != hipSuccess) return SAGE_ERR_HIP;
-  e = sage::launch_quant_qk(q, k, k_mean, dtype, B, H, N, d, q_i8, k_i8, q_scale, k_scale, s);
+  e = sage::launch_quant_qk(q, k, k_mean, dtype, B, H, N, d, in, q_i8, k_i8, q_scale, k_scale, s);
   return hip_status(e);
 }
 
@@ -216,6 +247,14 @@ size_t sage_quant_v_scratch_bytes(int B, int H, int N, int d, int pv_mode) {
 
 int sage_quant_v(const void* v, int dtype, int B, int H, int N, int d, int pv_mode, void* v_out,
                  float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {
+  return sage_quant_v_ex(v, dtype, SAGE_LAYOUT_HND, B, H, N, d, pv_mode, v_out, v_scale, scratch,
+                         scratch_bytes, stream);
+}
+
+int sage_quant_v_ex(const void* v, int dtype, int layout, int B, int H, int N, int d,
+                    int pv_mode, void* v_out, float* v_scale, void* scratch,
+                    size_t scratch_bytes, void* stream) {
+  if (layout != SAGE_LAYOUT_HND && layout != SAGE_LAYOUT_NHD) return SAGE_ERR_INVALID_ARG;
   if (!v || !v_out) return SAGE_ERR_INVALID_ARG;
   if (!aligned16(v) || !aligned16(v_out)) return SAGE_ERR_INVALID_ARG;
   if (dtype != SAGE_DT_F16 && dtype != SAGE_DT_BF16) return SAGE_ERR_INVALID_ARG;
@@ -236,11 +275,12 @@ int sage_quant_v(const void* v, int dtype, int B, int H, int N, int d, int pv_mo
     v_recip = reinterpret_cast<float*>(
         static_cast<uint8_t*>(scratch) +
         align_up((size_t)B * H * ceil_div(N, sage::kMeanChunk) * d * 4));
-    hipError_t e = sage::launch_colstats(nullptr, v, dtype, B, H, N, d, nullptr, part_max, nullptr,
-                                         v_scale, v_recip, s);
+    const sage::InLayout in{layout, nullptr, nullptr};
+    hipError_t e = sage::launch_colstats(nullptr, v, dtype, B, H, N, d, in, nullptr, part_max,
+                                         nullptr, v_scale, v_recip, s);
     if (e != hipSuccess) return SAGE_ERR_HIP;
   }
-  return hip_status(sage::launch_prep_v(v, v_recip, dtype, B, H, N, d, pv_mode,
+  return hip_status(sage::launch_prep_v(v, v_recip, dtype, B, H, N, d, pv_mode, layout,
                                         static_cast<uint8_t*>(v_out), s));
 }
 
@@ -264,7 +304,7 @@ int sage_attn_fwd_quantized(const int8_t* q_i8, const int8_t* k_i8, const void* 
   if (st != SAGE_OK) return st;
   return hip_status(sage::launch_attn(q_i8, k_i8, static_cast<const uint8_t*>(v_prep), q_scale,
                                       k_scale, v_scale, B, H, N, d, causal, pv_mode, out_dtype,
-                                      o, static_cast<hipStream_t>(stream)));
+                                      SAGE_LAYOUT_HND, o, static_cast<hipStream_t>(stream)));
 }
 
 int sage_attn_ref_rows_f32(const void* q, const void* k, const void* v, int dtype, int B, int H,

@@ -30,28 +30,37 @@ inline size_t v_tile_bytes(int d, int pv_mode) {
   return (size_t)d * (pv_mode == kPvFp16 ? 128 : 64);
 }
 
+// Layout of q, k, v (and o) and the optional RoPE tables applied to Q and K
+// ahead of smoothing and quantisation (float32 [N, d/2] cos and sin).
+struct InLayout {
+  int nhd;                  // 0: [B,H,N,d]; 1: token-major [B,N,H,d]
+  const float* rope_cos;    // null: no RoPE
+  const float* rope_sin;
+};
+
 // Prepass: column statistics of K (float32 partial sums per 256-token chunk)
 // and, if part_max != nullptr, of |V| (partial maxima), then the finalised
 // mean (and V scale / reciprocal when v_scale != nullptr).
 hipError_t launch_colstats(const void* k, const void* v, int dtype, int B, int H, int N, int d,
-                           float* part_sum, float* part_max, float* k_mean, float* v_scale,
-                           float* v_recip, hipStream_t s);
+                           const InLayout& in, float* part_sum, float* part_max, float* k_mean,
+                           float* v_scale, float* v_recip, hipStream_t s);
 
 // Prepass: INT8 quantisation of Q/sqrt(d) (128-token blocks) and of K - mean
 // (64-token blocks).  Either q or k may be null to skip that tensor.
 hipError_t launch_quant_qk(const void* q, const void* k, const float* k_mean, int dtype, int B,
-                           int H, int N, int d, int8_t* q_i8, int8_t* k_i8, float* q_scale,
-                           float* k_scale, hipStream_t s);
+                           int H, int N, int d, const InLayout& in, int8_t* q_i8, int8_t* k_i8,
+                           float* q_scale, float* k_scale, hipStream_t s);
 
 // Prepass: V -> fp16 or E4M3 in the tiled layout of the attention kernel.
 hipError_t launch_prep_v(const void* v, const float* v_recip, int dtype, int B, int H, int N,
-                         int d, int pv_mode, uint8_t* v_out, hipStream_t s);
+                         int d, int pv_mode, int nhd, uint8_t* v_out, hipStream_t s);
 
-// Attention kernel.  out_kind: 0 = fp16, 1 = bf16, 2 = float32.
+// Attention kernel.  out_kind: 0 = fp16, 1 = bf16, 2 = float32; nhd: o is
+// token-major [B,N,H,d] instead of [B,H,N,d].
 hipError_t launch_attn(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
                        const float* q_scale, const float* k_scale, const float* v_scale, int B,
-                       int H, int N, int d, int causal, int pv_mode, int out_kind, void* out,
-                       hipStream_t s);
+                       int H, int N, int d, int causal, int pv_mode, int out_kind, int nhd,
+                       void* out, hipStream_t s);
 
 // Float32 softmax attention on selected query rows (reference for profiling).
 hipError_t launch_ref_rows(const void* q, const void* k, const void* v, int dtype, int B, int H,

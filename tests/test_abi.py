@@ -198,3 +198,24 @@ def test_ref_rows_validation():
     assert h.sage_attn_ref_rows_f32(*bad) == UNSUPPORTED
     if not torch.cuda.is_available():
         assert h.sage_attn_ref_rows_f32(*args) == NO_DEVICE
+
+
+def test_layout_and_rope_validation():
+    h = lib()
+    ws = P + 0x100000
+    base = [P, P, P, P + 0x1000, 1, 2, 100, 64, 0, 0, 0]
+    # layout, rope_cos, rope_sin, out_f32, workspace, bytes, stream
+    assert h.sage_attn_fwd_ex(*base, 2, None, None, 0, ws, 1 << 40, None) == INVALID
+    assert h.sage_attn_fwd_ex(*base, 1, P, None, 0, ws, 1 << 40, None) == INVALID
+    assert h.sage_attn_fwd_ex(*base, 1, P + 4, P, 0, ws, 1 << 40, None) == INVALID
+    assert h.sage_attn_fwd_ex(*base, 0, None, None, 2, ws, 1 << 40, None) == INVALID
+    assert h.sage_smooth_quant_qk_ex(P, P, 0, 3, None, None, 1, 1, 300, 64, P, P, P, P, P, P,
+                                     1 << 30, None) == INVALID
+    assert h.sage_smooth_quant_qk_ex(P, P, 0, 0, None, P, 1, 1, 300, 64, P, P, P, P, P, P,
+                                     1 << 30, None) == INVALID
+    assert h.sage_quant_v_ex(P, 0, 5, 1, 1, 300, 64, 0, P, None, P, 1 << 30, None) == INVALID
+    if not torch.cuda.is_available():
+        assert h.sage_attn_fwd_ex(*base, 1, P, P, 1, ws, 1 << 40, None) == NO_DEVICE
+        assert h.sage_smooth_quant_qk_ex(P, P, 0, 1, P, P, 1, 1, 300, 64, P, P, P, P, P, P,
+                                         1 << 30, None) == NO_DEVICE
+        assert h.sage_quant_v_ex(P, 0, 1, 1, 1, 300, 64, 0, P, None, P, 1 << 30, None) == NO_DEVICE
