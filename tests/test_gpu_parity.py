@@ -216,3 +216,25 @@ def test_full_workload(name):
         g16 = to_np(o16[b, h, torch.from_numpy(rows).cuda()].float())
         compare_o(g32, ref, f"{name} (b={b},h={h}) O f32")
         assert np.all(np.abs(g16 - ref) <= O_MAX_ABS + ulp16(ref, wl.dtype)), "16-bit O"
+
+
+@pytest.mark.parametrize("name", ["t7_cogvideox", "t7_unidiffuser", "t7_ultrapixel", "t7_llama2",
+                                  "t7_timm"])
+def test_table7_shapes(name):
+    # real-model shapes (B, H, N, d) of the pages' Table 7, full size, with
+    # ragged token counts 17776, 1105 and 197: sampled rows of two heads
+    from workloads import TABLE7
+    wl = TABLE7[name]
+    note(f"table-7 shape {name}: {wl}")
+    inp = make_inputs(wl)
+    q, k, v = gpu_inputs(inp)
+    B, H, N = wl.B, wl.H, wl.N
+    o32 = qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out_f32=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(N, wl.causal, wl.seed)
+    for (b, h) in [(0, 0), (B - 1, H - 1)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.sage_attention(inp.qf[sl], inp.kf[sl], inp.vf[sl], causal=wl.causal,
+                                    pv_mode=wl.pv_mode, rows=rows)[0, 0]
+        compare_o(to_np(o32[b, h, torch.from_numpy(rows).cuda()]), ref,
+                  f"{name} (b={b},h={h}) O f32")

@@ -28,7 +28,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "round_to_bf16_bits",
+__all__ = ["Workload", "WORKLOADS", "TABLE7", "make_inputs", "round_to_bf16_bits",
            "round_to_fp16", "bf16_bits_to_f32", "Inputs", "rope_tables", "to_nhd"]
 
 
@@ -68,6 +68,23 @@ WORKLOADS = {
                    "8+8 mode: FP8 P~V with per-channel V scales"),
     "c5": Workload("c5", 1, 32, 32768, 128, "bf16", True, "fp8", 4, "kbias4",
                    "long context, causal, FP8 P~V"),
+}
+
+
+# The real-model shapes of "SageAttention ..." detail page, §5 Table 7
+# (B, H, N, d), with seeded synthetic activations of the Figure-4 kind (K with
+# a per-channel bias shared by all tokens).  The LLM shape runs causal.
+TABLE7 = {
+    "t7_cogvideox": Workload("t7_cogvideox", 2, 30, 17776, 64, "fp16", False, "fp16", 21,
+                             "kbias4", "CogVideoX shape, ragged N"),
+    "t7_unidiffuser": Workload("t7_unidiffuser", 2, 24, 1105, 64, "fp16", False, "fp16", 22,
+                               "kbias4", "Unidiffuser shape, ragged N"),
+    "t7_ultrapixel": Workload("t7_ultrapixel", 8, 30, 4096, 64, "fp16", False, "fp16", 23,
+                              "kbias4", "UltraPixel shape"),
+    "t7_llama2": Workload("t7_llama2", 1, 32, 4096, 128, "fp16", True, "fp16", 24, "kchan20",
+                          "Llama2 prefill shape, causal"),
+    "t7_timm": Workload("t7_timm", 12, 64, 197, 64, "fp16", False, "fp16", 25, "kbias4",
+                        "TIMM shape, 197 tokens"),
 }
 
 
@@ -145,7 +162,7 @@ def _apply_extras(wl: Workload, rng, q, k, v):
 def make_inputs(wl: Workload | str, **overrides) -> Inputs:
     """Draw q, k, v for a workload (or a named one with fields overridden)."""
     if isinstance(wl, str):
-        wl = WORKLOADS[wl]
+        wl = WORKLOADS[wl] if wl in WORKLOADS else TABLE7[wl]
     if overrides:
         wl = wl.with_(**overrides)
     shape = (wl.B, wl.H, wl.N, wl.d)
