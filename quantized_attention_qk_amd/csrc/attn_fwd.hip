@@ -407,6 +407,14 @@ __device__ __forceinline__ void pv_tile(v16f (&o)[D / 32], const PTile<PV>& pt,
   }
 }
 
+template <int D>
+__device__ __forceinline__ void rescale(v16f (&o)[D / 32], float alpha) {
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) o[cb] *= alpha;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The steady-state step as an explicit instruction schedule.
 //
@@ -439,7 +447,7 @@ struct StepPlan {
   static constexpr int NU = NPRE + 1 + 32 + NPACK + 1;
   // first micro-op of slot k (cumulative instruction weight, spread evenly)
   static constexpr int weight(int u) {
-    return u < NPRE ? 1 : u == NPRE ? 10 : u < NPRE + 1 + 32 + NPACK ? 2 : 3;
+    return u < NPRE ? 1 : u == NPRE ? (PV == kPvFp16 ? 6 : 10) : u < NPRE + 1 + 32 + NPACK ? 2 : 3;
   }
   static constexpr int total_weight() {
     int w = 0;
@@ -458,7 +466,7 @@ template <int D, int PV>
 using OpReg = std::conditional_t<PV == kPvFp16, v4i, v8i>;
 
 template <int D, int PV>
-__device__ __forceinline__ float fused_step(v16f (&o)[D / 32], const v4i (&qf)[D / 32],
+__device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D / 32],
                                             v16i (&s_cur)[2], v16i (&s_new)[2],
                                             const PTile<PV>& p_cur, PTile<PV>& p_new,
                                             const uint8_t* kb, const uint8_t* vb, float& m_run,
@@ -521,32 +529,48 @@ __device__ __forceinline__ float fused_step(v16f (&o)[D / 32], const v4i (&qf)[D
   int mpart[4];
   float f[32], e[32];
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
-  float m_new = 0.f, alpha = 1.f, nb = 0.f;
+  float m_new = 0.f, alpha = 1.f, nb = 0.f, lsum = 0.f;
   auto sc = [&](int i) __attribute__((always_inline)) -> int { return s_cur[i >> 4][i & 15]; };
   auto uop = [&]<int U>() __attribute__((always_inline)) {
     if constexpr (U < NPRE) {
       // FP16: max of two scores into one of 4 partial maxima.  FP8: triples
       // of that max and two conversions.
       constexpr int g = F16 ? U : U / 3, r = F16 ? 0 : U % 3;
-      if constexpr (r == 0) {
+      if constexpr (F16) {
+        // one chain of 3-input maxima (the slots spread it over the step),
+        // written so that each step folds into one v_max3
+        mpart[0] = g == 0 ? max(sc(0), sc(1)) : max(max(mpart[0], sc(2 * g)), sc(2 * g + 1));
+      } else if constexpr (r == 0) {
         const int v = max(sc(2 * g), sc(2 * g + 1));
         mpart[g & 3] = g < 4 ? v : max(mpart[g & 3], v);
       } else {
         f[2 * g + r - 1] = (float)sc(2 * g + r - 1);
       }
     } else if constexpr (U == NPRE) {
-      int mx = max(max(mpart[0], mpart[1]), max(mpart[2], mpart[3]));
-      mx = pair_max_i32(mx);
+      int mx = F16 ? mpart[0] : max(max(mpart[0], mpart[1]), max(mpart[2], mpart[3]));
       if constexpr (F16) {
-        const float mt = (__builtin_bit_cast(float, mx) - kMagic) * ts.c;
-        m_new = mt > m_run + kLazyMax ? __builtin_ceilf(mt * grid.inv) * grid.step : m_run;
+        // The row max only matters when it passes the lazy bound, and then
+        // some lane's own max passes it too: only then do the wavefront's
+        // rows combine their two halves and take the rule below.  The result
+        // is the same as applying the rule to every row.
+        m_new = m_run;
+        alpha = 1.f;
+        const float lane_mt = (__builtin_bit_cast(float, mx) - kMagic) * ts.c;
+        if (__builtin_amdgcn_ballot_w64(lane_mt > m_run + kLazyMax)) {
+          mx = pair_max_i32(mx);
+          const float mt = (__builtin_bit_cast(float, mx) - kMagic) * ts.c;
+          m_new = mt > m_run + kLazyMax ? __builtin_ceilf(mt * grid.inv) * grid.step : m_run;
+          alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        }
         nb = -(ts.k0 + m_new);
+        lsum = l_run * alpha;   // the row sum continues from the rescaled total
       } else {
+        mx = pair_max_i32(mx);
         const float mt = (float)mx * ts.c;
         m_new = fmaxf(m_run, mt);
         nb = kLog2_448 - m_new;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       }
-      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     } else if constexpr (U < NPRE + 1 + 32 + Plan::NPACK) {
       // exp of score i, and after every 2 (FP16) / 4 (FP8) scores their pack
       constexpr int v = U - NPRE - 1;
@@ -566,7 +590,7 @@ __device__ __forceinline__ float fused_step(v16f (&o)[D / 32], const v4i (&qf)[D
         asm volatile("" : "+v"(pk));
         p_new.w[w >> 2][w & 3] = (int)pk;
         const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
-        ls[w & 3] = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, pk), one, ls[w & 3], false);
+        lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, pk), one, lsum, false);
       } else {
         constexpr int w = grp;
         uint32_t pk = pack_fp8x4(e[4 * w], e[4 * w + 1], e[4 * w + 2], e[4 * w + 3]);
@@ -574,7 +598,7 @@ __device__ __forceinline__ float fused_step(v16f (&o)[D / 32], const v4i (&qf)[D
         p_new.w[w] = (int)pk;
       }
     } else {
-      l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
+      l_run = F16 ? lsum : l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
       m_run = m_new;
       asm volatile("" : "+v"(l_run));
     }
@@ -598,15 +622,7 @@ __device__ __forceinline__ float fused_step(v16f (&o)[D / 32], const v4i (&qf)[D
     }(), ...);
   }(std::make_integer_sequence<int, Plan::NM>{});
   uops.template operator()<Plan::first_uop(Plan::NM), Plan::NU>();
-  return alpha;
-}
-
-template <int D>
-__device__ __forceinline__ void rescale(v16f (&o)[D / 32], float alpha) {
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) o[cb] *= alpha;
-  }
+  rescale<D>(o, alpha);
 }
 
 // Software pipeline over the KV tiles of one workgroup (4 wavefronts), two
@@ -730,6 +746,11 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   // no masking, every load and MFMA present.  Step j writes K^(j+3) and
   // V(j+1) into the slots read during step j-1.
   int j = 0;
+  // delta_K of the tile whose softmax the next step runs, loaded one step
+  // ahead: a scalar load shares the LDS counter, so waiting for it inside a
+  // step would also wait for every LDS read in flight.  Its wait is placed at
+  // the end of the step instead, where no LDS read is outstanding.
+  float dk_next = ks_bh[min(1, ntiles - 1)];
   for (; j + 4 < nt && j + 2 < nt_full; j += 2) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -740,10 +761,11 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
       v16i(&s_new)[2] = u == 0 ? sA : sB;
       PTile<PV>& p_cur = u == 0 ? pA : pB;
       PTile<PV>& p_new = u == 0 ? pB : pA;
-      const float alpha =
-          fused_step<D, PV>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[u], vbuf[u], m_run, l_run,
-                            tile_scale<PV>(cq, ks_bh[jj + 1]), grid, init, n, hh);
-      rescale<D>(o, alpha);
+      const float dk = dk_next;
+      dk_next = ks_bh[jj + 2];   // jj + 2 < nt: in range
+      fused_step<D, PV>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[u], vbuf[u], m_run, l_run,
+                        tile_scale<PV>(cq, dk), grid, init, n, hh);
+      asm volatile("" ::"s"(dk_next));
       wait_lds_loads();
       __syncthreads();
     }

@@ -38,21 +38,21 @@ __device__ __forceinline__ void rope_pair(float lo, float hi, float c, float s, 
 // 0.0f; with RoPE it owns the two channel pairs (c, c+1) and (c+d/2, c+1+d/2)
 // and adds the rotated values.  Workgroups of 256 threads cover several
 // chunks.
+template <int D, bool ROPE>
+struct ColstatsShape {
+  static constexpr int P = ROPE ? D / 4 : D / 2;   // threads per 256-token chunk
+};
+
 template <int DT, int D, bool DO_K, bool DO_V, bool ROPE>
-__global__ __launch_bounds__(256) void colstats_kernel(const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ v, int N,
-                                                       int H, int nhd, int nchunks,
-                                                       const float* __restrict__ rope_cos,
-                                                       const float* __restrict__ rope_sin,
-                                                       float* __restrict__ part_sum,
-                                                       float* __restrict__ part_max) {
+__device__ __forceinline__ void colstats_chunk(const uint16_t* __restrict__ k,
+                                               const uint16_t* __restrict__ v, int N, int H,
+                                               int nhd, int nchunks,
+                                               const float* __restrict__ rope_cos,
+                                               const float* __restrict__ rope_sin,
+                                               float* __restrict__ part_sum,
+                                               float* __restrict__ part_max, int bh, int chunk,
+                                               int p) {
   constexpr int HD = D / 2;
-  constexpr int P = ROPE ? D / 4 : D / 2;   // threads per chunk
-  constexpr int CPW = 256 / P;
-  const int bh = blockIdx.y;
-  const int p = threadIdx.x % P;
-  const int chunk = blockIdx.x * CPW + threadIdx.x / P;
-  if (chunk >= nchunks) return;
   const int t0 = chunk * kMeanChunk;
   const int cnt = min(kMeanChunk, N - t0);
   const size_t ts = nhd ? (size_t)H * D : (size_t)D;   // token stride (elements)
@@ -132,16 +132,31 @@ __global__ __launch_bounds__(256) void colstats_kernel(const uint16_t* __restric
   }
 }
 
+template <int DT, int D, bool DO_K, bool DO_V, bool ROPE>
+__global__ __launch_bounds__(256) void colstats_kernel(const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v, int N,
+                                                       int H, int nhd, int nchunks,
+                                                       const float* __restrict__ rope_cos,
+                                                       const float* __restrict__ rope_sin,
+                                                       float* __restrict__ part_sum,
+                                                       float* __restrict__ part_max) {
+  constexpr int P = ColstatsShape<D, ROPE>::P;
+  constexpr int CPW = 256 / P;
+  const int chunk = blockIdx.x * CPW + threadIdx.x / P;
+  if (chunk >= nchunks) return;
+  colstats_chunk<DT, D, DO_K, DO_V, ROPE>(k, v, N, H, nhd, nchunks, rope_cos, rope_sin, part_sum,
+                                          part_max, blockIdx.y, chunk, threadIdx.x % P);
+}
+
 // Finalise: mean = (sequential sum of the chunk partials) / N; for FP8 V,
 // colmax = max of the partial maxima, delta_V = colmax/448, r = 448/colmax.
 template <int D, bool DO_K, bool DO_V>
-__global__ __launch_bounds__(128) void finalize_kernel(const float* __restrict__ part_sum,
-                                                       const float* __restrict__ part_max, int N,
-                                                       int nchunks, float* __restrict__ k_mean,
-                                                       float* __restrict__ v_scale,
-                                                       float* __restrict__ v_recip) {
-  const int bh = blockIdx.x;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+__device__ __forceinline__ void finalize_channel(const float* __restrict__ part_sum,
+                                                 const float* __restrict__ part_max, int N,
+                                                 int nchunks, float* __restrict__ k_mean,
+                                                 float* __restrict__ v_scale,
+                                                 float* __restrict__ v_recip, int bh, int c) {
+  {
     if constexpr (DO_K) {
       float tot = 0.f;
 #pragma unroll 16
@@ -158,22 +173,30 @@ __global__ __launch_bounds__(128) void finalize_kernel(const float* __restrict__
   }
 }
 
+template <int D, bool DO_K, bool DO_V>
+__global__ __launch_bounds__(128) void finalize_kernel(const float* __restrict__ part_sum,
+                                                       const float* __restrict__ part_max, int N,
+                                                       int nchunks, float* __restrict__ k_mean,
+                                                       float* __restrict__ v_scale,
+                                                       float* __restrict__ v_recip) {
+  for (int c = threadIdx.x; c < D; c += blockDim.x)
+    finalize_channel<D, DO_K, DO_V>(part_sum, part_max, N, nchunks, k_mean, v_scale, v_recip,
+                                    blockIdx.x, c);
+}
+
 // ---------------------------------------------------------------------------
 // INT8 block quantisation.  One workgroup per block (Q: 128 tokens, K: 64
 // tokens) of one (b, h); a block is a contiguous run of ntok*d elements read
 // as 16-byte chunks.  Values stay in registers between the absmax reduction
 // and the encoding.
 template <int DT, int D, bool ROPE>
-__global__ __launch_bounds__(256) void quant_qk_kernel(
+__device__ __forceinline__ void quant_block(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const float* __restrict__ k_mean, int N, int H, int nhd, int nqb, int nkb, int first_blk,
-    float inv_sqrt_d, const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
+    const float* __restrict__ k_mean, int N, int H, int nhd, int nqb, int nkb, float inv_sqrt_d,
+    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
     int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8, float* __restrict__ q_scale,
-    float* __restrict__ k_scale) {
+    float* __restrict__ k_scale, int bh, int bx, float* red) {
   constexpr int MAXC = kQBlock * D / 8 / 256;   // 16-byte chunks per thread (Q block)
-  __shared__ float red[4];
-  const int bh = blockIdx.y;
-  const int bx = blockIdx.x + first_blk;
   const bool isq = bx < nqb;
   const int blk = isq ? bx : bx - nqb;
   const int btok = isq ? kQBlock : kKBlock;
@@ -272,19 +295,34 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
   }
 }
 
+template <int DT, int D, bool ROPE>
+__global__ __launch_bounds__(256) void quant_qk_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const float* __restrict__ k_mean, int N, int H, int nhd, int nqb, int nkb, int first_blk,
+    float inv_sqrt_d, const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
+    int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8, float* __restrict__ q_scale,
+    float* __restrict__ k_scale) {
+  __shared__ float red[4];
+  quant_block<DT, D, ROPE>(q, k, k_mean, N, H, nhd, nqb, nkb, inv_sqrt_d, rope_cos, rope_sin,
+                           q_i8, k_i8, q_scale, k_scale, blockIdx.y, blockIdx.x + first_blk, red);
+}
+
 // ---------------------------------------------------------------------------
 // V preparation.  One workgroup per 64-key tile of one (b, h): the tile is
 // staged in LDS as raw 16-bit values, then every thread gathers the keys of
 // one output 16-byte chunk (layout documented in sage_attn.h) and converts.
+template <int D>
+struct PrepVTile {
+  static constexpr int LD = D + 8;   // halves per LDS row (16-byte aligned, rotated banks)
+  static constexpr int HALVES = kKvTile * LD;
+};
+
 template <int DT, int D, int PV>
-__global__ __launch_bounds__(256) void prep_v_kernel(const uint16_t* __restrict__ v,
-                                                     const float* __restrict__ v_recip, int N,
-                                                     int H, int nhd, int ntiles,
-                                                     uint8_t* __restrict__ v_out) {
-  constexpr int LD = D + 8;   // halves per LDS row (16-byte aligned, rotated banks)
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kKvTile * LD];
-  const int bh = blockIdx.y;
-  const int t = blockIdx.x;
+__device__ __forceinline__ void prep_v_tile(const uint16_t* __restrict__ v,
+                                            const float* __restrict__ v_recip, int N, int H,
+                                            int nhd, int ntiles, uint8_t* __restrict__ v_out,
+                                            int bh, int t, uint16_t* tile) {
+  constexpr int LD = PrepVTile<D>::LD;
   const int key0 = t * kKvTile;
   constexpr int NCH = kKvTile * D / 8;
   for (int c = threadIdx.x; c < NCH; c += 256) {
@@ -332,6 +370,63 @@ __global__ __launch_bounds__(256) void prep_v_kernel(const uint16_t* __restrict_
         w[e >> 2] = pack_fp8x4(f[0], f[1], f[2], f[3]);
       }
       *reinterpret_cast<uint4*>(out + (size_t)g * 16) = uint4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+template <int DT, int D, int PV>
+__global__ __launch_bounds__(256) void prep_v_kernel(const uint16_t* __restrict__ v,
+                                                     const float* __restrict__ v_recip, int N,
+                                                     int H, int nhd, int ntiles,
+                                                     uint8_t* __restrict__ v_out) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[PrepVTile<D>::HALVES];
+  prep_v_tile<DT, D, PV>(v, v_recip, N, H, nhd, ntiles, v_out, blockIdx.y, blockIdx.x, tile);
+}
+
+// ---------------------------------------------------------------------------
+// Whole prepass of one (b, h) in one workgroup, for short sequences: the same
+// per-chunk, per-channel, per-block and per-tile bodies as the kernels above,
+// run one after another with workgroup barriers between the phases (column
+// statistics -> mean and V scales -> INT8 blocks of Q and K -> V tiles).  One
+// launch instead of four; the arithmetic, and so every bit, is the same.
+template <int DT, int D, int PV, bool ROPE, bool DO_QK, bool DO_V>
+__global__ __launch_bounds__(256) void prepass_head_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int N, int H, int nhd, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, float inv_sqrt_d, float* __restrict__ part_sum,
+    float* __restrict__ part_max, float* __restrict__ k_mean, float* __restrict__ v_scale,
+    float* __restrict__ v_recip, int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8,
+    float* __restrict__ q_scale, float* __restrict__ k_scale, uint8_t* __restrict__ v_out) {
+  constexpr bool VSTAT = DO_V && PV == kPvFp8;   // V column maxima needed
+  __shared__ __attribute__((aligned(16))) uint16_t tile[PrepVTile<D>::HALVES];
+  __shared__ float red[4];
+  const int bh = blockIdx.x;
+  const int nch = (N + kMeanChunk - 1) / kMeanChunk;
+  const int nqb = (N + kQBlock - 1) / kQBlock, nkb = (N + kKBlock - 1) / kKBlock;
+  const int ntiles = (N + kKvTile - 1) / kKvTile;
+  if constexpr (DO_QK || VSTAT) {
+    constexpr int P = ColstatsShape<D, ROPE && DO_QK>::P;
+    for (int w = threadIdx.x; w < nch * P; w += 256)
+      colstats_chunk<DT, D, DO_QK, VSTAT, ROPE && DO_QK>(k, v, N, H, nhd, nch, rope_cos,
+                                                         rope_sin, part_sum, part_max, bh,
+                                                         w / P, w % P);
+    __syncthreads();
+    for (int c = threadIdx.x; c < D; c += 256)
+      finalize_channel<D, DO_QK, VSTAT>(part_sum, part_max, N, nch, k_mean, v_scale, v_recip,
+                                        bh, c);
+    __syncthreads();
+  }
+  if constexpr (DO_QK) {
+    for (int bx = 0; bx < nqb + nkb; ++bx) {
+      quant_block<DT, D, ROPE>(q, k, k_mean, N, H, nhd, nqb, nkb, inv_sqrt_d, rope_cos, rope_sin,
+                               q_i8, k_i8, q_scale, k_scale, bh, bx, red);
+      __syncthreads();   // red is reused by the next block
+    }
+  }
+  if constexpr (DO_V) {
+    for (int t = 0; t < ntiles; ++t) {
+      prep_v_tile<DT, D, PV>(v, v_recip, N, H, nhd, ntiles, v_out, bh, t, tile);
+      __syncthreads();   // the LDS tile is reused by the next one
     }
   }
 }
@@ -431,6 +526,42 @@ hipError_t launch_prep_v(const void* v, const float* v_recip, int dtype, int B, 
   SAGE_PV_CASE(0, 64, 0) SAGE_PV_CASE(0, 64, 1) SAGE_PV_CASE(0, 128, 0) SAGE_PV_CASE(0, 128, 1)
   SAGE_PV_CASE(1, 64, 0) SAGE_PV_CASE(1, 64, 1) SAGE_PV_CASE(1, 128, 0) SAGE_PV_CASE(1, 128, 1)
 #undef SAGE_PV_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int DT, int D, int PV>
+static hipError_t prepass_head_dispatch(const void* q, const void* k, const void* v, int B,
+                                        int H, int N, const InLayout& in, const PrepassOut& o,
+                                        hipStream_t s) {
+  const float isd = (float)(1.0 / __builtin_sqrt((double)D));
+  const bool qk = q != nullptr, dv = v != nullptr, rope = in.rope_cos != nullptr;
+  auto qp = static_cast<const uint16_t*>(q);
+  auto kp = static_cast<const uint16_t*>(k);
+  auto vp = static_cast<const uint16_t*>(v);
+#define SAGE_HEAD(ROPE, QK, DV)                                                               \
+  prepass_head_kernel<DT, D, PV, ROPE, QK, DV><<<B * H, 256, 0, s>>>(                         \
+      qp, kp, vp, N, H, in.nhd, in.rope_cos, in.rope_sin, isd, o.part_sum, o.part_max,        \
+      o.k_mean, o.v_scale, o.v_recip, o.q_i8, o.k_i8, o.q_scale, o.k_scale, o.v_out);
+  if (qk && dv) {
+    if (rope) { SAGE_HEAD(true, true, true) } else { SAGE_HEAD(false, true, true) }
+  } else if (qk) {
+    if (rope) { SAGE_HEAD(true, true, false) } else { SAGE_HEAD(false, true, false) }
+  } else if (dv) {
+    SAGE_HEAD(false, false, true)
+  }
+#undef SAGE_HEAD
+  return hipGetLastError();
+}
+
+hipError_t launch_prepass_head(const void* q, const void* k, const void* v, int dtype, int B,
+                               int H, int N, int d, int pv_mode, const InLayout& in,
+                               const PrepassOut& o, hipStream_t s) {
+#define SAGE_PH(DT, D, PV)                                                     \
+  if (dtype == DT && d == D && pv_mode == PV)                                  \
+    return prepass_head_dispatch<DT, D, PV>(q, k, v, B, H, N, in, o, s);
+  SAGE_PH(0, 64, 0) SAGE_PH(0, 64, 1) SAGE_PH(0, 128, 0) SAGE_PH(0, 128, 1)
+  SAGE_PH(1, 64, 0) SAGE_PH(1, 64, 1) SAGE_PH(1, 128, 0) SAGE_PH(1, 128, 1)
+#undef SAGE_PH
   return hipErrorInvalidValue;
 }
 

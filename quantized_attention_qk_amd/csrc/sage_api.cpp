@@ -121,15 +121,24 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, 
   uint8_t* v_t = w + L.v_t;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fp8 = pv_mode == SAGE_PV_FP8;
-  hipError_t e = sage::launch_colstats(k, fp8 ? v : nullptr, dtype, B, H, N, d, in,
-                                       F(L.part_sum), fp8 ? F(L.part_max) : nullptr, F(L.k_mean),
-                                       F(L.v_scale), F(L.v_recip), s);
-  if (e != hipSuccess) return SAGE_ERR_HIP;
-  e = sage::launch_quant_qk(q, k, F(L.k_mean), dtype, B, H, N, d, in, q_i8, k_i8, F(L.q_scale),
-                            F(L.k_scale), s);
-  if (e != hipSuccess) return SAGE_ERR_HIP;
-  e = sage::launch_prep_v(v, F(L.v_recip), dtype, B, H, N, d, pv_mode, layout, v_t, s);
-  if (e != hipSuccess) return SAGE_ERR_HIP;
+  hipError_t e;
+  if (N <= sage::kHeadPrepassMaxN) {
+    const sage::PrepassOut po{F(L.part_sum), fp8 ? F(L.part_max) : nullptr, F(L.k_mean),
+                              F(L.v_scale), F(L.v_recip), q_i8, k_i8, F(L.q_scale),
+                              F(L.k_scale), v_t};
+    e = sage::launch_prepass_head(q, k, v, dtype, B, H, N, d, pv_mode, in, po, s);
+    if (e != hipSuccess) return SAGE_ERR_HIP;
+  } else {
+    e = sage::launch_colstats(k, fp8 ? v : nullptr, dtype, B, H, N, d, in, F(L.part_sum),
+                              fp8 ? F(L.part_max) : nullptr, F(L.k_mean), F(L.v_scale),
+                              F(L.v_recip), s);
+    if (e != hipSuccess) return SAGE_ERR_HIP;
+    e = sage::launch_quant_qk(q, k, F(L.k_mean), dtype, B, H, N, d, in, q_i8, k_i8,
+                              F(L.q_scale), F(L.k_scale), s);
+    if (e != hipSuccess) return SAGE_ERR_HIP;
+    e = sage::launch_prep_v(v, F(L.v_recip), dtype, B, H, N, d, pv_mode, layout, v_t, s);
+    if (e != hipSuccess) return SAGE_ERR_HIP;
+  }
   e = sage::launch_attn(q_i8, k_i8, v_t, F(L.q_scale), F(L.k_scale), F(L.v_scale), B, H, N, d,
                         causal, pv_mode, out_kind, layout, o, s);
   return hip_status(e);
@@ -224,6 +233,12 @@ int sage_smooth_quant_qk_ex(const void* q, const void* k, int dtype, int layout,
   if ((st = device_check()) != SAGE_OK) return st;
   const sage::InLayout in{layout, rope_cos, rope_sin};
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N <= sage::kHeadPrepassMaxN) {
+    const sage::PrepassOut po{static_cast<float*>(scratch), nullptr, k_mean, nullptr, nullptr,
+                              q_i8, k_i8, q_scale, k_scale, nullptr};
+    return hip_status(sage::launch_prepass_head(q, k, nullptr, dtype, B, H, N, d, SAGE_PV_FP16,
+                                                in, po, s));
+  }
   hipError_t e = sage::launch_colstats(k, nullptr, dtype, B, H, N, d, in,
                                        static_cast<float*>(scratch), nullptr, k_mean, nullptr,
                                        nullptr, s);
@@ -270,11 +285,21 @@ int sage_quant_v_ex(const void* v, int dtype, int layout, int B, int H, int N, i
   if (st != SAGE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* v_recip = nullptr;
+  float* part_max = nullptr;
   if (fp8) {
-    float* part_max = static_cast<float*>(scratch);
+    part_max = static_cast<float*>(scratch);
     v_recip = reinterpret_cast<float*>(
         static_cast<uint8_t*>(scratch) +
         align_up((size_t)B * H * ceil_div(N, sage::kMeanChunk) * d * 4));
+  }
+  if (N <= sage::kHeadPrepassMaxN) {
+    const sage::PrepassOut po{nullptr, part_max, nullptr, v_scale, v_recip, nullptr, nullptr,
+                              nullptr, nullptr, static_cast<uint8_t*>(v_out)};
+    const sage::InLayout in{layout, nullptr, nullptr};
+    return hip_status(sage::launch_prepass_head(nullptr, nullptr, v, dtype, B, H, N, d, pv_mode,
+                                                in, po, s));
+  }
+  if (fp8) {
     const sage::InLayout in{layout, nullptr, nullptr};
     hipError_t e = sage::launch_colstats(nullptr, v, dtype, B, H, N, d, in, nullptr, part_max,
                                          nullptr, v_scale, v_recip, s);

@@ -53,6 +53,10 @@ SMALL = [
     small("s1105", N=1105, d=64, H=1, causal=True, extras="kchan20"),
     small("s640", B=2, H=3, N=640, d=128, dtype="bf16", extras="q8_kbias5"),
     small("s257", N=257, d=128, pv_mode="fp8", extras="none"),
+    # longer than the one-workgroup-per-head prepass handles: the multi-kernel
+    # prepass, with ragged chunk, block and tile tails
+    small("s2113", B=1, H=2, N=2113, d=64, pv_mode="fp8", extras="kbias4"),
+    small("s2177", B=1, H=1, N=2177, d=128, dtype="bf16", causal=True),
 ]
 
 
