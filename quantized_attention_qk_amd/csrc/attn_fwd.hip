@@ -285,6 +285,20 @@ __device__ __forceinline__ TileScale tile_scale(float cq, float dk) {
 // because P^ = 448 P~ must not exceed the E4M3 range.
 constexpr float kLazyMax = 8.0f;
 
+// Steady-state FP16 tiles go further and skip the max: their exps use the
+// running max as it stands, and the row sum, which is computed anyway, checks
+// the result.  When some lane's sum over its 32 keys exceeds this bound (so a
+// P~ of the tile may exceed it, or overflowed FP16 to infinity) the wavefront
+// recomputes the tile's scores from K^ (still in LDS) and takes the max-based
+// rule above; otherwise every P~ of the tile is at most 2^14, well inside FP16
+// range, and the state changes by l += sum only.
+constexpr float kOptimisticSum = 16384.0f;
+
+// K^ tile slots in LDS: three in FP16 mode, so that the tile whose softmax a
+// step runs is still resident when the step may have to recompute its scores.
+template <int PV>
+constexpr int kKSlots = PV == kPvFp16 ? 3 : 2;
+
 // Online softmax of one tile: returns alpha = exp2(m_old - m_new) and writes
 // P~ (FP8: 448 P~) into the MFMA operand.  MASK selects the variant that
 // masks keys >= N and (causal) keys > query; a fully masked tile leaves the
@@ -440,14 +454,30 @@ struct StepPlan {
     for (int i = 0; i < k; ++i) c += is_pv(i) == is_pv(k);
     return c;
   }
-  // softmax micro-ops: NPRE maxima (FP8: with the conversions), one combine,
-  // then the exps and packs, then the finish
-  static constexpr int NPRE = PV == kPvFp16 ? 16 : 48;
+  // softmax micro-ops: NPRE maxima with the conversions (FP8 only: FP16
+  // steady-state tiles skip the max), one combine, then the exps and packs,
+  // then the finish
+  static constexpr int NPRE = PV == kPvFp16 ? 0 : 48;
   static constexpr int NPACK = PV == kPvFp16 ? 16 : 8;
+  // FP16: the 48 exp/pack micro-ops of the 16 score pairs g run as a
+  // three-stage pipeline, arguments (A_g: two fma), exps (B_g) and pack +
+  // row sum (C_g), in the order A_s, B_s-1, C_s-2 for s = 0, 1, ..., so that
+  // no micro-op waits on the one just before it.  op16(v) = (stage, g).
+  struct StageOp { int stage, g; };
+  static constexpr StageOp op16(int v) {
+    int k = 0;
+    for (int s = 0; s < 18; ++s)
+      for (int st = 0; st < 3; ++st) {
+        const int g = s - st;
+        if (g < 0 || g >= 16) continue;
+        if (k++ == v) return StageOp{st, g};
+      }
+    return StageOp{-1, -1};
+  }
   static constexpr int NU = NPRE + 1 + 32 + NPACK + 1;
   // first micro-op of slot k (cumulative instruction weight, spread evenly)
   static constexpr int weight(int u) {
-    return u < NPRE ? 1 : u == NPRE ? (PV == kPvFp16 ? 6 : 10) : u < NPRE + 1 + 32 + NPACK ? 2 : 3;
+    return u < NPRE ? 1 : u == NPRE ? (PV == kPvFp16 ? 1 : 10) : u < NPRE + 1 + 32 + NPACK ? 2 : 3;
   }
   static constexpr int total_weight() {
     int w = 0;
@@ -469,7 +499,8 @@ template <int D, int PV>
 __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D / 32],
                                             v16i (&s_cur)[2], v16i (&s_new)[2],
                                             const PTile<PV>& p_cur, PTile<PV>& p_new,
-                                            const uint8_t* kb, const uint8_t* vb, float& m_run,
+                                            const uint8_t* kb, const uint8_t* kb_prev,
+                                            const uint8_t* vb, float& m_run,
                                             float& l_run, TileScale ts, MaxGrid grid,
                                             const v16i& init, int n, int hh) {
   using Plan = StepPlan<D, PV>;
@@ -527,44 +558,29 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
   constexpr bool F16 = PV == kPvFp16;
   constexpr int NPRE = Plan::NPRE;
   int mpart[4];
-  float f[32], e[32];
+  float f[32], e[32], t[32];
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
   float m_new = 0.f, alpha = 1.f, nb = 0.f, lsum = 0.f;
   auto sc = [&](int i) __attribute__((always_inline)) -> int { return s_cur[i >> 4][i & 15]; };
   auto uop = [&]<int U>() __attribute__((always_inline)) {
     if constexpr (U < NPRE) {
-      // FP16: max of two scores into one of 4 partial maxima.  FP8: triples
-      // of that max and two conversions.
-      constexpr int g = F16 ? U : U / 3, r = F16 ? 0 : U % 3;
-      if constexpr (F16) {
-        // one chain of 3-input maxima (the slots spread it over the step),
-        // written so that each step folds into one v_max3
-        mpart[0] = g == 0 ? max(sc(0), sc(1)) : max(max(mpart[0], sc(2 * g)), sc(2 * g + 1));
-      } else if constexpr (r == 0) {
+      // FP8 only: triples of (max of two scores into one of 4 partial
+      // maxima, two conversions)
+      constexpr int g = U / 3, r = U % 3;
+      if constexpr (r == 0) {
         const int v = max(sc(2 * g), sc(2 * g + 1));
         mpart[g & 3] = g < 4 ? v : max(mpart[g & 3], v);
       } else {
         f[2 * g + r - 1] = (float)sc(2 * g + r - 1);
       }
     } else if constexpr (U == NPRE) {
-      int mx = F16 ? mpart[0] : max(max(mpart[0], mpart[1]), max(mpart[2], mpart[3]));
       if constexpr (F16) {
-        // The row max only matters when it passes the lazy bound, and then
-        // some lane's own max passes it too: only then do the wavefront's
-        // rows combine their two halves and take the rule below.  The result
-        // is the same as applying the rule to every row.
-        m_new = m_run;
-        alpha = 1.f;
-        const float lane_mt = (__builtin_bit_cast(float, mx) - kMagic) * ts.c;
-        if (__builtin_amdgcn_ballot_w64(lane_mt > m_run + kLazyMax)) {
-          mx = pair_max_i32(mx);
-          const float mt = (__builtin_bit_cast(float, mx) - kMagic) * ts.c;
-          m_new = mt > m_run + kLazyMax ? __builtin_ceilf(mt * grid.inv) * grid.step : m_run;
-          alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        }
-        nb = -(ts.k0 + m_new);
-        lsum = l_run * alpha;   // the row sum continues from the rescaled total
+        // exps against the running max as it stands; the row sum continues
+        // from the running total
+        nb = -(ts.k0 + m_run);
+        lsum = l_run;
       } else {
+        int mx = max(max(mpart[0], mpart[1]), max(mpart[2], mpart[3]));
         mx = pair_max_i32(mx);
         const float mt = (float)mx * ts.c;
         m_new = fmaxf(m_run, mt);
@@ -572,33 +588,44 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
         alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       }
     } else if constexpr (U < NPRE + 1 + 32 + Plan::NPACK) {
-      // exp of score i, and after every 2 (FP16) / 4 (FP8) scores their pack
-      constexpr int v = U - NPRE - 1;
-      constexpr int per = F16 ? 3 : 5;   // 2 exps + pack, or 4 exps + pack
-      constexpr int grp = v / per, pos = v % per;
-      constexpr int nper = per - 1;
-      if constexpr (pos < nper) {
-        constexpr int i = grp * nper + pos;
-        const float x = F16 ? __builtin_bit_cast(float, sc(i)) : f[i];
-        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, ts.c, nb));
-        if constexpr (!F16) ls[i & 3] += e[i];
-      } else if constexpr (F16) {
-        constexpr int w = grp;   // pair (2w, 2w+1) -> step w/4, element w%4
-        uint32_t pk = pack_f16x2(e[2 * w], e[2 * w + 1]);
-        // pin: keep this micro-op in its slot (otherwise the backend sinks
-        // the softmax below the rescale branch, out of the MFMA slots)
-        asm volatile("" : "+v"(pk));
-        p_new.w[w >> 2][w & 3] = (int)pk;
-        const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
-        lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, pk), one, lsum, false);
+      if constexpr (F16) {
+        constexpr auto op = Plan::op16(U - NPRE - 1);
+        constexpr int g = op.g;
+        if constexpr (op.stage == 0) {
+          t[2 * g] = __builtin_fmaf(__builtin_bit_cast(float, sc(2 * g)), ts.c, nb);
+          t[2 * g + 1] = __builtin_fmaf(__builtin_bit_cast(float, sc(2 * g + 1)), ts.c, nb);
+        } else if constexpr (op.stage == 1) {
+          e[2 * g] = __builtin_amdgcn_exp2f(t[2 * g]);
+          e[2 * g + 1] = __builtin_amdgcn_exp2f(t[2 * g + 1]);
+        } else {
+          // pair (2g, 2g+1) -> step g/4, element g%4
+          uint32_t pk = pack_f16x2(e[2 * g], e[2 * g + 1]);
+          // pin: keep this micro-op in its slot (otherwise the backend sinks
+          // the softmax below the branch, out of the MFMA slots)
+          asm volatile("" : "+v"(pk));
+          p_new.w[g >> 2][g & 3] = (int)pk;
+          const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
+          lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, pk), one, lsum, false);
+        }
       } else {
-        constexpr int w = grp;
-        uint32_t pk = pack_fp8x4(e[4 * w], e[4 * w + 1], e[4 * w + 2], e[4 * w + 3]);
-        asm volatile("" : "+v"(pk));
-        p_new.w[w] = (int)pk;
+        // FP8: exp of score i, and after every 4 scores their pack
+        constexpr int v = U - NPRE - 1;
+        constexpr int grp = v / 5, pos = v % 5;   // 4 exps + pack
+        if constexpr (pos < 4) {
+          constexpr int i = grp * 4 + pos;
+          e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[i], ts.c, nb));
+          ls[i & 3] += e[i];
+        } else {
+          constexpr int w = grp;
+          uint32_t pk = pack_fp8x4(e[4 * w], e[4 * w + 1], e[4 * w + 2], e[4 * w + 3]);
+          asm volatile("" : "+v"(pk));
+          p_new.w[w] = (int)pk;
+        }
       }
+    } else if constexpr (F16) {
+      asm volatile("" : "+v"(lsum));
     } else {
-      l_run = F16 ? lsum : l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
+      l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
       m_run = m_new;
       asm volatile("" : "+v"(l_run));
     }
@@ -622,7 +649,20 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
     }(), ...);
   }(std::make_integer_sequence<int, Plan::NM>{});
   uops.template operator()<Plan::first_uop(Plan::NM), Plan::NU>();
-  rescale<D>(o, alpha);
+  if constexpr (F16) {
+    // the tile's sum lsum - l_run bounds each of its P~ (infinity included)
+    if (__builtin_amdgcn_ballot_w64(!(lsum - l_run <= kOptimisticSum))) {
+      // rare: recompute the tile's scores (into the registers they came in,
+      // free by now) and take the max-based rule
+      qk_tile<D>(s_cur, qf, kb_prev, n, hh, init);
+      rescale<D>(o, softmax_tile<PV, false, false>(s_cur, m_run, l_run, p_new, ts, grid, 0, 0,
+                                                   0, hh));
+    } else {
+      l_run = lsum;
+    }
+  } else {
+    rescale<D>(o, alpha);
+  }
 }
 
 // Software pipeline over the KV tiles of one workgroup (4 wavefronts), two
@@ -632,7 +672,8 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
 //     O     += P~(j) V(j)           [FP16/FP8 MFMA]
 //     softmax(S(j+1)) -> P~(j+1)    [VALU, independent of both]
 // then rescales O by alpha(j+1).  K^ tile j+3 and V tile j+1 are loaded from
-// HBM during step j and written to LDS after its compute (double buffers,
+// HBM during step j straight into LDS (V double-buffered; K^ in three slots
+// in FP16 mode, so K^(j+1) is still there if step j must recompute S(j+1);
 // one barrier per step).  All wavefronts run every step of the workgroup; a
 // causal tile beyond a wavefront's last row is fully masked and changes
 // nothing.
@@ -646,7 +687,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   constexpr int KB = KTile<D>::BYTES;
   constexpr int VB = VTile<D, PV>::BYTES;
   constexpr int NCB = D / 32;   // 32-channel blocks of the output
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KB];
+  constexpr int NKS = kKSlots<PV>;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[NKS][KB];
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][VB];
 
   // Workgroup -> (b*h, query block).
@@ -710,7 +752,12 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   using VL = VLoader<D, PV, kWaves>;
   const v4i krs = buffer_rsrc(k_bh, N * D);
   const v4i vrs = buffer_rsrc(v_bh, ntiles * VB);
-  const uint32_t kl[2] = {lds_addr(kbuf[0]), lds_addr(kbuf[1])};
+  // K^ tile t lives in slot t % NKS (tile indices here are wavefront-uniform;
+  // with two slots and an even j, the slot of tile j + u + c is (u + c) & 1)
+  auto kslot = [&](int t, int u_plus_c) __attribute__((always_inline)) {
+    return NKS == 2 ? (u_plus_c & 1) : t % NKS;
+  };
+  const uint32_t kl0 = lds_addr(kbuf[0]);
   const uint32_t vl[2] = {lds_addr(vbuf[0]), lds_addr(vbuf[1])};
   float m_run = -__builtin_inff();
   float l_run = 0.f;
@@ -729,16 +776,16 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   };
 
   // Prologue: S(0), S(1), P~(0); then K^(2) into the slot of K^(0).
-  kld.template issue<true>(krs, 0, N, kl[0], wave);
+  kld.template issue<true>(krs, 0, N, kl0, wave);
   VL::issue(vrs, 0, vl[0], wave, lane);
-  if (nt > 1) kld.template issue<true>(krs, kKvTile, N, kl[1], wave);
+  if (nt > 1) kld.template issue<true>(krs, kKvTile, N, kl0 + KB, wave);
   wait_lds_loads();
   __syncthreads();
   qk_tile<D>(sA, qf, kbuf[0], n, hh, init);
   if (nt > 1) qk_tile<D>(sB, qf, kbuf[1], n, hh, init);
   softmax_any(sA, pA, 0);   // alpha irrelevant: O is still zero
   __syncthreads();          // every wave has read K^(0)
-  if (nt > 2) kld.template issue<true>(krs, 2 * kKvTile, N, kl[0], wave);
+  if (nt > 2) kld.template issue<true>(krs, 2 * kKvTile, N, kl0 + kslot(2, 2) * KB, wave);
   wait_lds_loads();
   __syncthreads();
 
@@ -755,7 +802,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int jj = j + u;
-      kld.template issue<false>(krs, (jj + 3) * kKvTile, N, kl[1 - u], wave);
+      kld.template issue<false>(krs, (jj + 3) * kKvTile, N, kl0 + kslot(jj + 3, u + 3) * KB,
+                                wave);
       VL::issue(vrs, jj + 1, vl[1 - u], wave, lane);
       v16i(&s_cur)[2] = u == 0 ? sB : sA;
       v16i(&s_new)[2] = u == 0 ? sA : sB;
@@ -763,7 +811,11 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
       PTile<PV>& p_new = u == 0 ? pB : pA;
       const float dk = dk_next;
       dk_next = ks_bh[jj + 2];   // jj + 2 < nt: in range
-      fused_step<D, PV>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[u], vbuf[u], m_run, l_run,
+      // FP16: keep the accumulator start value resident (not rebuilt every
+      // step); in FP8 mode it is zero, an inline constant
+      if constexpr (PV == kPvFp16) asm volatile("" : "+v"(init));
+      fused_step<D, PV>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[kslot(jj + 2, u + 2)],
+                        kbuf[kslot(jj + 1, u + 1)], vbuf[u], m_run, l_run,
                         tile_scale<PV>(cq, dk), grid, init, n, hh);
       asm volatile("" ::"s"(dk_next));
       wait_lds_loads();
@@ -776,13 +828,15 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     for (int u = 0; u < 2; ++u) {
       const int jj = j + u;
       if (jj < nt) {
-        if (jj + 3 < nt) kld.template issue<true>(krs, (jj + 3) * kKvTile, N, kl[1 - u], wave);
+        if (jj + 3 < nt)
+          kld.template issue<true>(krs, (jj + 3) * kKvTile, N, kl0 + kslot(jj + 3, u + 3) * KB,
+                                   wave);
         if (jj + 1 < nt) VL::issue(vrs, jj + 1, vl[1 - u], wave, lane);
         v16i(&s_cur)[2] = u == 0 ? sB : sA;
         v16i(&s_new)[2] = u == 0 ? sA : sB;
         PTile<PV>& p_cur = u == 0 ? pA : pB;
         PTile<PV>& p_new = u == 0 ? pB : pA;
-        if (jj + 2 < nt) qk_tile<D>(s_new, qf, kbuf[u], n, hh, init);
+        if (jj + 2 < nt) qk_tile<D>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init);
         pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh);
         if (jj + 1 < nt) rescale<D>(o, softmax_any(s_cur, p_new, jj + 1));
         wait_lds_loads();
