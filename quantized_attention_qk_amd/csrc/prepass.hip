@@ -43,7 +43,7 @@ struct ColstatsShape {
   static constexpr int P = ROPE ? D / 4 : D / 2;   // threads per 256-token chunk
 };
 
-template <int DT, int D, bool DO_K, bool DO_V, bool ROPE>
+template <int DT, int D, bool DO_K, bool DO_V, bool ROPE, int UNR = 16>
 __device__ __forceinline__ void colstats_chunk(const uint16_t* __restrict__ k,
                                                const uint16_t* __restrict__ v, int N, int H,
                                                int nhd, int nchunks,
@@ -58,34 +58,39 @@ __device__ __forceinline__ void colstats_chunk(const uint16_t* __restrict__ k,
   const size_t ts = nhd ? (size_t)H * D : (size_t)D;   // token stride (elements)
   const size_t base = row_off<D>(bh, t0, H, N, nhd) + 2 * p;
   const size_t out = ((size_t)bh * nchunks + chunk) * D + 2 * p;
+  // Loads are issued in batches of UNR tokens (those at or past the chunk's
+  // end are skipped) before the batch is added in token order.
   if constexpr (!ROPE) {
     if constexpr (DO_K) {
       const uint16_t* kp = k + base;
       float s0 = 0.f, s1 = 0.f;
-      if (cnt == kMeanChunk) {
-#pragma unroll 16
-        for (int t = 0; t < kMeanChunk; ++t) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(kp + t * ts);
-          s0 += in_to_f32<DT>((uint16_t)(w & 0xffffu));
-          s1 += in_to_f32<DT>((uint16_t)(w >> 16));
-        }
-      } else {
-        for (int t = 0; t < cnt; ++t) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(kp + t * ts);
-          s0 += in_to_f32<DT>((uint16_t)(w & 0xffffu));
-          s1 += in_to_f32<DT>((uint16_t)(w >> 16));
-        }
+      for (int t0 = 0; t0 < cnt; t0 += UNR) {
+        uint32_t w[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+          w[u] = t0 + u < cnt ? *reinterpret_cast<const uint32_t*>(kp + (t0 + u) * ts) : 0u;
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+          if (t0 + u < cnt) {
+            s0 += in_to_f32<DT>((uint16_t)(w[u] & 0xffffu));
+            s1 += in_to_f32<DT>((uint16_t)(w[u] >> 16));
+          }
       }
       *reinterpret_cast<v2f*>(part_sum + out) = v2f{s0, s1};
     }
     if constexpr (DO_V) {
       const uint16_t* vp = v + base;
       float m0 = 0.f, m1 = 0.f;
-#pragma unroll 16
-      for (int t = 0; t < cnt; ++t) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(vp + t * ts);
-        m0 = fmaxf(m0, fabsf(in_to_f32<DT>((uint16_t)(w & 0xffffu))));
-        m1 = fmaxf(m1, fabsf(in_to_f32<DT>((uint16_t)(w >> 16))));
+      for (int t0 = 0; t0 < cnt; t0 += UNR) {
+        uint32_t w[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+          w[u] = t0 + u < cnt ? *reinterpret_cast<const uint32_t*>(vp + (t0 + u) * ts) : 0u;
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {   // a skipped token reads 0, which changes no maximum
+          m0 = fmaxf(m0, fabsf(in_to_f32<DT>((uint16_t)(w[u] & 0xffffu))));
+          m1 = fmaxf(m1, fabsf(in_to_f32<DT>((uint16_t)(w[u] >> 16))));
+        }
       }
       *reinterpret_cast<v2f*>(part_max + out) = v2f{m0, m1};
     }
@@ -95,21 +100,31 @@ __device__ __forceinline__ void colstats_chunk(const uint16_t* __restrict__ k,
       const float* cp = rope_cos + (size_t)t0 * HD + 2 * p;
       const float* sp = rope_sin + (size_t)t0 * HD + 2 * p;
       float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll 8
-      for (int t = 0; t < cnt; ++t) {
-        const uint32_t lo = *reinterpret_cast<const uint32_t*>(kp + t * ts);
-        const uint32_t hi = *reinterpret_cast<const uint32_t*>(kp + t * ts + HD);
-        const v2f c = *reinterpret_cast<const v2f*>(cp + (size_t)t * HD);
-        const v2f sn = *reinterpret_cast<const v2f*>(sp + (size_t)t * HD);
-        float r0, r1, r2, r3;
-        rope_pair(in_to_f32<DT>((uint16_t)(lo & 0xffffu)), in_to_f32<DT>((uint16_t)(hi & 0xffffu)),
-                  c[0], sn[0], r0, r2);
-        rope_pair(in_to_f32<DT>((uint16_t)(lo >> 16)), in_to_f32<DT>((uint16_t)(hi >> 16)), c[1],
-                  sn[1], r1, r3);
-        s0 += r0;
-        s1 += r1;
-        s2 += r2;
-        s3 += r3;
+      constexpr int RB = 8;   // tokens per batch of loads (four loads each)
+      for (int t0 = 0; t0 < cnt; t0 += RB) {
+        uint32_t lo[RB], hi[RB];
+        v2f c[RB], sn[RB];
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          const int t = min(t0 + u, cnt - 1);   // a skipped token re-reads the last one
+          lo[u] = *reinterpret_cast<const uint32_t*>(kp + t * ts);
+          hi[u] = *reinterpret_cast<const uint32_t*>(kp + t * ts + HD);
+          c[u] = *reinterpret_cast<const v2f*>(cp + (size_t)t * HD);
+          sn[u] = *reinterpret_cast<const v2f*>(sp + (size_t)t * HD);
+        }
+#pragma unroll
+        for (int u = 0; u < RB; ++u)
+          if (t0 + u < cnt) {
+            float r0, r1, r2, r3;
+            rope_pair(in_to_f32<DT>((uint16_t)(lo[u] & 0xffffu)),
+                      in_to_f32<DT>((uint16_t)(hi[u] & 0xffffu)), c[u][0], sn[u][0], r0, r2);
+            rope_pair(in_to_f32<DT>((uint16_t)(lo[u] >> 16)), in_to_f32<DT>((uint16_t)(hi[u] >> 16)),
+                      c[u][1], sn[u][1], r1, r3);
+            s0 += r0;
+            s1 += r1;
+            s2 += r2;
+            s3 += r3;
+          }
       }
       *reinterpret_cast<v2f*>(part_sum + out) = v2f{s0, s1};
       *reinterpret_cast<v2f*>(part_sum + out + HD) = v2f{s2, s3};
@@ -352,7 +367,7 @@ __device__ __forceinline__ void prep_v_tile(const uint16_t* __restrict__ v,
       *reinterpret_cast<uint4*>(out + (size_t)g * 16) = uint4{w[0], w[1], w[2], w[3]};
     }
   } else {
-    const float* rc = v_recip + (size_t)bh * D;
+    const float* rc = v_recip;   // this head's 448/colmax, d entries
     for (int g = threadIdx.x; g < D * 4; g += 256) {
       const int c = g >> 2;
       const int lq = (g & 3) ^ row_swizzle<64>(c);
@@ -380,53 +395,200 @@ __global__ __launch_bounds__(256) void prep_v_kernel(const uint16_t* __restrict_
                                                      int H, int nhd, int ntiles,
                                                      uint8_t* __restrict__ v_out) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[PrepVTile<D>::HALVES];
-  prep_v_tile<DT, D, PV>(v, v_recip, N, H, nhd, ntiles, v_out, blockIdx.y, blockIdx.x, tile);
+  prep_v_tile<DT, D, PV>(v, PV == kPvFp8 ? v_recip + (size_t)blockIdx.y * D : nullptr, N, H, nhd,
+                         ntiles, v_out, blockIdx.y, blockIdx.x, tile);
 }
 
 // ---------------------------------------------------------------------------
-// Whole prepass of one (b, h) in one workgroup, for short sequences: the same
-// per-chunk, per-channel, per-block and per-tile bodies as the kernels above,
-// run one after another with workgroup barriers between the phases (column
-// statistics -> mean and V scales -> INT8 blocks of Q and K -> V tiles).  One
-// launch instead of four; the arithmetic, and so every bit, is the same.
+// One-launch prepass for short sequences.  Workgroups take roles, ordered so
+// that the longest ones start first:
+//   role 0 of a head     K: column sums -> mean -> all K^ blocks of the head,
+//                        each wavefront quantising its own blocks;
+//   roles 1 .. nqb       one Q^ block each (no statistics needed);
+//   then ntiles roles    one V tile each (FP8: the tile's workgroup takes the
+//                        head's column maxima itself).
+// Every value is computed by the same expressions, in the same order, as in
+// the multi-kernel path above (a maximum does not depend on order), so the
+// results are identical bit for bit.
+
+// K^ block blk of head bh by one wavefront.  Every lane owns the same 8
+// channels in all of its chunks (64 * 8 is a multiple of d); the block is read
+// twice, once for the absmax and once for the encoding, to keep registers low.
+template <int DT, int D, bool ROPE>
+__device__ __forceinline__ void kblock_x8(const uint16_t* __restrict__ k, int bh, int tok, int N,
+                                          int H, int nhd, int ch0, const float (&mu)[8],
+                                          const float* __restrict__ rope_cos,
+                                          const float* __restrict__ rope_sin, float (&x)[8]) {
+  constexpr int HD = D / 2;
+  const uint16_t* row = k + row_off<D>(bh, tok, H, N, nhd);
+  const uint4 raw = *reinterpret_cast<const uint4*>(row + ch0);
+  const uint32_t ww[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t pp[4] = {0u, 0u, 0u, 0u};
+  v4f cs[2], sn[2];
+  if constexpr (ROPE) {
+    const uint4 par = *reinterpret_cast<const uint4*>(row + (ch0 + HD) % D);
+    pp[0] = par.x; pp[1] = par.y; pp[2] = par.z; pp[3] = par.w;
+    const size_t toff = (size_t)tok * HD + (ch0 % HD);
+    cs[0] = *reinterpret_cast<const v4f*>(rope_cos + toff);
+    cs[1] = *reinterpret_cast<const v4f*>(rope_cos + toff + 4);
+    sn[0] = *reinterpret_cast<const v4f*>(rope_sin + toff);
+    sn[1] = *reinterpret_cast<const v4f*>(rope_sin + toff + 4);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float f = in_to_f32<DT>((uint16_t)(ww[e >> 1] >> ((e & 1) * 16)));
+    if constexpr (ROPE) {
+      const float g = in_to_f32<DT>((uint16_t)(pp[e >> 1] >> ((e & 1) * 16)));
+      const float c = cs[e >> 2][e & 3], sv = sn[e >> 2][e & 3];
+      const bool low = ch0 < HD;
+      float rl, rh;
+      rope_pair(low ? f : g, low ? g : f, c, sv, rl, rh);
+      f = low ? rl : rh;
+    }
+    x[e] = f * 1.0f - mu[e];   // as the block quantiser: scale 1 for K, one rounding
+  }
+}
+
+template <int DT, int D, bool ROPE>
+__device__ __forceinline__ void quant_kblock_wave(
+    const uint16_t* __restrict__ k, const float* __restrict__ k_mean, int N, int H, int nhd,
+    int nkb, const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
+    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, int bh, int blk, int lane) {
+  constexpr int CPR = D / 8;                  // chunks per token row
+  constexpr int CPL = kKBlock * CPR / 64;     // chunks per lane
+  const int tok0 = blk * kKBlock;
+  const int ntok = min(kKBlock, N - tok0);
+  const int ch0 = (lane * 8) % D;
+  const float* mean = k_mean + (size_t)bh * D;
+  float mu[8];
+  {
+    const v4f m0 = *reinterpret_cast<const v4f*>(mean + ch0);
+    const v4f m1 = *reinterpret_cast<const v4f*>(mean + ch0 + 4);
+    mu[0] = m0[0]; mu[1] = m0[1]; mu[2] = m0[2]; mu[3] = m0[3];
+    mu[4] = m1[0]; mu[5] = m1[1]; mu[6] = m1[2]; mu[7] = m1[3];
+  }
+  float amax = 0.f;
+#pragma unroll 4
+  for (int i = 0; i < CPL; ++i) {
+    const int r = (lane + 64 * i) / CPR;
+    if (r < ntok) {
+      float x[8];
+      kblock_x8<DT, D, ROPE>(k, bh, tok0 + r, N, H, nhd, ch0, mu, rope_cos, rope_sin, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    }
+  }
+  const float a = wave_max(amax);
+  const float rcp = a > 0.f ? 127.f / a : 0.f;
+  int8_t* dst = k_i8 + ((size_t)bh * N + tok0) * D;
+#pragma unroll 4
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    const int r = c / CPR;
+    if (r < ntok) {
+      float x[8];
+      kblock_x8<DT, D, ROPE>(k, bh, tok0 + r, N, H, nhd, ch0, mu, rope_cos, rope_sin, x);
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float t = __builtin_rintf(x[e] * rcp);
+        t = fminf(fmaxf(t, -127.f), 127.f);
+        packed[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)t) << ((e & 3) * 8);
+      }
+      *reinterpret_cast<uint2*>(dst + (size_t)c * 8) = uint2{packed[0], packed[1]};
+    }
+  }
+  if (lane == 0) k_scale[(size_t)bh * nkb + blk] = a / 127.f;
+}
+
+// Column maxima |V| of head bh over all N tokens, by the whole workgroup, into
+// vmax[D] (LDS); part[4][D] is LDS scratch.
+template <int DT, int D>
+__device__ __forceinline__ void head_colmax(const uint16_t* __restrict__ v, int bh, int N, int H,
+                                            int nhd, float* part, float* vmax) {
+  constexpr int CPR = D / 8;
+  constexpr int RPP = 256 / CPR;   // token rows per pass of the workgroup
+  const int tid = threadIdx.x;
+  const int cc = tid % CPR, r0 = tid / CPR;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int t = r0; t < N; t += RPP) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(v + row_off<D>(bh, t, H, N, nhd) + cc * 8);
+    const uint32_t ww[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      m[e] = fmaxf(m[e], fabsf(in_to_f32<DT>((uint16_t)(ww[e >> 1] >> ((e & 1) * 16)))));
+  }
+  // lanes l and l + CPR*j of a wavefront hold the same channels
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    for (int off = CPR; off < 64; off <<= 1) m[e] = fmaxf(m[e], __shfl_xor(m[e], off, 64));
+  const int wave = tid >> 6, lane = tid & 63;
+  if (lane < CPR)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[wave * D + lane * 8 + e] = m[e];
+  __syncthreads();
+  for (int c = tid; c < D; c += 256)
+    vmax[c] = fmaxf(fmaxf(part[c], part[D + c]), fmaxf(part[2 * D + c], part[3 * D + c]));
+  __syncthreads();
+}
+
 template <int DT, int D, int PV, bool ROPE, bool DO_QK, bool DO_V>
-__global__ __launch_bounds__(256) void prepass_head_kernel(
+__global__ __launch_bounds__(256) void prepass_roles_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int N, int H, int nhd, const float* __restrict__ rope_cos,
-    const float* __restrict__ rope_sin, float inv_sqrt_d, float* __restrict__ part_sum,
-    float* __restrict__ part_max, float* __restrict__ k_mean, float* __restrict__ v_scale,
-    float* __restrict__ v_recip, int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8,
-    float* __restrict__ q_scale, float* __restrict__ k_scale, uint8_t* __restrict__ v_out) {
-  constexpr bool VSTAT = DO_V && PV == kPvFp8;   // V column maxima needed
+    const uint16_t* __restrict__ v, int N, int H, int BH, int nhd,
+    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, float inv_sqrt_d,
+    float* __restrict__ part_sum, float* __restrict__ k_mean, float* __restrict__ v_scale,
+    int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8, float* __restrict__ q_scale,
+    float* __restrict__ k_scale, uint8_t* __restrict__ v_out) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[PrepVTile<D>::HALVES];
   __shared__ float red[4];
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x % BH;
+  int role = blockIdx.x / BH;
   const int nch = (N + kMeanChunk - 1) / kMeanChunk;
   const int nqb = (N + kQBlock - 1) / kQBlock, nkb = (N + kKBlock - 1) / kKBlock;
   const int ntiles = (N + kKvTile - 1) / kKvTile;
-  if constexpr (DO_QK || VSTAT) {
-    constexpr int P = ColstatsShape<D, ROPE && DO_QK>::P;
-    for (int w = threadIdx.x; w < nch * P; w += 256)
-      colstats_chunk<DT, D, DO_QK, VSTAT, ROPE && DO_QK>(k, v, N, H, nhd, nch, rope_cos,
-                                                         rope_sin, part_sum, part_max, bh,
-                                                         w / P, w % P);
-    __syncthreads();
-    for (int c = threadIdx.x; c < D; c += 256)
-      finalize_channel<D, DO_QK, VSTAT>(part_sum, part_max, N, nch, k_mean, v_scale, v_recip,
-                                        bh, c);
-    __syncthreads();
-  }
   if constexpr (DO_QK) {
-    for (int bx = 0; bx < nqb + nkb; ++bx) {
-      quant_block<DT, D, ROPE>(q, k, k_mean, N, H, nhd, nqb, nkb, inv_sqrt_d, rope_cos, rope_sin,
-                               q_i8, k_i8, q_scale, k_scale, bh, bx, red);
-      __syncthreads();   // red is reused by the next block
+    if (role == 0) {
+      constexpr int P = ColstatsShape<D, ROPE>::P;
+      for (int w = threadIdx.x; w < nch * P; w += 256)
+        colstats_chunk<DT, D, true, false, ROPE, 32>(k, nullptr, N, H, nhd, nch, rope_cos,
+                                                     rope_sin, part_sum, nullptr, bh, w / P,
+                                                     w % P);
+      __syncthreads();
+      for (int c = threadIdx.x; c < D; c += 256)
+        finalize_channel<D, true, false>(part_sum, nullptr, N, nch, k_mean, nullptr, nullptr,
+                                         bh, c);
+      __syncthreads();
+      const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+      for (int blk = wave; blk < nkb; blk += 4)
+        quant_kblock_wave<DT, D, ROPE>(k, k_mean, N, H, nhd, nkb, rope_cos, rope_sin, k_i8,
+                                       k_scale, bh, blk, lane);
+      return;
     }
+    role -= 1;
+    if (role < nqb) {   // a Q block: quant_block's index bx < nqb selects Q
+      quant_block<DT, D, ROPE>(q, k, k_mean, N, H, nhd, nqb, nkb, inv_sqrt_d, rope_cos,
+                               rope_sin, q_i8, k_i8, q_scale, k_scale, bh, role, red);
+      return;
+    }
+    role -= nqb;
   }
   if constexpr (DO_V) {
-    for (int t = 0; t < ntiles; ++t) {
-      prep_v_tile<DT, D, PV>(v, v_recip, N, H, nhd, ntiles, v_out, bh, t, tile);
-      __syncthreads();   // the LDS tile is reused by the next one
+    if (role >= ntiles) return;
+    if constexpr (PV == kPvFp8) {
+      __shared__ float part[4 * D], vrc[D];
+      head_colmax<DT, D>(v, bh, N, H, nhd, part, vrc);
+      // the same expressions as the finalisation of the multi-kernel path
+      for (int c = threadIdx.x; c < D; c += 256) {
+        const float cm = vrc[c];
+        if (role == 0) v_scale[(size_t)bh * D + c] = cm / 448.f;
+        vrc[c] = cm > 0.f ? 448.f / cm : 0.f;
+      }
+      __syncthreads();
+      prep_v_tile<DT, D, PV>(v, vrc, N, H, nhd, ntiles, v_out, bh, role, tile);
+    } else {
+      prep_v_tile<DT, D, PV>(v, nullptr, N, H, nhd, ntiles, v_out, bh, role, tile);
     }
   }
 }
@@ -535,13 +697,17 @@ static hipError_t prepass_head_dispatch(const void* q, const void* k, const void
                                         hipStream_t s) {
   const float isd = (float)(1.0 / __builtin_sqrt((double)D));
   const bool qk = q != nullptr, dv = v != nullptr, rope = in.rope_cos != nullptr;
+  const int BH = B * H;
+  const int roles = (qk ? 1 + ceil_div(N, kQBlock) : 0) + (dv ? ceil_div(N, kKvTile) : 0);
+  const long long grid = (long long)BH * roles;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   auto qp = static_cast<const uint16_t*>(q);
   auto kp = static_cast<const uint16_t*>(k);
   auto vp = static_cast<const uint16_t*>(v);
-#define SAGE_HEAD(ROPE, QK, DV)                                                               \
-  prepass_head_kernel<DT, D, PV, ROPE, QK, DV><<<B * H, 256, 0, s>>>(                         \
-      qp, kp, vp, N, H, in.nhd, in.rope_cos, in.rope_sin, isd, o.part_sum, o.part_max,        \
-      o.k_mean, o.v_scale, o.v_recip, o.q_i8, o.k_i8, o.q_scale, o.k_scale, o.v_out);
+#define SAGE_HEAD(ROPE, QK, DV)                                                                \
+  prepass_roles_kernel<DT, D, PV, ROPE, QK, DV><<<dim3((unsigned)grid), 256, 0, s>>>(          \
+      qp, kp, vp, N, H, BH, in.nhd, in.rope_cos, in.rope_sin, isd, o.part_sum, o.k_mean,       \
+      o.v_scale, o.q_i8, o.k_i8, o.q_scale, o.k_scale, o.v_out);
   if (qk && dv) {
     if (rope) { SAGE_HEAD(true, true, true) } else { SAGE_HEAD(false, true, true) }
   } else if (qk) {

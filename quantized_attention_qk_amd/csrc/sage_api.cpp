@@ -123,9 +123,8 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, 
   const bool fp8 = pv_mode == SAGE_PV_FP8;
   hipError_t e;
   if (N <= sage::kHeadPrepassMaxN) {
-    const sage::PrepassOut po{F(L.part_sum), fp8 ? F(L.part_max) : nullptr, F(L.k_mean),
-                              F(L.v_scale), F(L.v_recip), q_i8, k_i8, F(L.q_scale),
-                              F(L.k_scale), v_t};
+    const sage::PrepassOut po{F(L.part_sum), F(L.k_mean), F(L.v_scale), q_i8, k_i8,
+                              F(L.q_scale), F(L.k_scale), v_t};
     e = sage::launch_prepass_head(q, k, v, dtype, B, H, N, d, pv_mode, in, po, s);
     if (e != hipSuccess) return SAGE_ERR_HIP;
   } else {
@@ -234,8 +233,8 @@ int sage_smooth_quant_qk_ex(const void* q, const void* k, int dtype, int layout,
   const sage::InLayout in{layout, rope_cos, rope_sin};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (N <= sage::kHeadPrepassMaxN) {
-    const sage::PrepassOut po{static_cast<float*>(scratch), nullptr, k_mean, nullptr, nullptr,
-                              q_i8, k_i8, q_scale, k_scale, nullptr};
+    const sage::PrepassOut po{static_cast<float*>(scratch), k_mean, nullptr, q_i8, k_i8,
+                              q_scale, k_scale, nullptr};
     return hip_status(sage::launch_prepass_head(q, k, nullptr, dtype, B, H, N, d, SAGE_PV_FP16,
                                                 in, po, s));
   }
@@ -293,8 +292,8 @@ int sage_quant_v_ex(const void* v, int dtype, int layout, int B, int H, int N, i
         align_up((size_t)B * H * ceil_div(N, sage::kMeanChunk) * d * 4));
   }
   if (N <= sage::kHeadPrepassMaxN) {
-    const sage::PrepassOut po{nullptr, part_max, nullptr, v_scale, v_recip, nullptr, nullptr,
-                              nullptr, nullptr, static_cast<uint8_t*>(v_out)};
+    const sage::PrepassOut po{nullptr, nullptr, v_scale, nullptr, nullptr, nullptr, nullptr,
+                              static_cast<uint8_t*>(v_out)};
     const sage::InLayout in{layout, nullptr, nullptr};
     return hip_status(sage::launch_prepass_head(nullptr, nullptr, v, dtype, B, H, N, d, pv_mode,
                                                 in, po, s));

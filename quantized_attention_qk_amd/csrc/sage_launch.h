@@ -55,13 +55,11 @@ hipError_t launch_quant_qk(const void* q, const void* k, const float* k_mean, in
 hipError_t launch_prep_v(const void* v, const float* v_recip, int dtype, int B, int H, int N,
                          int d, int pv_mode, int nhd, uint8_t* v_out, hipStream_t s);
 
-// Outputs of the prepass (any may be null when its stage is skipped).
+// Outputs of the one-launch prepass (any may be null when its stage is skipped).
 struct PrepassOut {
   float* part_sum;   // float32 [B*H, ceil(N/256), d] column partial sums of K
-  float* part_max;   // float32 [B*H, ceil(N/256), d] column partial maxima of |V| (FP8)
   float* k_mean;
   float* v_scale;
-  float* v_recip;
   int8_t* q_i8;
   int8_t* k_i8;
   float* q_scale;
@@ -69,12 +67,11 @@ struct PrepassOut {
   uint8_t* v_out;
 };
 
-// Sequences up to this length run the whole prepass of a head in one
-// workgroup (one launch instead of four).
+// Sequences up to this length run the prepass in one launch whose workgroups
+// take roles: one per head for the K statistics and K^ blocks, one per Q^
+// block, one per V tile.
 constexpr int kHeadPrepassMaxN = 2048;
 
-// Prepass of every (b, h) in one launch: K statistics, mean, INT8 Q and K
-// (when q != null; k must then be non-null), V preparation (when v != null).
 hipError_t launch_prepass_head(const void* q, const void* k, const void* v, int dtype, int B,
                                int H, int N, int d, int pv_mode, const InLayout& in,
                                const PrepassOut& o, hipStream_t s);
