@@ -60,6 +60,25 @@ def e4m3_decode(code) -> np.ndarray:
     return s * val
 
 
+def e4m3_flip_step(y, rel) -> np.ndarray:
+    """For values y >= 0 (as encoded by e4m3_encode), the size of the change of
+    the decoded value if y rounded to its other neighbouring code, wherever y
+    lies within a relative distance rel (array or scalar) of the rounding
+    boundary between two codes; 0 elsewhere.  Used to bound how far O can move
+    when an evaluation of y slightly different from the float64 one rounds
+    across a boundary."""
+    y = np.asarray(y, dtype=np.float64)
+    rel = np.asarray(rel, dtype=np.float64)
+    c = e4m3_encode(y).astype(np.int64) & 0x7F
+    v = e4m3_decode(c.astype(np.uint8))
+    vp = e4m3_decode(np.maximum(c - 1, 0).astype(np.uint8))
+    vn = e4m3_decode(np.minimum(c + 1, 0x7E).astype(np.uint8))
+    tol = rel * y
+    near_lo = (c > 0) & (np.abs(y - 0.5 * (vp + v)) <= tol)
+    near_hi = (c < 0x7E) & (np.abs(y - 0.5 * (v + vn)) <= tol)
+    return np.where(near_hi, vn - v, np.where(near_lo, v - vp, 0.0))
+
+
 def fp16_round(x) -> np.ndarray:
     """Round to IEEE binary16 (nearest even) and return the values as float64."""
     return np.asarray(x).astype(np.float16).astype(np.float64)

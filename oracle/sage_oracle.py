@@ -60,7 +60,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import e4m3_decode, e4m3_encode, fp16_round
+from .codecs import e4m3_decode, e4m3_encode, e4m3_flip_step, fp16_round
 
 # ---------------------------------------------------------------------------
 # Blocking contract (reading: the pages leave b_q, b_kv open).
@@ -72,6 +72,7 @@ MEAN_CHUNK = 256   # tokens per float32 partial sum of the K column mean
 INT8_RANGE = np.float32(127.0)   # symmetric INT8: delta = max|X| / 127
 FP8_RANGE = np.float32(448.0)    # E4M3: delta = max|X| / 448
 P_STATIC_FP8 = 1.0 / 448.0       # static delta_P, max P~ = 1
+LOG2E = 1.4426950408889634       # log2(e), float64
 P_STATIC_INT8 = 1.0 / 127.0
 
 
@@ -216,7 +217,7 @@ def s_int32_tile(q_i8, k_i8, b, h, q0, nq, k0, nk) -> np.ndarray:
 
 
 def attention(q_op, q_rowscale, k_op, k_keyscale, v_op, v_chanscale, *, causal,
-              p_round, rows=None, record=False):
+              p_round, rows=None, record=False, fp8_flip=False):
     """Tiled attention with an online softmax for one (b, h).
 
     [SA] §3 Algorithm 1 and §4 Eq. 4-5, in float64:
@@ -236,6 +237,16 @@ def attention(q_op, q_rowscale, k_op, k_keyscale, v_op, v_chanscale, *, causal,
     q_op [R, d], q_rowscale [R], k_op [N, d], k_keyscale [N], v_op [N, d],
     v_chanscale [d]; rows = the query positions of the R rows (default 0..R-1).
     When `record`, also returns the per-tile P~ row maxima and the final m, l.
+
+    fp8_flip (FP8 P~V, reading C-s): also return, per output element, a bound
+    on how far O moves if every 448 P~ lying within the relative error of a
+    float32 evaluation of exp(S - m) from an E4M3 rounding boundary rounded to
+    the other side.  The error model: about six float32 roundings of numbers
+    of the size of |S| and |m| in log2 units (the scales, the max, the
+    argument), with a margin of four, plus that of the exp itself,
+        rel = 2^-23 * 4 (|S| + |m|) log2(e) + 2^-21.
+    A float value of fp8_flip replaces the model by that constant relative
+    distance.  Returns (O, bound) then.
     """
     q_op = np.asarray(q_op, dtype=np.float64)
     k_op = np.asarray(k_op, dtype=np.float64)
@@ -248,6 +259,8 @@ def attention(q_op, q_rowscale, k_op, k_keyscale, v_op, v_chanscale, *, causal,
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     acc = np.zeros((R, v_op.shape[1]))
+    flip = np.zeros((R, v_op.shape[1]))
+    vabs = np.abs(v_op)
     pmax_tiles = []
     for k0 in range(0, N, KV_TILE):
         k1 = min(k0 + KV_TILE, N)
@@ -264,10 +277,21 @@ def attention(q_op, q_rowscale, k_op, k_keyscale, v_op, v_chanscale, *, causal,
         p = np.where(np.isfinite(m_new)[:, None], p, 0.0)
         l = alpha * l + p.sum(axis=1)
         acc = alpha[:, None] * acc + p_round(p) @ v_op[k0:k1]
+        if fp8_flip is not False:
+            if fp8_flip is True:
+                rel = (2.0 ** -23 * 4.0 * (np.abs(np.where(np.isfinite(s), s, 0.0))
+                                           + np.abs(np.where(np.isfinite(m_new), m_new, 0.0))[:, None])
+                       * LOG2E + 2.0 ** -21)
+            else:
+                rel = float(fp8_flip)
+            step = e4m3_flip_step(p * 448.0, rel) * P_STATIC_FP8
+            flip = alpha[:, None] * flip + step @ vabs[k0:k1]
         m = m_new
         if record:
             pmax_tiles.append(p.max(axis=1))
     out = acc / l[:, None] * np.asarray(v_chanscale, dtype=np.float64)[None, :]
+    if fp8_flip is not False:
+        return out, flip / l[:, None] * np.abs(np.asarray(v_chanscale, dtype=np.float64))[None, :]
     if record:
         return out, dict(pmax_tiles=np.stack(pmax_tiles, axis=1), m=m, l=l)
     return out
@@ -286,7 +310,7 @@ def _p_round_for(pv_mode: str):
 
 
 def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
-                   rows=None, heads=None, record=False, prep=None):
+                   rows=None, heads=None, record=False, prep=None, fp8_flip=False):
     """The whole forward pass on float32 inputs [B, H, N, d].
 
     quant="int8": the method.  quant="none": identity quantiser (Q/sqrt(d) and
@@ -297,6 +321,8 @@ def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
     prep: optionally a precomputed smooth_quant_qk dict (quant="int8").
     Returns O float64 [B, H, R, d] (R = N or len(rows)); heads not evaluated
     are left NaN.  With `record`, also a dict of per-head intermediates.
+    fp8_flip (pv_mode "fp8", quant "int8", not with `record`): also returns the
+    per-element bound of `attention` on O's move from E4M3 boundary cases.
     """
     qf = np.asarray(qf, dtype=np.float32)
     kf = np.asarray(kf, dtype=np.float32)
@@ -306,6 +332,9 @@ def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
     out = np.full((B, H, len(rows_arr), d), np.nan)
     recs = {}
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    if fp8_flip and (pv_mode != "fp8" or quant != "int8" or record):
+        raise ValueError("fp8_flip needs pv_mode='fp8', quant='int8' and no record")
+    flips = np.full(out.shape, np.nan) if fp8_flip else None
 
     if quant == "int8":
         pq = prep if prep is not None else smooth_quant_qk(qf, kf, smooth=smooth)
@@ -320,11 +349,16 @@ def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
             kks = pq["k_scale"][b, h, np.arange(N) // K_BLOCK]
             vcs = vscale[b, h].astype(np.float64) if vscale is not None else np.ones(d)
             res = attention(q_op, qrs, k_op, kks, vvals[b, h], vcs, causal=causal,
-                            p_round=_p_round_for(pv_mode), rows=rows_arr, record=record)
+                            p_round=_p_round_for(pv_mode), rows=rows_arr, record=record,
+                            fp8_flip=fp8_flip)
             if record:
                 out[b, h], recs[(b, h)] = res
+            elif fp8_flip:
+                out[b, h], flips[b, h] = res
             else:
                 out[b, h] = res
+        if fp8_flip:
+            return out, flips
         return (out, recs) if record else out
 
     if quant == "none":

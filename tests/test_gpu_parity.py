@@ -7,7 +7,9 @@ Bar (each check names it):
   oracle's own codes;
 * O (float32 output of the same kernels): max |O - O_oracle| <= 2e-3 and
   cosine >= 0.9999; O in the 16-bit input dtype additionally within one ulp
-  of that dtype (the final rounding).
+  of that dtype (the final rounding).  FP8 P~V: each element may exceed 2e-3
+  by the oracle's bound for 448 P~ values that lie, to float32 accuracy, on an
+  E4M3 rounding boundary (reading C-s; the count is reported).
 Small cases compare every element; the five full workloads compare the whole
 prepass and sampled query rows of O (first, last, ragged tail, diagonal and
 seeded rows of several heads), computed by the oracle row by row.
@@ -57,6 +59,14 @@ SMALL = [
     # prepass, with ragged chunk, block and tile tails
     small("s2113", B=1, H=2, N=2113, d=64, pv_mode="fp8", extras="kbias4"),
     small("s2177", B=1, H=1, N=2177, d=128, dtype="bf16", causal=True),
+    # scores that climb along the keys (recipe "ramp"): later tiles lie far
+    # above the running maximum, so the FP16 kernel's steady-state steps take
+    # their recompute branch (on a large share of the steps) and FP8 rescales
+    # often
+    small("r1000", N=1000, d=64, extras="ramp"),
+    small("r2000b", N=2000, d=128, dtype="bf16", extras="ramp"),
+    small("r1500c", N=1500, d=128, causal=True, extras="ramp"),
+    small("r1000f8", N=1000, d=64, pv_mode="fp8", extras="ramp"),
 ]
 
 
@@ -121,13 +131,32 @@ def test_debug_s_bit_exact(wl):
             np.testing.assert_array_equal(s, ref, err_msg=f"S_i32 b={b} h={h}")
 
 
-def compare_o(o_gpu, o_ref, what):
+def compare_o(o_gpu, o_ref, what, allow=None):
+    """max |O - O_oracle| <= 2e-3 and cosine >= 0.9999.  FP8 P~V: `allow` is
+    the oracle's per-element bound on O's move from 448 P~ values that lie, to
+    float32 accuracy, on an E4M3 rounding boundary (reading C-s); the elements
+    that need it are reported."""
     err = np.abs(o_gpu.astype(np.float64) - o_ref)
     cos = oracle.cos_sim(o_gpu, o_ref)
-    note(f"{what}: max|dO| = {err.max():.3e}  cos = {cos:.7f}")
-    assert err.max() <= O_MAX_ABS, f"{what}: max abs err {err.max()}"
+    extra = ""
+    if allow is not None:
+        over = err > O_MAX_ABS
+        extra = f"  beyond 2e-3 (E4M3 boundary cases): {int(over.sum())}"
+        assert np.all(err <= O_MAX_ABS + allow), \
+            f"{what}: max excess {float((err - O_MAX_ABS - allow).max())}"
+    note(f"{what}: max|dO| = {err.max():.3e}  cos = {cos:.7f}{extra}")
+    if allow is None:
+        assert err.max() <= O_MAX_ABS, f"{what}: max abs err {err.max()}"
     assert cos >= O_COS, f"{what}: cos {cos}"
     return err.max()
+
+
+def oracle_o(wl, qf, kf, vf, **kw):
+    """The oracle's O and, in FP8 mode, its E4M3 boundary bound (else None)."""
+    if wl.pv_mode == "fp8":
+        return oracle.sage_attention(qf, kf, vf, causal=wl.causal, pv_mode="fp8",
+                                     fp8_flip=True, **kw)
+    return oracle.sage_attention(qf, kf, vf, causal=wl.causal, pv_mode=wl.pv_mode, **kw), None
 
 
 def ulp16(x, dtype):
@@ -147,10 +176,11 @@ def test_fwd_parity_small(wl):
     o32 = to_np(qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out_f32=True))
     o16 = qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode)
     o16 = to_np(o16.float())
-    ref = oracle.sage_attention(inp.qf, inp.kf, inp.vf, causal=wl.causal, pv_mode=wl.pv_mode)
-    compare_o(o32, ref, f"{wl.name} O f32")
+    ref, allow = oracle_o(wl, inp.qf, inp.kf, inp.vf)
+    compare_o(o32, ref, f"{wl.name} O f32", allow)
     err16 = np.abs(o16 - ref)
-    assert np.all(err16 <= O_MAX_ABS + ulp16(ref, wl.dtype)), f"{wl.name} O 16-bit"
+    lim16 = O_MAX_ABS + ulp16(ref, wl.dtype) + (0.0 if allow is None else allow)
+    assert np.all(err16 <= lim16), f"{wl.name} O 16-bit"
 
 
 @pytest.mark.parametrize("wl", SMALL[:4], ids=lambda w: w.name)
@@ -214,12 +244,14 @@ def test_full_workload(name):
     for (b, h) in pairs:
         note(f"{name}: rows of head (b={b}, h={h})")
         sl = (slice(b, b + 1), slice(h, h + 1))
-        ref = oracle.sage_attention(inp.qf[sl], inp.kf[sl], inp.vf[sl], causal=wl.causal,
-                                    pv_mode=wl.pv_mode, rows=rows)[0, 0]
+        ref, allow = oracle_o(wl, inp.qf[sl], inp.kf[sl], inp.vf[sl], rows=rows)
+        ref = ref[0, 0]
+        allow = None if allow is None else allow[0, 0]
         g32 = to_np(o32[b, h, torch.from_numpy(rows).cuda()])
         g16 = to_np(o16[b, h, torch.from_numpy(rows).cuda()].float())
-        compare_o(g32, ref, f"{name} (b={b},h={h}) O f32")
-        assert np.all(np.abs(g16 - ref) <= O_MAX_ABS + ulp16(ref, wl.dtype)), "16-bit O"
+        compare_o(g32, ref, f"{name} (b={b},h={h}) O f32", allow)
+        lim16 = O_MAX_ABS + ulp16(ref, wl.dtype) + (0.0 if allow is None else allow)
+        assert np.all(np.abs(g16 - ref) <= lim16), "16-bit O"
 
 
 @pytest.mark.parametrize("name", ["t7_cogvideox", "t7_unidiffuser", "t7_ultrapixel", "t7_llama2",

@@ -231,3 +231,33 @@ def test_rows_subset_matches_full_and_causality():
 
 def test_kv_tile_contract():
     assert KV_TILE == 64
+
+
+def test_fp8_flip_bound_covers_perturbed_rounding():
+    """The FP8 boundary bound of the oracle (reading C-s): when every 448 P~ is
+    perturbed by a relative amount below the band, codes that flip lie within
+    the band, so O moves by at most the returned bound; with a band wide enough
+    to flip codes, O does move (the bound is not vacuous)."""
+    import oracle
+    import oracle.sage_oracle as so
+    from oracle.codecs import e4m3_decode, e4m3_encode
+    from workloads import small, make_inputs
+    wl = small("flip", N=150, d=64, pv_mode="fp8", extras="ramp")
+    inp = make_inputs(wl)
+    pq = oracle.smooth_quant_qk(inp.qf, inp.kf)
+    _, codes, vscale = oracle.prep_v(inp.vf, "fp8")
+    vvals = e4m3_decode(codes)
+    b, h = 0, 1
+    args = (pq["q_i8"][b, h].astype(np.float64), pq["q_scale"][b, h, np.arange(wl.N) // 128],
+            pq["k_i8"][b, h].astype(np.float64), pq["k_scale"][b, h, np.arange(wl.N) // 64],
+            vvals[b, h], vscale[b, h].astype(np.float64))
+    band = 2e-3
+    o, bound = so.attention(*args, causal=False, p_round=so._p_round_for("fp8"), fp8_flip=band)
+    moved = 0.0
+    for rho in (0.999 * band, -0.999 * band):
+        pr = lambda p, r=rho: e4m3_decode(e4m3_encode(p * 448.0 * (1.0 + r))) / 448.0
+        o2 = so.attention(*args, causal=False, p_round=pr)
+        d = np.abs(o2 - o)
+        assert np.all(d <= bound + 1e-12), float((d - bound).max())
+        moved = max(moved, float(d.max()))
+    assert moved > 0.0

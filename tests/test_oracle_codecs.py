@@ -90,3 +90,22 @@ def test_static_p_scale_maps_max_to_top_code(v):
     assert GOLD["p_tilde_max"]["value"] == 1.0
     code = e4m3_encode(np.array([448.0 * v]))[0]
     assert e4m3_decode(np.array([code]))[0] == 448.0 * v
+
+
+def test_e4m3_flip_step_hand_values():
+    """e4m3_flip_step: the decoded-value change of rounding to the other
+    neighbouring code, for values within a relative distance of a boundary."""
+    from oracle.codecs import e4m3_flip_step
+    y = np.array([17.0,      # the 16/18 boundary itself (ties to even -> 16): step 2
+                  17.01,     # within 1e-3 of 17, rounds to 18: step 2 (back to 16)
+                  17.1,      # 0.1 away from 17 > 1e-3 * 17.1: no step
+                  432.0,     # the 416/448 boundary: step 32
+                  448.0,     # top code; its lower boundary 432 is far: no step
+                  0.0,       # zero: no step
+                  2.0 ** -10,  # the 0 / 2^-9 boundary (ties to even -> 0): step 2^-9
+                  1.0])      # exactly representable, boundaries at 0.96875 / 1.0625
+    got = e4m3_flip_step(y, 1e-3)
+    np.testing.assert_array_equal(got, [2.0, 2.0, 0.0, 32.0, 0.0, 0.0, 2.0 ** -9, 0.0])
+    # a relative distance array is applied element by element
+    got = e4m3_flip_step(np.array([17.05, 17.05]), np.array([1e-3, 5e-3]))
+    np.testing.assert_array_equal(got, [0.0, 2.0])

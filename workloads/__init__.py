@@ -155,6 +155,17 @@ def _apply_extras(wl: Workload, rng, q, k, v):
         q[..., c0] += np.float32(5.0)
         k[..., t0, c0] -= np.float32(60.0)
         v[..., t0, :] = np.float32(6.0e4)
+    elif e == "ramp":
+        # scores that climb along the keys: one channel of K grows linearly
+        # with the token index (to 15*sqrt(d)) and Q carries +4 in that
+        # channel, so the logits rise by about 60 (natural units) from the
+        # first key to the last.  Later tiles then lie far above the running
+        # maximum of earlier ones (a recompute case of the attention kernel).
+        N = k.shape[2]
+        c0 = int(rng.integers(0, d))
+        q[..., c0] += np.float32(4.0)
+        ramp = np.arange(N, dtype=np.float32) / np.float32(max(N - 1, 1))
+        k[..., c0] += ramp * np.float32(15.0 * np.sqrt(d))
     else:
         raise ValueError(f"unknown extras recipe {e!r}")
 
