@@ -121,11 +121,11 @@ def main():
     import torch
 
     import quantized_attention_qk_amd as qa
-    from workloads import TABLE7, WORKLOADS, make_inputs
+    from workloads import make_inputs, named
 
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
-    wl = WORKLOADS[args.workload] if args.workload in WORKLOADS else TABLE7[args.workload]
+    wl = named(args.workload)
     B, H, N, d = wl.B, wl.H, wl.N, wl.d
     inp = make_inputs(wl)
     q, k, v = inp.torch_tensors("cuda")

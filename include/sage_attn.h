@@ -87,6 +87,10 @@ size_t sage_attn_workspace_bytes(int B, int H, int N, int d, int pv_mode);
  *      and V^ = E4M3(V * 448/colmax|V|), delta_V = colmax|V|/448 per channel;
  *      FP32 accumulation in both modes
  *   5. O = O / l (FP8: times delta_V / 448), rounded to the input dtype (RNE).
+ * In FP16 mode the kernel keeps the running max lazily (P~ may reach 2^14
+ * before m is refreshed; softmax is invariant under the shift) and l sums the
+ * fp16 values of P~ that enter the product; FP8 mode keeps the exact max and
+ * the unquantised sum.  Results agree with the definition above to rounding.
  *
  * q, k, v: inputs [B,H,N,d] of `dtype`; o: output [B,H,N,d] of `dtype`.
  * workspace: device memory of at least sage_attn_workspace_bytes(B,H,N,d,pv_mode)

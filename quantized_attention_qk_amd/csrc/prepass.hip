@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void colstats_kernel(const uint16_t* __restric
   constexpr int CPW = 256 / P;
   const int chunk = blockIdx.x * CPW + threadIdx.x / P;
   if (chunk >= nchunks) return;
-  colstats_chunk<DT, D, DO_K, DO_V, ROPE>(k, v, N, H, nhd, nchunks, rope_cos, rope_sin, part_sum,
+  colstats_chunk<DT, D, DO_K, DO_V, ROPE, 32>(k, v, N, H, nhd, nchunks, rope_cos, rope_sin, part_sum,
                                           part_max, blockIdx.y, chunk, threadIdx.x % P);
 }
 

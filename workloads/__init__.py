@@ -28,7 +28,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "TABLE7", "make_inputs", "round_to_bf16_bits",
+__all__ = ["Workload", "WORKLOADS", "TABLE7", "SHARDS", "named", "make_inputs", "round_to_bf16_bits",
            "round_to_fp16", "bf16_bits_to_f32", "Inputs", "rope_tables", "to_nhd"]
 
 
@@ -86,6 +86,22 @@ TABLE7 = {
     "t7_timm": Workload("t7_timm", 12, 64, 197, 64, "fp16", False, "fp16", 25, "kbias4",
                         "TIMM shape, 197 tokens"),
 }
+
+
+# One GPU's share of a workload sharded by heads over 8 GPUs (heads are
+# independent, so each GPU runs the same kernel on H/8 heads at full N).
+SHARDS = {
+    "c3_shard8": Workload("c3_shard8", 1, 3, 16384, 128, "bf16", False, "fp16", 2, "q8_kbias5",
+                          "c3 split by heads over 8 GPUs: 3 heads per GPU"),
+}
+
+
+def named(name: str) -> Workload:
+    """A workload of WORKLOADS, TABLE7 or SHARDS by name."""
+    for table in (WORKLOADS, TABLE7, SHARDS):
+        if name in table:
+            return table[name]
+    raise KeyError(name)
 
 
 def round_to_fp16(x: np.ndarray) -> np.ndarray:
@@ -173,7 +189,7 @@ def _apply_extras(wl: Workload, rng, q, k, v):
 def make_inputs(wl: Workload | str, **overrides) -> Inputs:
     """Draw q, k, v for a workload (or a named one with fields overridden)."""
     if isinstance(wl, str):
-        wl = WORKLOADS[wl] if wl in WORKLOADS else TABLE7[wl]
+        wl = named(wl)
     if overrides:
         wl = wl.with_(**overrides)
     shape = (wl.B, wl.H, wl.N, wl.d)
