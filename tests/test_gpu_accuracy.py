@@ -1,0 +1,69 @@
+"""Accuracy of the HIP path against exact attention (needs an MI355X).
+
+The pages' accuracy table ("SageAttention ..." detail page, §5 Table 2:
+CosSim, Relative L1 and RMSE of INT8 Q K^T with FP16 or E4M3 P~V against
+full precision) is measured on real model activations.  Here the same three
+metrics are taken for the GPU output (float32 O of the whole pass) and for
+the oracle's own quantised pass, both against softmax(Q K^T / sqrt(d)) V in
+float64 (the oracle with the identity quantiser, which its tests pin to the
+textbook formula), on sampled query rows of full-size workloads with the
+seeded synthetic inputs.  The check: the GPU reaches the method's accuracy
+(CosSim within 1e-5 and Relative L1 within 2% of the oracle's).  The printed
+values are the ones quoted in the design notes; the synthetic inputs are
+harsher than real activations (c3 scales two Q channels by 8, which INT8 Q
+blocks feel, as only K is smoothed).
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import make_inputs, named
+
+pytestmark = pytest.mark.gpu
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_constants.json")))
+
+
+def note(msg):
+    print(f"[gpu-accuracy] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("name", ["c3", "c4", "c5", "t7_cogvideox"])
+def test_accuracy_against_full_precision(name):
+    import quantized_attention_qk_amd as qa
+    wl = named(name)
+    inp = make_inputs(wl)
+    q, k, v = inp.torch_tensors("cuda")
+    o = qa.sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out_f32=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(wl.seed + 7)
+    rows = np.unique(np.concatenate([[0, wl.N - 1], rng.integers(0, wl.N, 30)]))
+    heads = sorted({(0, 0), (wl.B - 1, wl.H - 1), (int(rng.integers(0, wl.B)),
+                                                  int(rng.integers(0, wl.H)))})
+    got, meth, ref = [], [], []
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        exact = oracle.sage_attention(inp.qf[sl], inp.kf[sl], inp.vf[sl], causal=wl.causal,
+                                      pv_mode="none", quant="none", rows=rows)[0, 0]
+        quant = oracle.sage_attention(inp.qf[sl], inp.kf[sl], inp.vf[sl], causal=wl.causal,
+                                      pv_mode=wl.pv_mode, rows=rows)[0, 0]
+        got.append(o[b, h, torch.from_numpy(rows).cuda()].cpu().numpy())
+        meth.append(quant)
+        ref.append(exact)
+    got, meth, ref = np.stack(got), np.stack(meth), np.stack(ref)
+    m_gpu = (oracle.cos_sim(got, ref), oracle.rel_l1(got, ref), oracle.rmse(got, ref))
+    m_orc = (oracle.cos_sim(meth, ref), oracle.rel_l1(meth, ref), oracle.rmse(meth, ref))
+    key = "table2_int8_fp16" if wl.pv_mode == "fp16" else "table2_int8_e4m3"
+    g = GOLD[key]
+    note(f"{name} ({wl.pv_mode.upper()} P~V) vs exact: GPU CosSim {m_gpu[0]:.6f} RelL1 "
+         f"{m_gpu[1]:.4f} RMSE {m_gpu[2]:.3e} | oracle (method) CosSim {m_orc[0]:.6f} RelL1 "
+         f"{m_orc[1]:.4f} RMSE {m_orc[2]:.3e} | pages on real activations CosSim {g['cos']} "
+         f"RelL1 {g['rel_l1']} RMSE {g['rmse']}")
+    assert m_gpu[0] >= m_orc[0] - 1e-5
+    assert m_gpu[1] <= m_orc[1] * 1.02
