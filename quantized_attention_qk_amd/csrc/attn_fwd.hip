@@ -789,38 +789,49 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   wait_lds_loads();
   __syncthreads();
 
-  // Steady state: two steps per trip (static LDS slots and register roles),
-  // no masking, every load and MFMA present.  Step j writes K^(j+3) and
-  // V(j+1) into the slots read during step j-1.
-  int j = 0;
-  // delta_K of the tile whose softmax the next step runs, loaded one step
+  // Steady state: no masking, every load and MFMA present.  Step jj writes
+  // K^(jj+3) and V(jj+1) into the slots read before it (K^ slot sw, V slot
+  // 1 - U%2), runs QK on K^(jj+2) (slot sr) and may recompute from K^(jj+1)
+  // (slot sp); register roles alternate with U%2.
+  // delta_K of the tile whose softmax the next step runs is loaded one step
   // ahead: a scalar load shares the LDS counter, so waiting for it inside a
   // step would also wait for every LDS read in flight.  Its wait is placed at
   // the end of the step instead, where no LDS read is outstanding.
   float dk_next = ks_bh[min(1, ntiles - 1)];
-  for (; j + 4 < nt && j + 2 < nt_full; j += 2) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int jj = j + u;
-      kld.template issue<false>(krs, (jj + 3) * kKvTile, N, kl0 + kslot(jj + 3, u + 3) * KB,
-                                wave);
-      VL::issue(vrs, jj + 1, vl[1 - u], wave, lane);
-      v16i(&s_cur)[2] = u == 0 ? sB : sA;
-      v16i(&s_new)[2] = u == 0 ? sA : sB;
-      PTile<PV>& p_cur = u == 0 ? pA : pB;
-      PTile<PV>& p_new = u == 0 ? pB : pA;
-      const float dk = dk_next;
-      dk_next = ks_bh[jj + 2];   // jj + 2 < nt: in range
-      // FP16: keep the accumulator start value resident (not rebuilt every
-      // step); in FP8 mode it is zero, an inline constant
-      if constexpr (PV == kPvFp16) asm volatile("" : "+v"(init));
-      fused_step<D, PV>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[kslot(jj + 2, u + 2)],
-                        kbuf[kslot(jj + 1, u + 1)], vbuf[u], m_run, l_run,
-                        tile_scale<PV>(cq, dk), grid, init, n, hh);
-      asm volatile("" ::"s"(dk_next));
-      wait_lds_loads();
-      __syncthreads();
+  auto steady = [&]<int U>(int jj, int sw, int sr, int sp) __attribute__((always_inline)) {
+    kld.template issue<false>(krs, (jj + 3) * kKvTile, N, kl0 + sw * KB, wave);
+    VL::issue(vrs, jj + 1, vl[1 - (U & 1)], wave, lane);
+    v16i(&s_cur)[2] = (U & 1) == 0 ? sB : sA;
+    v16i(&s_new)[2] = (U & 1) == 0 ? sA : sB;
+    PTile<PV>& p_cur = (U & 1) == 0 ? pA : pB;
+    PTile<PV>& p_new = (U & 1) == 0 ? pB : pA;
+    const float dk = dk_next;
+    dk_next = ks_bh[jj + 2];   // jj + 2 < nt: in range
+    // FP16: keep the accumulator start value resident (not rebuilt every
+    // step); in FP8 mode it is zero, an inline constant
+    if constexpr (PV == kPvFp16) asm volatile("" : "+v"(init));
+    fused_step<D, PV>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[sr], kbuf[sp], vbuf[U & 1], m_run,
+                      l_run, tile_scale<PV>(cq, dk), grid, init, n, hh);
+    asm volatile("" ::"s"(dk_next));
+    wait_lds_loads();
+    __syncthreads();
+  };
+  int j = 0;
+  if constexpr (NKS == 3) {
+    // six steps per trip: with j a multiple of 6 every K^ slot (t % 3) is a
+    // constant, so all LDS addresses are immediates
+    for (; j + 8 < nt && j + 6 < nt_full; j += 6) {
+      steady.template operator()<0>(j + 0, 0, 2, 1);
+      steady.template operator()<1>(j + 1, 1, 0, 2);
+      steady.template operator()<2>(j + 2, 2, 1, 0);
+      steady.template operator()<3>(j + 3, 0, 2, 1);
+      steady.template operator()<4>(j + 4, 1, 0, 2);
+      steady.template operator()<5>(j + 5, 2, 1, 0);
     }
+  }
+  for (; j + 4 < nt && j + 2 < nt_full; j += 2) {
+    steady.template operator()<0>(j, kslot(j + 3, 3), kslot(j + 2, 2), kslot(j + 1, 1));
+    steady.template operator()<1>(j + 1, kslot(j + 4, 4), kslot(j + 3, 3), kslot(j + 2, 2));
   }
   // Tail: the last steps, with masking and missing tiles handled explicitly.
   for (; j < nt; j += 2) {
