@@ -274,3 +274,28 @@ def test_table7_shapes(name):
                                     pv_mode=wl.pv_mode, rows=rows)[0, 0]
         compare_o(to_np(o32[b, h, torch.from_numpy(rows).cuda()]), ref,
                   f"{name} (b={b},h={h}) O f32")
+
+
+# ---------------------------------------------------------------------------
+# Maximum sizes: one head of about a million tokens (K^ tile index up to
+# 16384, a V' head of 256 MiB), ragged, in both P~V modes.
+@pytest.mark.parametrize("wl", [
+    small("long1m", B=1, H=1, N=(1 << 20) + 37, d=128, dtype="bf16", pv_mode="fp16", seed=31),
+    small("long512kc8", B=1, H=1, N=(1 << 19) + 5, d=64, causal=True, pv_mode="fp8", seed=32),
+], ids=lambda w: w.name)
+def test_long_sequence(wl):
+    note(f"long sequence {wl}")
+    inp = make_inputs(wl)
+    q, k, v = gpu_inputs(inp)
+    res = qa().smooth_quant_qk(q, k)
+    vt, vs = qa().quant_v(v, wl.pv_mode)
+    torch.cuda.synchronize()
+    check_prepass(inp, res, vt, vs)
+    del res, vt, vs
+    o32 = qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out_f32=True)
+    torch.cuda.synchronize()
+    N = wl.N
+    rows = np.array(sorted({0, 1, 63, 64, 12345, N // 2, N - 65, N - 2, N - 1}))
+    ref, allow = oracle_o(wl, inp.qf, inp.kf, inp.vf, rows=rows)
+    g32 = to_np(o32[0, 0, torch.from_numpy(rows).cuda()])
+    compare_o(g32, ref[0, 0], f"{wl.name} O f32", None if allow is None else allow[0, 0])
