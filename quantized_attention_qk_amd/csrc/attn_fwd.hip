@@ -28,9 +28,14 @@
 //   FP8, log2(448) is folded into the same subtraction so the MFMA operand is
 //   448 P~ directly, and l is kept in the same units.
 // * K^ and prepared-V tiles go from HBM straight into LDS (buffer_load ...
-//   lds, double buffered, XOR-swizzled rows), one step ahead of their use.
-//   The copies are issued from inline assembly: the compiler would otherwise
-//   make every LDS read of the current tiles wait for them.
+//   lds, XOR-swizzled rows; V double-buffered, K^ in three slots in FP16
+//   mode), one step ahead of their use.  The copies are issued from inline
+//   assembly: the compiler would otherwise make every LDS read of the current
+//   tiles wait for them.
+// * FP16 mode reads the INT32 accumulator as a float with no instruction
+//   (it starts from the bit pattern of 1.5 * 2^23) and, in steady-state
+//   steps, takes no max at all: the exps use the running max as it stands and
+//   the row sum checks them (a rare recompute otherwise).
 // * The output rescale by alpha is skipped when no row of the wavefront has a
 //   new maximum (alpha == 1 exactly), which is bit-identical.
 #include <type_traits>
