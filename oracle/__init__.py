@@ -11,4 +11,4 @@ from .sage_oracle import (  # noqa: F401
     sage_attention, brute_attention, cos_sim, rel_l1, rmse, s_int32_tile,
     inv_sqrt_d, rope_rotate_half,
 )
-from .codecs import e4m3_encode, e4m3_decode, e4m3_flip_step, fp16_round  # noqa: F401
+from .codecs import e4m3_encode, e4m3_decode, e4m3_flip_step, fp16_round, int8_flip_step  # noqa: F401

@@ -8,6 +8,8 @@
   Encoding rounds to nearest, ties to even, and saturates to +-448
   ("satfinite"), written here from the format definition, bit by bit.
 * FP16 rounding is numpy's IEEE binary16 cast (round to nearest even).
+* INT8 P^ of the all-INT8 kernel variant: P^ = round(127 P~), nearest even,
+  in [0, 127] (P~ <= 1 under the exact running max).
 """
 from __future__ import annotations
 
@@ -77,6 +79,21 @@ def e4m3_flip_step(y, rel) -> np.ndarray:
     near_lo = (c > 0) & (np.abs(y - 0.5 * (vp + v)) <= tol)
     near_hi = (c < 0x7E) & (np.abs(y - 0.5 * (v + vn)) <= tol)
     return np.where(near_hi, vn - v, np.where(near_lo, v - vp, 0.0))
+
+
+def int8_flip_step(y, rel) -> np.ndarray:
+    """For values y in [0, 127] rounded to the nearest integer (ties to even),
+    the size of the change of the code (1) if y rounded to its other
+    neighbouring integer, wherever y lies within a relative distance rel
+    (array or scalar) of a half-integer between two codes in [0, 127]; 0
+    elsewhere.  The INT8 counterpart of e4m3_flip_step."""
+    y = np.asarray(y, dtype=np.float64)
+    rel = np.asarray(rel, dtype=np.float64)
+    c = np.clip(np.rint(y), 0.0, 127.0)
+    tol = rel * y
+    near_lo = (c > 0) & (np.abs(y - (c - 0.5)) <= tol)
+    near_hi = (c < 127) & (np.abs(y - (c + 0.5)) <= tol)
+    return np.where(near_lo | near_hi, 1.0, 0.0)
 
 
 def fp16_round(x) -> np.ndarray:

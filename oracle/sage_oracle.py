@@ -25,7 +25,12 @@ FP8 "8+8" P~V variant of [SA2pp] "三、技术架构"):
    exp(m_old - m_new) ([SA] §3 Algorithm 1; §4 Eq. 4-5).
 4. P~V in FP16, or in FP8 E4M3 with a static delta_P = 1/448 and a
    per-channel delta_V = colmax|V|/448 ([SA2pp] "三", core formulas; the static
-   P~ scale follows from max P~ = 1, [SA] §7 "key implementation details").
+   P~ scale follows from max P~ = 1, [SA] §7 "key implementation details"),
+   or in INT8 (the all-INT8 kernel variant of [SA] §3 Figure 5, chosen per
+   layer in [SA] §6 step 4): static delta_P = 1/127 ([SA] §7), INT8 V with a
+   per-channel delta_V = colmax|V|/127, and the INT8 product P^ V^ of each
+   tile dequantised and added to the output as Eq. 4-5 write it
+   (O = diag(exp(m_old - m_new)) O_prev + delta_P delta_V P^ V^).
 5. O = diag(l)^-1 O ([SA] §3 Algorithm 1).
 
 Readings where the pages leave a step open (each listed in the design notes):
@@ -50,6 +55,11 @@ Readings where the pages leave a step open (each listed in the design notes):
 * l sums the unquantised P~.
 * FP8 uses the static scale delta_P = 1/448, so P^ = E4M3(448 * P~);
   delta_V is per (batch, head, channel) over all N tokens.
+* INT8 P~V: P^ = round(127 P~) (nearest even; P~ <= 1, so P^ in [0, 127]);
+  V is quantised per (batch, head, channel) over all N tokens like the FP8
+  mode's V (the pages give no granularity for this variant's V), with
+  r = fp32(127/colmax), code = clamp(rne(fp32(V * r)), -127, 127) and
+  delta_V = fp32(colmax/127).
 * Causal masking: key j is visible to query i iff j <= i.
 * The attention arithmetic after the INT32 product runs in float64 (the
   softmax "stays in full precision", [SA] §4, note under Eq. 4-5).
@@ -60,7 +70,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import e4m3_decode, e4m3_encode, e4m3_flip_step, fp16_round
+from .codecs import e4m3_decode, e4m3_encode, e4m3_flip_step, fp16_round, int8_flip_step
 
 # ---------------------------------------------------------------------------
 # Blocking contract (reading: the pages leave b_q, b_kv open).
@@ -185,13 +195,17 @@ def rope_rotate_half(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndar
 
 # ---------------------------------------------------------------------------
 # V preparation: FP16 P~V keeps V in FP16 ([SA] §3 Algorithm 1, FP16 matmul);
-# FP8 P~V quantises V per channel, delta_V = colmax|V|/448 ([SA2pp] "三").
+# FP8 P~V quantises V per channel, delta_V = colmax|V|/448 ([SA2pp] "三");
+# INT8 P~V ([SA] §3 Figure 5) quantises V per channel to INT8, delta_V =
+# colmax|V|/127 (granularity: reading, as for FP8).
 def prep_v(vf: np.ndarray, pv_mode: str):
     """Returns (v_values float64 [B,H,N,d], v_codes, v_scale float32 [B,H,d] or None).
 
     fp16: v_values = fp16_rne(V); v_codes = the float16 array.
     fp8:  cm = max_t |V[t, c]|; r = fp32(448/cm); codes = E4M3(fp32(V * r));
           v_values = decoded codes; v_scale = fp32(cm / 448).
+    int8: cm as for fp8; r = fp32(127/cm); codes = clamp(rne(fp32(V * r)),
+          -127, 127) as int8; v_values = the codes; v_scale = fp32(cm / 127).
     """
     vf = np.asarray(vf, dtype=np.float32)
     if pv_mode == "fp16":
@@ -204,6 +218,13 @@ def prep_v(vf: np.ndarray, pv_mode: str):
         prod = (vf * r[:, :, None, :]).astype(np.float32)
         codes = e4m3_encode(prod)
         return e4m3_decode(codes), codes, (cm / FP8_RANGE).astype(np.float32)
+    if pv_mode == "int8":
+        cm = np.abs(vf).max(axis=2)                                      # [B,H,d]
+        with np.errstate(divide="ignore"):
+            r = np.where(cm > 0, INT8_RANGE / cm, np.float32(0.0)).astype(np.float32)
+        prod = (vf * r[:, :, None, :]).astype(np.float32)
+        codes = np.clip(np.rint(prod), -127, 127).astype(np.int8)
+        return codes.astype(np.float64), codes, (cm / INT8_RANGE).astype(np.float32)
     raise ValueError(pv_mode)
 
 
@@ -217,7 +238,7 @@ def s_int32_tile(q_i8, k_i8, b, h, q0, nq, k0, nk) -> np.ndarray:
 
 
 def attention(q_op, q_rowscale, k_op, k_keyscale, v_op, v_chanscale, *, causal,
-              p_round, rows=None, record=False, fp8_flip=False):
+              p_round, rows=None, record=False, p_flip=False, p_codec="fp8"):
     """Tiled attention with an online softmax for one (b, h).
 
     [SA] §3 Algorithm 1 and §4 Eq. 4-5, in float64:
@@ -232,20 +253,22 @@ def attention(q_op, q_rowscale, k_op, k_keyscale, v_op, v_chanscale, *, causal,
       O = acc / l * v_chanscale[None, :]
 
     For FP8 P~V, p_round(P~) = E4M3(448 P~)/448 (the static delta_P) and
-    v_chanscale = delta_V, so O = sum P^ V^ delta_P delta_V / l.
+    v_chanscale = delta_V, so O = sum P^ V^ delta_P delta_V / l.  INT8 P~V
+    alike with p_round(P~) = round(127 P~)/127 and the INT8 V codes.
 
     q_op [R, d], q_rowscale [R], k_op [N, d], k_keyscale [N], v_op [N, d],
     v_chanscale [d]; rows = the query positions of the R rows (default 0..R-1).
     When `record`, also returns the per-tile P~ row maxima and the final m, l.
 
-    fp8_flip (FP8 P~V, reading C-s): also return, per output element, a bound
-    on how far O moves if every 448 P~ lying within the relative error of a
-    float32 evaluation of exp(S - m) from an E4M3 rounding boundary rounded to
-    the other side.  The error model: about six float32 roundings of numbers
-    of the size of |S| and |m| in log2 units (the scales, the max, the
-    argument), with a margin of four, plus that of the exp itself,
+    p_flip (quantised P~, reading C-s): also return, per output element, a
+    bound on how far O moves if every P~ / delta_P lying within the relative
+    error of a float32 evaluation of exp(S - m) from a rounding boundary of
+    the P^ codec (p_codec "fp8": E4M3 of 448 P~; "int8": integers of 127 P~)
+    rounded to the other side.  The error model: about six float32 roundings
+    of numbers of the size of |S| and |m| in log2 units (the scales, the max,
+    the argument), with a margin of four, plus that of the exp itself,
         rel = 2^-23 * 4 (|S| + |m|) log2(e) + 2^-21.
-    A float value of fp8_flip replaces the model by that constant relative
+    A float value of p_flip replaces the model by that constant relative
     distance.  Returns (O, bound) then.
     """
     q_op = np.asarray(q_op, dtype=np.float64)
@@ -277,20 +300,25 @@ def attention(q_op, q_rowscale, k_op, k_keyscale, v_op, v_chanscale, *, causal,
         p = np.where(np.isfinite(m_new)[:, None], p, 0.0)
         l = alpha * l + p.sum(axis=1)
         acc = alpha[:, None] * acc + p_round(p) @ v_op[k0:k1]
-        if fp8_flip is not False:
-            if fp8_flip is True:
+        if p_flip is not False:
+            if p_flip is True:
                 rel = (2.0 ** -23 * 4.0 * (np.abs(np.where(np.isfinite(s), s, 0.0))
                                            + np.abs(np.where(np.isfinite(m_new), m_new, 0.0))[:, None])
                        * LOG2E + 2.0 ** -21)
             else:
-                rel = float(fp8_flip)
-            step = e4m3_flip_step(p * 448.0, rel) * P_STATIC_FP8
+                rel = float(p_flip)
+            if p_codec == "fp8":
+                step = e4m3_flip_step(p * 448.0, rel) * P_STATIC_FP8
+            elif p_codec == "int8":
+                step = int8_flip_step(p * 127.0, rel) * P_STATIC_INT8
+            else:
+                raise ValueError(p_codec)
             flip = alpha[:, None] * flip + step @ vabs[k0:k1]
         m = m_new
         if record:
             pmax_tiles.append(p.max(axis=1))
     out = acc / l[:, None] * np.asarray(v_chanscale, dtype=np.float64)[None, :]
-    if fp8_flip is not False:
+    if p_flip is not False:
         return out, flip / l[:, None] * np.abs(np.asarray(v_chanscale, dtype=np.float64))[None, :]
     if record:
         return out, dict(pmax_tiles=np.stack(pmax_tiles, axis=1), m=m, l=l)
@@ -304,13 +332,16 @@ def _p_round_for(pv_mode: str):
         # P^ = E4M3(P~ / delta_P) with the static delta_P = 1/448; the product
         # P^ V^ is dequantised by delta_P here and by delta_V per channel.
         return lambda p: e4m3_decode(e4m3_encode(p * 448.0)) * P_STATIC_FP8
+    if pv_mode == "int8":
+        # P^ = round(P~ / delta_P) with the static delta_P = 1/127
+        return lambda p: np.clip(np.rint(p * 127.0), 0.0, 127.0) * P_STATIC_INT8
     if pv_mode == "none":
         return lambda p: p
     raise ValueError(pv_mode)
 
 
 def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
-                   rows=None, heads=None, record=False, prep=None, fp8_flip=False):
+                   rows=None, heads=None, record=False, prep=None, p_flip=False):
     """The whole forward pass on float32 inputs [B, H, N, d].
 
     quant="int8": the method.  quant="none": identity quantiser (Q/sqrt(d) and
@@ -321,8 +352,9 @@ def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
     prep: optionally a precomputed smooth_quant_qk dict (quant="int8").
     Returns O float64 [B, H, R, d] (R = N or len(rows)); heads not evaluated
     are left NaN.  With `record`, also a dict of per-head intermediates.
-    fp8_flip (pv_mode "fp8", quant "int8", not with `record`): also returns the
-    per-element bound of `attention` on O's move from E4M3 boundary cases.
+    p_flip (pv_mode "fp8" or "int8", quant "int8", not with `record`): also
+    returns the per-element bound of `attention` on O's move from rounding
+    boundary cases of P^.
     """
     qf = np.asarray(qf, dtype=np.float32)
     kf = np.asarray(kf, dtype=np.float32)
@@ -332,9 +364,9 @@ def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
     out = np.full((B, H, len(rows_arr), d), np.nan)
     recs = {}
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
-    if fp8_flip and (pv_mode != "fp8" or quant != "int8" or record):
-        raise ValueError("fp8_flip needs pv_mode='fp8', quant='int8' and no record")
-    flips = np.full(out.shape, np.nan) if fp8_flip else None
+    if p_flip and (pv_mode not in ("fp8", "int8") or quant != "int8" or record):
+        raise ValueError("p_flip needs pv_mode 'fp8' or 'int8', quant='int8' and no record")
+    flips = np.full(out.shape, np.nan) if p_flip else None
 
     if quant == "int8":
         pq = prep if prep is not None else smooth_quant_qk(qf, kf, smooth=smooth)
@@ -350,14 +382,14 @@ def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
             vcs = vscale[b, h].astype(np.float64) if vscale is not None else np.ones(d)
             res = attention(q_op, qrs, k_op, kks, vvals[b, h], vcs, causal=causal,
                             p_round=_p_round_for(pv_mode), rows=rows_arr, record=record,
-                            fp8_flip=fp8_flip)
+                            p_flip=p_flip, p_codec=pv_mode if p_flip else "fp8")
             if record:
                 out[b, h], recs[(b, h)] = res
-            elif fp8_flip:
+            elif p_flip:
                 out[b, h], flips[b, h] = res
             else:
                 out[b, h] = res
-        if fp8_flip:
+        if p_flip:
             return out, flips
         return (out, recs) if record else out
 

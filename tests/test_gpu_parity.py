@@ -152,10 +152,11 @@ def compare_o(o_gpu, o_ref, what, allow=None):
 
 
 def oracle_o(wl, qf, kf, vf, **kw):
-    """The oracle's O and, in FP8 mode, its E4M3 boundary bound (else None)."""
-    if wl.pv_mode == "fp8":
-        return oracle.sage_attention(qf, kf, vf, causal=wl.causal, pv_mode="fp8",
-                                     fp8_flip=True, **kw)
+    """The oracle's O and, with a quantised P~ (FP8 or INT8 P~V), its bound on
+    the effect of rounding-boundary cases of P^ (else None)."""
+    if wl.pv_mode in ("fp8", "int8"):
+        return oracle.sage_attention(qf, kf, vf, causal=wl.causal, pv_mode=wl.pv_mode,
+                                     p_flip=True, **kw)
     return oracle.sage_attention(qf, kf, vf, causal=wl.causal, pv_mode=wl.pv_mode, **kw), None
 
 

@@ -10,6 +10,10 @@
   textbook result exactly (pins the block scales and 1/sqrt(d)).
 * FP8 P~V (SageAttention2++ review page, section 三): the output stays within
   the error bound implied by E4M3 rounding of P^ = 448 P~ and of V.
+* INT8 P~V (the all-INT8 variant of the detail page, §3 Figure 5, with the
+  static delta_P = 1/127 of §7): equal scores average the INT8 V exactly, a
+  dominant key returns its V row, and the rounding of P^ = 127 P~ moves O by
+  at most half a step per key.
 """
 import json
 import math
@@ -252,7 +256,7 @@ def test_fp8_flip_bound_covers_perturbed_rounding():
             pq["k_i8"][b, h].astype(np.float64), pq["k_scale"][b, h, np.arange(wl.N) // 64],
             vvals[b, h], vscale[b, h].astype(np.float64))
     band = 2e-3
-    o, bound = so.attention(*args, causal=False, p_round=so._p_round_for("fp8"), fp8_flip=band)
+    o, bound = so.attention(*args, causal=False, p_round=so._p_round_for("fp8"), p_flip=band)
     moved = 0.0
     for rho in (0.999 * band, -0.999 * band):
         pr = lambda p, r=rho: e4m3_decode(e4m3_encode(p * 448.0 * (1.0 + r))) / 448.0
@@ -261,3 +265,116 @@ def test_fp8_flip_bound_covers_perturbed_rounding():
         assert np.all(d <= bound + 1e-12), float((d - bound).max())
         moved = max(moved, float(d.max()))
     assert moved > 0.0
+
+
+def _int8_head_args(qf, kf, vf, b=0, h=0):
+    import oracle
+    N = qf.shape[2]
+    pq = oracle.smooth_quant_qk(qf, kf)
+    vals, _, vscale = oracle.prep_v(vf, "int8")
+    return (pq["q_i8"][b, h].astype(np.float64), pq["q_scale"][b, h, np.arange(N) // 128],
+            pq["k_i8"][b, h].astype(np.float64), pq["k_scale"][b, h, np.arange(N) // 64],
+            vals[b, h], vscale[b, h].astype(np.float64))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_pv_equal_scores_average_v(causal):
+    # Q = 0: every score is 0, every P~ = 1, every P^ = 127 (no rounding), so
+    # row i of O is the mean of the dequantised INT8 V over its visible keys.
+    inp = make_inputs(small(N=150, d=64, seed=61))
+    qf = np.zeros_like(inp.qf)
+    o = sage_attention(qf, inp.kf, inp.vf, causal=causal, pv_mode="int8")
+    _, codes, vscale = prep_v(inp.vf, "int8")
+    deq = codes.astype(np.float64) * vscale[:, :, None, :].astype(np.float64)
+    if causal:
+        ref = np.cumsum(deq, axis=2) / np.arange(1, 151)[None, None, :, None]
+    else:
+        ref = np.broadcast_to(deq.mean(axis=2, keepdims=True), deq.shape)
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,dom", [(False, 77), (True, 0)])
+def test_int8_pv_dominant_key_returns_its_row(causal, dom):
+    # One key scores 40 above every other (e^-40: P^ = 0 for the rest and l = 1
+    # to float64 precision): O = the dequantised INT8 V row of that key.
+    N, d = 130, 64
+    rng = np.random.default_rng(62)
+    qf = np.zeros((1, 1, N, d), np.float32)
+    qf[..., 0] = 32.0                      # Q/sqrt(d) = 4 in channel 0
+    kf = (0.01 * rng.standard_normal((1, 1, N, d))).astype(np.float32)
+    kf[0, 0, dom, 0] += 10.0
+    vf = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    o = sage_attention(qf, kf, vf, causal=causal, pv_mode="int8")
+    _, codes, vscale = prep_v(vf, "int8")
+    row = codes[0, 0, dom].astype(np.float64) * vscale[0, 0].astype(np.float64)
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(row, (N, d)), rtol=0, atol=1e-13)
+
+
+def test_int8_pv_rounding_bound():
+    # |round(127 P~)/127 - P~| <= 1/254 for every key, and alpha <= 1, so O
+    # moves from its exact-P~ value (same INT8 V) by at most
+    # (1/254) sum_keys |V_deq| / l per element.
+    import oracle.sage_oracle as so
+    inp = make_inputs(small(N=300, d=64, seed=63, extras="kbias4"))
+    args = _int8_head_args(inp.qf, inp.kf, inp.vf, 0, 1)
+    oi = so.attention(*args, causal=False, p_round=so._p_round_for("int8"))
+    oe, rec = so.attention(*args, causal=False, p_round=lambda p: p, record=True)
+    vdeq = np.abs(args[4] * args[5][None, :])
+    bound = vdeq.sum(axis=0)[None, :] / 254.0 / rec["l"][:, None]
+    diff = np.abs(oi - oe)
+    assert np.all(diff <= bound * (1 + 1e-12))
+    assert diff.max() > 0
+    # and the oracle's full pass uses exactly this per-head computation
+    full = sage_attention(inp.qf, inp.kf, inp.vf, causal=False, pv_mode="int8")
+    np.testing.assert_allclose(full[0, 1], oi, rtol=0, atol=0)
+
+
+def test_int8_flip_bound_covers_perturbed_rounding():
+    """The INT8 counterpart of the FP8 boundary bound (reading C-s): every
+    127 P~ perturbed by a relative amount below the band moves O by at most the
+    returned bound, and a band this wide does move it."""
+    import oracle.sage_oracle as so
+    wl = small("flip8", N=150, d=64, pv_mode="int8", extras="ramp")
+    inp = make_inputs(wl)
+    args = _int8_head_args(inp.qf, inp.kf, inp.vf, 0, 1)
+    band = 2e-3
+    o, bound = so.attention(*args, causal=False, p_round=so._p_round_for("int8"), p_flip=band,
+                            p_codec="int8")
+    moved = 0.0
+    for rho in (0.999 * band, -0.999 * band):
+        pr = lambda p, r=rho: np.clip(np.rint(p * 127.0 * (1.0 + r)), 0, 127) / 127.0
+        o2 = so.attention(*args, causal=False, p_round=pr)
+        d = np.abs(o2 - o)
+        assert np.all(d <= bound + 1e-12), float((d - bound).max())
+        moved = max(moved, float(d.max()))
+    assert moved > 0.0
+
+
+def test_int8_pv_accuracy_levels_table2():
+    """[SA] §5 Table 2 puts INT8 P~,V below E4M3 (cosine 99.70% vs 99.94% on
+    real layers).  Its mechanism: with delta_P = 1/127 every P~ below 1/254
+    becomes P^ = 0.  A sink row (one key 6 above a flat background, whose V
+    has a nonzero mean) loses the whole background: O is the sink's INT8 V
+    row over l, exactly, and the cosine falls below FP8's.  On diffuse
+    synthetic rows (no such loss) INT8 V is finer than E4M3, and the level is
+    at least the page's INT8 cosine."""
+    N, d = 1024, 64
+    rng = np.random.default_rng(5)
+    qf = np.zeros((1, 1, N, d), np.float32)
+    qf[..., 0] = 8.0                                   # Q/sqrt(d) = 1 in channel 0
+    kf = (0.05 * rng.standard_normal((1, 1, N, d))).astype(np.float32)
+    kf[0, 0, 0, 0] += 6.0
+    vf = (rng.standard_normal((1, 1, N, d)) + 1.0).astype(np.float32)
+    ref = brute_attention(qf, kf, vf, causal=False)
+    o8 = sage_attention(qf, kf, vf, causal=False, pv_mode="fp8")
+    _, recs = sage_attention(qf, kf, vf, causal=False, pv_mode="int8", record=True)
+    oi = sage_attention(qf, kf, vf, causal=False, pv_mode="int8")
+    _, codes, vscale = prep_v(vf, "int8")
+    row = codes[0, 0, 0].astype(np.float64) * vscale[0, 0].astype(np.float64)
+    np.testing.assert_allclose(oi[0, 0], row[None, :] / recs[(0, 0)]["l"][:, None], rtol=1e-13,
+                               atol=0)
+    assert cos_sim(oi, ref) < cos_sim(o8, ref) - 0.05
+    inp = make_inputs(small(N=1024, d=64, H=2, seed=0, extras="kbias4"))
+    ref = brute_attention(inp.qf, inp.kf, inp.vf, causal=False)
+    oi = sage_attention(inp.qf, inp.kf, inp.vf, causal=False, pv_mode="int8")
+    assert cos_sim(oi, ref) >= GOLD["table2_int8_int8"]["cos"]

@@ -109,3 +109,23 @@ def test_e4m3_flip_step_hand_values():
     # a relative distance array is applied element by element
     got = e4m3_flip_step(np.array([17.05, 17.05]), np.array([1e-3, 5e-3]))
     np.testing.assert_array_equal(got, [0.0, 2.0])
+
+
+def test_int8_flip_step_hand_values():
+    """int8_flip_step: 1 where y (127 P~, rounded to an integer code in
+    [0, 127], ties to even) lies within a relative distance of a half-integer
+    between two codes, else 0."""
+    from oracle.codecs import int8_flip_step
+    y = np.array([2.5,       # a midpoint itself (ties to even -> 2): step
+                  2.501,     # 0.001 from 2.5 <= 1e-3 * 2.501: step
+                  2.6,       # 0.1 from 2.5: no step
+                  127.0,     # top code; its lower midpoint 126.5 is far: no step
+                  0.0,       # zero: no step
+                  0.4999,    # 1e-4 from the 0/1 midpoint: step
+                  3.0])      # an integer: no step
+    got = int8_flip_step(y, 1e-3)
+    np.testing.assert_array_equal(got, [1.0, 1.0, 0.0, 0.0, 0.0, 1.0, 0.0])
+    # a relative distance array is applied element by element; near the top
+    # code only the lower midpoint counts (no code above 127)
+    got = int8_flip_step(np.array([126.99, 126.99, 127.45]), np.array([1e-3, 1e-2, 1e-3]))
+    np.testing.assert_array_equal(got, [0.0, 1.0, 0.0])

@@ -4,7 +4,8 @@ V preparation and the exact INT32 product.
 Pages: "SageAttention: Accurate 8-Bit Attention ..." detail page, §3
 Algorithm 1 and §4 Eq. 6 (smooth K: subtract the token mean of every channel);
 "SageAttention2++ ..." review page, section 三 core formulas
-(delta = max|X|/127, X^ = round(X/delta); delta_V = colmax|V|/448).
+(delta = max|X|/127, X^ = round(X/delta); delta_V = colmax|V|/448); the
+all-INT8 variant's V (detail page §3 Figure 5) with delta_V = colmax|V|/127.
 """
 import json
 import os
@@ -180,3 +181,38 @@ def test_prep_v_fp8_error_bound_and_fp16():
     v16, _, s = prep_v(inp.vf, "fp16")
     assert s is None
     np.testing.assert_array_equal(v16, inp.vf.astype(np.float16).astype(np.float64))
+
+
+def test_prep_v_int8_hand_worked():
+    # channel 0: colmax 1 -> r = 127, V r = [127, -63.5, 31.75, 95.25] ->
+    # codes [127, -64 (tie to even), 32, 95], delta_V = fp32(1/127);
+    # channel 1 all zero -> codes 0, delta_V = 0; channel 2: colmax 2.54 ->
+    # r = fp32(127/2.54) = 50, codes of [-2.54, 1.27, 0.01, 0] = [-127, 64 (63.5
+    # ties to even), 0 (0.5 ties to even), 0]
+    v = np.array([[1.0, 0.0, -2.54], [-0.5, 0.0, 1.27], [0.25, 0.0, 0.01],
+                  [0.75, 0.0, 0.0]], dtype=np.float32)[None, None]
+    vals, codes, vscale = prep_v(v, "int8")
+    assert codes.dtype == np.int8
+    r2 = np.float32(np.float32(127.0) / np.float32(2.54))
+    exp2 = np.clip(np.rint((v[0, 0, :, 2] * r2).astype(np.float32)), -127, 127)
+    np.testing.assert_array_equal(codes[0, 0, :, 0], [127, -64, 32, 95])
+    np.testing.assert_array_equal(codes[0, 0, :, 1], [0, 0, 0, 0])
+    np.testing.assert_array_equal(codes[0, 0, :, 2], exp2)
+    assert codes[0, 0, 0, 2] == -127
+    np.testing.assert_array_equal(vals, codes.astype(np.float64))
+    np.testing.assert_array_equal(vscale[0, 0], np.array([1.0, 0.0, 2.54], np.float32) / np.float32(127))
+
+
+def test_prep_v_int8_closed_forms():
+    inp = make_inputs(small(N=700, d=64, seed=10))
+    vals, codes, vscale = prep_v(inp.vf, "int8")
+    cm = np.abs(inp.vf).max(axis=2)
+    r = (np.float32(127.0) / cm).astype(np.float32)
+    x = (inp.vf * r[:, :, None, :]).astype(np.float64)
+    assert np.all(np.abs(x - codes) <= 0.5)                          # nearest integer
+    assert np.all(np.abs(codes).max(axis=2) == 127)                  # colmax -> 127
+    assert np.all(np.abs(codes.astype(np.int64)) <= 127)
+    rec = codes * vscale[:, :, None, :].astype(np.float64)
+    # half a step, plus the float32 rounding of r and delta_V (r delta_V != 1)
+    tol = 0.5 * vscale[:, :, None, :].astype(np.float64) + np.abs(inp.vf) * 2.0 ** -21
+    assert np.all(np.abs(rec - inp.vf) <= tol)
