@@ -47,7 +47,9 @@ typedef enum {
   SAGE_ERR_NO_DEVICE = 5      /* no HIP device is visible */
 } sage_status;
 
-enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8 = 1 };   /* P~V precision: FP16, or FP8 E4M3 ("8+8") */
+/* P~V precision: FP16, FP8 E4M3 ("8+8"), or INT8 (the all-INT8 kernel variant,
+ * [SA] §3 Figure 5, chosen per layer in [SA] §6 step 4) */
+enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8 = 1, SAGE_PV_INT8 = 2 };
 enum { SAGE_DT_F16 = 0, SAGE_DT_BF16 = 1 };   /* element type of q, k, v and o */
 enum { SAGE_OUT_F32 = 2 };                     /* float32 output (sage_attn_fwd_quantized only) */
 enum { SAGE_LAYOUT_HND = 0,                    /* q, k, v, o as [B,H,N,d] */
@@ -85,12 +87,19 @@ size_t sage_attn_workspace_bytes(int B, int H, int N, int d, int pv_mode);
  *   4. pv_mode SAGE_PV_FP16: O += fp16(P~) V'_j with V' = fp16(V);
  *      pv_mode SAGE_PV_FP8:  O += E4M3(448 P~) V^_j with the static delta_P = 1/448
  *      and V^ = E4M3(V * 448/colmax|V|), delta_V = colmax|V|/448 per channel;
- *      FP32 accumulation in both modes
- *   5. O = O / l (FP8: times delta_V / 448), rounded to the input dtype (RNE).
+ *      FP32 accumulation in both modes;
+ *      pv_mode SAGE_PV_INT8: O = alpha O + (P^ V^_j as INT32) with P^ =
+ *      rne(127 P~) in [0, 127] (static delta_P = 1/127, [SA] §7 key
+ *      implementation details) and V^ = clamp(rne(V * 127/colmax|V|), -127,
+ *      127), delta_V = colmax|V|/127 per channel; each tile's INT32 product is
+ *      converted to float32 (exactly) and added
+ *   5. O = O / l (FP8, INT8: times delta_V / 448 or / 127), rounded to the
+ *      input dtype (RNE).
  * In FP16 mode the kernel keeps the running max lazily (P~ may reach 2^14
  * before m is refreshed; softmax is invariant under the shift) and l sums the
  * fp16 values of P~ that enter the product; FP8 mode keeps the exact max and
- * the unquantised sum.  Results agree with the definition above to rounding.
+ * the unquantised sum; so does INT8 mode.  Results agree with the definition
+ * above to rounding.
  *
  * q, k, v: inputs [B,H,N,d] of `dtype`; o: output [B,H,N,d] of `dtype`.
  * workspace: device memory of at least sage_attn_workspace_bytes(B,H,N,d,pv_mode)
@@ -177,10 +186,13 @@ size_t sage_quant_v_scratch_bytes(int B, int H, int N, int d, int pv_mode);
  *     and logical chunk p / 16 is stored at physical chunk (p / 16) ^ ((c / 4) % 4).
  *     Codes: OCP E4M3FN of fp32(V * r_c), round to nearest even, with
  *     r_c = fp32(448 / colmax_t |V[t, c]|) (0 for an all-zero channel).
+ *   SAGE_PV_INT8: the FP8 layout, with int8 codes
+ *     clamp(rne(fp32(V * r_c)), -127, 127), r_c = fp32(127 / colmax_t |V[t, c]|).
  *
  * Tile (b, h, t) starts at byte ((b*H + h) * ceil(N/64) + t) * d * rowbytes.
- * v_scale (FP8 only, else may be NULL): float32 [B,H,d] = fp32(colmax / 448).
- * scratch: >= sage_quant_v_scratch_bytes(...) bytes, 16-byte aligned
+ * v_scale (FP8 and INT8, else may be NULL): float32 [B,H,d] = fp32(colmax / 448)
+ * or fp32(colmax / 127).  scratch: >= sage_quant_v_scratch_bytes(...) bytes,
+ * 16-byte aligned
  * (FP16 mode needs none).  v_out: >= sage_quant_v_bytes(...), 16-byte aligned.
  */
 int sage_quant_v(const void* v, int dtype, int B, int H, int N, int d, int pv_mode,
@@ -197,7 +209,7 @@ int sage_quant_v_ex(const void* v, int dtype, int layout, int B, int H, int N, i
  * Steps 3-5 alone: the attention kernel on operands already prepared by
  * sage_smooth_quant_qk and sage_quant_v (e.g. K and V quantised once and
  * reused).  q_i8, k_i8, q_scale, k_scale: as written by sage_smooth_quant_qk;
- * v_prep (and v_scale for SAGE_PV_FP8, else may be NULL): as written by
+ * v_prep (and v_scale for SAGE_PV_FP8 and SAGE_PV_INT8, else may be NULL): as written by
  * sage_quant_v with the same pv_mode.  o: [B,H,N,d] of out_dtype
  * (SAGE_DT_F16, SAGE_DT_BF16 or SAGE_OUT_F32).  Same numerics as sage_attn_fwd.
  */

@@ -13,7 +13,7 @@ import torch  # noqa: F401  (must be loaded before the HIP library)
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_attn.so")
 
 SAGE_OK = 0
-SAGE_PV = {"fp16": 0, "fp8": 1}
+SAGE_PV = {"fp16": 0, "fp8": 1, "int8": 2}
 SAGE_DT = {torch.float16: 0, torch.bfloat16: 1}
 SAGE_LAYOUT = {"HND": 0, "NHD": 1}
 

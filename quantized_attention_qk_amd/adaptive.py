@@ -3,9 +3,12 @@
 "SageAttention: Accurate 8-Bit Attention ..." detail page, §2 Q2 item 3 (and
 §4 check 6, §6 step 4): each layer is profiled once against full precision;
 layers whose cosine similarity stays above 99.8% use the faster kernel, the
-others fall back to the more precise one.  On gfx950 the faster variant is
-INT8 QK^T with FP8 E4M3 P~V (the FP8 MFMA runs at the INT8 rate, twice the
-FP16 rate); the precise one keeps P~V in FP16.
+others fall back to the more precise one.  The page's faster kernel is the
+all-INT8 one (INT8 P~V), its precise one keeps P~V in FP16; candidates=
+("int8",) reproduces that choice.  On gfx950 the default fast candidate is
+FP8 E4M3 P~V: the FP8 MFMA runs at the INT8 rate with a float32 accumulator,
+so it needs no per-tile conversion of an INT32 product and is the faster of
+the two.  Several candidates are tried in the order given (fastest first).
 
 Every number is computed on the GPU: the candidate kernel's float32 output
 and a float32 full-precision reference (sage_attn_ref_rows_f32) on a seeded
@@ -47,24 +50,38 @@ def layer_cosine(q, k, v, causal: bool = False, pv_mode: str = "fp8", rows: int 
     return float((got @ ref) / (got.norm() * ref.norm()))
 
 
-def choose_mode(cos_fast: float, threshold: float = DEFAULT_THRESHOLD) -> str:
-    """The faster P~V kernel where it is accurate enough, else FP16."""
-    return "fp8" if cos_fast >= threshold else "fp16"
+FAST_MODES = ("fp8", "int8")
+
+
+def choose_mode(cos_fast, threshold: float = DEFAULT_THRESHOLD, candidates=("fp8",)) -> str:
+    """The first candidate whose cosine (a float, or a dict mode -> cosine)
+    reaches the threshold, else FP16."""
+    for mode in candidates:
+        if mode not in FAST_MODES:
+            raise ValueError(f"not a fast P~V mode: {mode!r}")
+        c = cos_fast[mode] if isinstance(cos_fast, dict) else cos_fast
+        if c >= threshold:
+            return mode
+    return "fp16"
 
 
 def select_pv_modes(layers, threshold: float = DEFAULT_THRESHOLD, rows: int = 512,
-                    seed: int = 0) -> dict:
+                    seed: int = 0, candidates=("fp8",)) -> dict:
     """layers: mapping name -> (q, k, v) or (q, k, v, causal), device tensors.
 
-    Returns {name: {"pv_mode": "fp8" | "fp16", "cos_fp8": float}}, the table
-    the pages build once per model and then reuse.
+    Returns {name: {"pv_mode": one of candidates or "fp16", "cos_<mode>":
+    float for each candidate}}, the table the pages build once per model and
+    then reuse.
     """
     table = {}
     for name, spec in layers.items():
         q, k, v = spec[:3]
         causal = bool(spec[3]) if len(spec) > 3 else False
-        cos = layer_cosine(q, k, v, causal=causal, pv_mode="fp8", rows=rows, seed=seed)
-        table[name] = {"pv_mode": choose_mode(cos, threshold), "cos_fp8": cos}
+        cos = {m: layer_cosine(q, k, v, causal=causal, pv_mode=m, rows=rows, seed=seed)
+               for m in candidates}
+        entry = {"pv_mode": choose_mode(cos, threshold, candidates)}
+        entry.update({f"cos_{m}": c for m, c in cos.items()})
+        table[name] = entry
     return table
 
 
@@ -77,6 +94,6 @@ def load_modes(path: str) -> dict:
     with open(path) as f:
         table = json.load(f)
     for name, e in table.items():
-        if e.get("pv_mode") not in ("fp16", "fp8"):
+        if e.get("pv_mode") not in ("fp16",) + FAST_MODES:
             raise ValueError(f"layer {name!r}: bad pv_mode {e.get('pv_mode')!r}")
     return table

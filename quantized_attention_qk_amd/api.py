@@ -136,7 +136,7 @@ def quant_v(v: torch.Tensor, pv_mode: str = "fp16", layout: str = "HND"):
     mode = SAGE_PV[pv_mode]
     v_out = torch.empty(int(lib().sage_quant_v_bytes(B, H, N, d, mode)), dtype=torch.uint8,
                         device=dev)
-    v_scale = torch.empty((B, H, d), dtype=torch.float32, device=dev) if mode == 1 else None
+    v_scale = torch.empty((B, H, d), dtype=torch.float32, device=dev) if mode != 0 else None
     nscr = int(lib().sage_quant_v_scratch_bytes(B, H, N, d, mode))
     scratch = torch.empty(max(nscr, 16), dtype=torch.uint8, device=dev)
     check(lib().sage_quant_v_ex(v.data_ptr(), SAGE_DT[v.dtype], SAGE_LAYOUT[layout], B, H, N, d,
@@ -194,7 +194,8 @@ def debug_s_i32(q_i8: torch.Tensor, k_i8: torch.Tensor, b: int, h: int, q0: int,
 
 def untile_v(v_out, B: int, H: int, N: int, d: int, pv_mode: str = "fp16"):
     """Inverse of the tiled V layout documented for sage_quant_v: returns a
-    numpy array [B, H, N, d] (float16 values, or uint8 E4M3 codes)."""
+    numpy array [B, H, N, d] (float16 values, uint8 E4M3 codes or int8
+    codes)."""
     import numpy as np
     raw = v_out.cpu().numpy() if hasattr(v_out, "cpu") else np.asarray(v_out)
     nt = -(-N // 64)
@@ -215,4 +216,6 @@ def untile_v(v_out, B: int, H: int, N: int, d: int, pv_mode: str = "fp16"):
         out = np.zeros((B, H, nt, 64, d), np.uint8)
         cc = np.broadcast_to(c[:, :, None], key.shape)
         out[:, :, :, key, cc] = t
+        if pv_mode == "int8":
+            out = out.view(np.int8)
     return out.reshape(B, H, nt * 64, d)[:, :, :N]

@@ -8,7 +8,10 @@
 // or in FP8 E4M3 with a static delta_P = 1/448 and a per-channel delta_V, as in
 // the "8+8" variant of the "SageAttention2++ ..." review page (section 三) --
 // accumulated in FP32 (gfx950 has no FP16-accumulator MFMA), and finally
-// O = O / l.
+// O = O / l.  The all-INT8 variant (detail page, §3 Figure 5) quantises P~
+// with the static delta_P = 1/127 (§7) and V per channel to INT8; each tile's
+// INT32 product P^ V^ is converted to float and added to the rescaled output,
+// O = alpha O + P^ V^, as Eq. 4-5 write it.
 //
 // MI355X mapping
 // * Workgroup = 4 wavefronts = 128 query rows = one delta_Q block of one (b, h).
@@ -17,7 +20,8 @@
 //   in the 32x32 accumulator lane l holds query l%32 and keys
 //   8*(r/4) + 4*(l/32) + r%4 (r = register 0..15).  That is exactly the B
 //   operand layout of O^T = V^T P~^T (v_mfma_f32_32x32x16_f16, or
-//   v_mfma_scale_f32_32x32x64_f8f6f4 for FP8), so P~ goes from the softmax to
+//   v_mfma_scale_f32_32x32x64_f8f6f4 for FP8, two v_mfma_i32_32x32x32_i8 over
+//   the two 32-key halves for INT8), so P~ goes from the softmax to
 //   the second MFMA without leaving registers; V is stored pre-permuted (see
 //   sage_quant_v) so that its A operand is one 16-byte LDS read per lane.
 // * Row reductions (max over keys) are in-lane over 32 values plus one
@@ -48,6 +52,7 @@ namespace sage {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_448 = 8.807354922057604f;   // log2(448)
+constexpr float kLog2_127 = 6.988684686772166f;   // log2(127)
 
 template <int D>
 struct KTile {
@@ -231,7 +236,8 @@ __device__ __forceinline__ void store4(void* out, size_t idx, float a, float b, 
 }
 
 // P~ of one tile as the B operand of the P~V MFMA: FP16 = four 8-half steps
-// (16 keys each), FP8 = one 32-byte operand covering the 64 keys.
+// (16 keys each), FP8 = one 32-byte operand covering the 64 keys, INT8 = the
+// same 32 bytes, split into the 16-byte operands of the two 32-key halves.
 template <int PV>
 struct PTile;
 template <>
@@ -242,6 +248,19 @@ template <>
 struct PTile<kPvFp8> {
   v8i w;
 };
+template <>
+struct PTile<kPvInt8> {
+  v8i w;
+};
+
+// Four floats in [0, 255] -> four u8 codes, round to nearest even
+// (v_cvt_pk_u8_f32), first value in the low byte.
+__device__ __forceinline__ uint32_t pack_u8x4(float a, float b, float c, float d) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(a, 0u, 0u);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(b, 1u, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(c, 2u, w);
+  return __builtin_amdgcn_cvt_pk_u8_f32(d, 3u, w);
+}
 
 // S^T = K^ Q^T for one 64-key tile: two 32x32 INT32 blocks.
 template <int D>
@@ -305,7 +324,7 @@ template <int PV>
 constexpr int kKSlots = PV == kPvFp16 ? 3 : 2;
 
 // Online softmax of one tile: returns alpha = exp2(m_old - m_new) and writes
-// P~ (FP8: 448 P~) into the MFMA operand.  MASK selects the variant that
+// P~ (FP8: 448 P~; INT8: round(127 P~)) into the MFMA operand.  MASK selects the variant that
 // masks keys >= N and (causal) keys > query; a fully masked tile leaves the
 // state unchanged (P~ = 0, alpha = 1).
 template <int PV, bool CAUSAL, bool MASK>
@@ -341,7 +360,15 @@ __device__ __forceinline__ float softmax_tile(v16i (&s)[2], float& m_run, float&
   } else {
     const float mt = (float)mx * ts.c;
     m_new = fmaxf(m_run, mt);
-    nb = kLog2_448 - m_new;
+    nb = (PV == kPvInt8 ? kLog2_127 : kLog2_448) - m_new;
+    if constexpr (PV == kPvInt8) {
+      // 127 P~ of the row's largest score must round to at most 127 (128
+      // would read as -128 in the INT8 MFMA): when |m| is so large that the
+      // float32 rounding of nb lifts it, lower nb by the excess.  Every other
+      // score's argument is at most this one's (fma is monotone in s).
+      const float tmax = __builtin_fmaf((float)mx, ts.c, nb);
+      nb -= fmaxf(tmax - kLog2_127, 0.f);
+    }
   }
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 
@@ -386,7 +413,9 @@ __device__ __forceinline__ float softmax_tile(v16i (&s)[2], float& m_run, float&
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int blk = w >> 2, r0 = 4 * (w & 3);
-      pt.w[w] = (int)pack_fp8x4(p[blk][r0], p[blk][r0 + 1], p[blk][r0 + 2], p[blk][r0 + 3]);
+      pt.w[w] = PV == kPvFp8
+                    ? (int)pack_fp8x4(p[blk][r0], p[blk][r0 + 1], p[blk][r0 + 2], p[blk][r0 + 3])
+                    : (int)pack_u8x4(p[blk][r0], p[blk][r0 + 1], p[blk][r0 + 2], p[blk][r0 + 3]);
     }
   }
   l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
@@ -394,10 +423,12 @@ __device__ __forceinline__ float softmax_tile(v16i (&s)[2], float& m_run, float&
   return alpha;
 }
 
-// O^T += V^T P~^T for one tile, V from LDS.
+// O^T += V^T P~^T for one tile, V from LDS.  INT8: O = alpha O + P^ V^ with
+// the INT32 product of the tile converted to float (|P^ V^| <= 64 127^2 <
+// 2^24, exact), alpha being the rescale factor of this tile's softmax.
 template <int D, int PV>
 __device__ __forceinline__ void pv_tile(v16f (&o)[D / 32], const PTile<PV>& pt,
-                                        const uint8_t* vb, int n, int hh) {
+                                        const uint8_t* vb, int n, int hh, float alpha = 1.f) {
   constexpr int NCB = D / 32;
   if constexpr (PV == kPvFp16) {
 #pragma unroll
@@ -412,7 +443,7 @@ __device__ __forceinline__ void pv_tile(v16f (&o)[D / 32], const PTile<PV>& pt,
                                                        0, 0);
       }
     }
-  } else {
+  } else if constexpr (PV == kPvFp8) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int row = 32 * cb + n;
@@ -422,6 +453,26 @@ __device__ __forceinline__ void pv_tile(v16f (&o)[D / 32], const PTile<PV>& pt,
       const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       // scale operands 127 = E8M0 exponent of 1.0 (no block scaling)
       o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pt.w, o[cb], 0, 0, 0, 127, 0, 127);
+    }
+  } else {
+    const v4i plo = {pt.w[0], pt.w[1], pt.w[2], pt.w[3]};
+    const v4i phi = {pt.w[4], pt.w[5], pt.w[6], pt.w[7]};
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int row = 32 * cb + n;
+      const int sw = row_swizzle<64>(row);
+      const v4i a0 = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh) ^ sw) << 4));
+      const v4i a1 = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh + 1) ^ sw) << 4));
+      v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, plo, v16i{}, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, phi, acc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // copy the element to a scalar first (see softmax_tile)
+        const int pr = acc[r];
+        o[cb][r] = __builtin_fmaf(o[cb][r], alpha, (float)pr);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -771,6 +822,9 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   for (int cb = 0; cb < NCB; ++cb) o[cb] = v16f{};
   v16i sA[2], sB[2];
   PTile<PV> pA, pB;
+  // INT8: the rescale factor of the tile whose P^ V^ comes next, applied in
+  // the same fused multiply-add that adds the product
+  float alpha_pend = 1.f;
 
   auto softmax_any = [&](v16i (&sc)[2], PTile<PV>& pn, int t) __attribute__((always_inline)) {
     const TileScale ts = tile_scale<PV>(cq, ks_bh[t]);
@@ -822,6 +876,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     __syncthreads();
   };
   int j = 0;
+  // INT8 P~V runs every step through the generic path below
   if constexpr (NKS == 3) {
     // six steps per trip: with j a multiple of 6 every K^ slot (t % 3) is a
     // constant, so all LDS addresses are immediates
@@ -834,9 +889,36 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
       steady.template operator()<5>(j + 5, 2, 1, 0);
     }
   }
-  for (; j + 4 < nt && j + 2 < nt_full; j += 2) {
-    steady.template operator()<0>(j, kslot(j + 3, 3), kslot(j + 2, 2), kslot(j + 1, 1));
-    steady.template operator()<1>(j + 1, kslot(j + 4, 4), kslot(j + 3, 3), kslot(j + 2, 2));
+  if constexpr (PV != kPvInt8) {
+    for (; j + 4 < nt && j + 2 < nt_full; j += 2) {
+      steady.template operator()<0>(j, kslot(j + 3, 3), kslot(j + 2, 2), kslot(j + 1, 1));
+      steady.template operator()<1>(j + 1, kslot(j + 4, 4), kslot(j + 3, 3), kslot(j + 2, 2));
+    }
+  } else {
+    // INT8: the same unmasked steps with every load and MFMA present, in
+    // source order (P^ V^(jj), S(jj+2), softmax(S(jj+1))), the rescale of each
+    // tile folded into the next tile's product
+    auto plain = [&]<int U>(int jj) __attribute__((always_inline)) {
+      kld.template issue<false>(krs, (jj + 3) * kKvTile, N, kl0 + ((U + 3) & 1) * KB, wave);
+      VL::issue(vrs, jj + 1, vl[1 - U], wave, lane);
+      v16i(&s_cur)[2] = U == 0 ? sB : sA;
+      v16i(&s_new)[2] = U == 0 ? sA : sB;
+      PTile<PV>& p_cur = U == 0 ? pA : pB;
+      PTile<PV>& p_new = U == 0 ? pB : pA;
+      const float dk = dk_next;
+      dk_next = ks_bh[jj + 2];
+      pv_tile<D, PV>(o, p_cur, vbuf[U], n, hh, alpha_pend);
+      alpha_pend = softmax_tile<PV, CAUSAL, false>(s_cur, m_run, l_run, p_new,
+                                                   tile_scale<PV>(cq, dk), grid, 0, N, 0, hh);
+      qk_tile<D>(s_new, qf, kbuf[U], n, hh, init);
+      asm volatile("" ::"s"(dk_next));
+      wait_lds_loads();
+      __syncthreads();
+    };
+    for (; j + 4 < nt && j + 2 < nt_full; j += 2) {
+      plain.template operator()<0>(j);
+      plain.template operator()<1>(j + 1);
+    }
   }
   // Tail: the last steps, with masking and missing tiles handled explicitly.
   for (; j < nt; j += 2) {
@@ -852,16 +934,25 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
         v16i(&s_new)[2] = u == 0 ? sA : sB;
         PTile<PV>& p_cur = u == 0 ? pA : pB;
         PTile<PV>& p_new = u == 0 ? pB : pA;
-        if (jj + 2 < nt) qk_tile<D>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init);
-        pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh);
-        if (jj + 1 < nt) rescale<D>(o, softmax_any(s_cur, p_new, jj + 1));
+        if constexpr (PV == kPvInt8) {
+          // P^ V^, softmax, then the next scores: the two score tiles are
+          // never live at once (the INT32 product needs the registers)
+          pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh, alpha_pend);
+          if (jj + 1 < nt) alpha_pend = softmax_any(s_cur, p_new, jj + 1);
+          if (jj + 2 < nt) qk_tile<D>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init);
+        } else {
+          if (jj + 2 < nt) qk_tile<D>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init);
+          pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh, alpha_pend);
+          if (jj + 1 < nt) rescale<D>(o, softmax_any(s_cur, p_new, jj + 1));
+        }
         wait_lds_loads();
         __syncthreads();
       }
     }
   }
 
-  // Epilogue: O = O / l (FP8: l is in units of 448 P~, and delta_V per channel).
+  // Epilogue: O = O / l (FP8, INT8: l is in units of 448 P~ or 127 P~, and
+  // delta_V per channel).
   const float l_tot = pair_sum_f32(l_run);
   const float inv = 1.0f / l_tot;
   if (qrow < N) {
@@ -877,7 +968,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           y[u] = o[cb][4 * j4 + u] * inv;
-          if constexpr (PV == kPvFp8) y[u] *= v_scale[(size_t)bh * D + c0 + u];
+          if constexpr (PV != kPvFp16) y[u] *= v_scale[(size_t)bh * D + c0 + u];
         }
         store4<OUT>(out, orow + c0, y[0], y[1], y[2], y[3]);
       }
@@ -956,8 +1047,10 @@ hipError_t launch_attn(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_
                                        B, H, N, nhd, out, s);
   SAGE_ATTN_CASE(64, 0, 0) SAGE_ATTN_CASE(64, 0, 1) SAGE_ATTN_CASE(64, 0, 2)
   SAGE_ATTN_CASE(64, 1, 0) SAGE_ATTN_CASE(64, 1, 1) SAGE_ATTN_CASE(64, 1, 2)
+  SAGE_ATTN_CASE(64, 2, 0) SAGE_ATTN_CASE(64, 2, 1) SAGE_ATTN_CASE(64, 2, 2)
   SAGE_ATTN_CASE(128, 0, 0) SAGE_ATTN_CASE(128, 0, 1) SAGE_ATTN_CASE(128, 0, 2)
   SAGE_ATTN_CASE(128, 1, 0) SAGE_ATTN_CASE(128, 1, 1) SAGE_ATTN_CASE(128, 1, 2)
+  SAGE_ATTN_CASE(128, 2, 0) SAGE_ATTN_CASE(128, 2, 1) SAGE_ATTN_CASE(128, 2, 2)
 #undef SAGE_ATTN_CASE
   return hipErrorInvalidValue;
 }

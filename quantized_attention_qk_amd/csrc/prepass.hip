@@ -4,7 +4,9 @@
 //   of Q/sqrt(d) and of the smoothed K (§3 Algorithm 1; the SageAttention2++
 //   review page, section 三 core formulas: delta = max|X|/127), and the
 //   preparation of V: fp16, or E4M3 with delta_V = colmax|V|/448 (same
-//   section of the SageAttention2++ review page).
+//   section of the SageAttention2++ review page), or INT8 with delta_V =
+//   colmax|V|/127 for the all-INT8 kernel variant (SageAttention detail page,
+//   §3 Figure 5).
 //
 // Every quantisation decision is taken in float32 in a fixed order so that the
 // codes and scales are reproducible bit for bit: no FP contraction (this file
@@ -163,14 +165,16 @@ __global__ __launch_bounds__(256) void colstats_kernel(const uint16_t* __restric
                                           part_max, blockIdx.y, chunk, threadIdx.x % P);
 }
 
-// Finalise: mean = (sequential sum of the chunk partials) / N; for FP8 V,
-// colmax = max of the partial maxima, delta_V = colmax/448, r = 448/colmax.
+// Finalise: mean = (sequential sum of the chunk partials) / N; for quantised
+// V, colmax = max of the partial maxima, delta_V = colmax/vr, r = vr/colmax
+// with vr the code range (FP8 448, INT8 127).
 template <int D, bool DO_K, bool DO_V>
 __device__ __forceinline__ void finalize_channel(const float* __restrict__ part_sum,
                                                  const float* __restrict__ part_max, int N,
                                                  int nchunks, float* __restrict__ k_mean,
                                                  float* __restrict__ v_scale,
-                                                 float* __restrict__ v_recip, int bh, int c) {
+                                                 float* __restrict__ v_recip, float vr, int bh,
+                                                 int c) {
   {
     if constexpr (DO_K) {
       float tot = 0.f;
@@ -182,8 +186,8 @@ __device__ __forceinline__ void finalize_channel(const float* __restrict__ part_
       float cm = 0.f;
 #pragma unroll 16
       for (int j = 0; j < nchunks; ++j) cm = fmaxf(cm, part_max[((size_t)bh * nchunks + j) * D + c]);
-      v_scale[(size_t)bh * D + c] = cm / 448.f;
-      v_recip[(size_t)bh * D + c] = cm > 0.f ? 448.f / cm : 0.f;
+      v_scale[(size_t)bh * D + c] = cm / vr;
+      v_recip[(size_t)bh * D + c] = cm > 0.f ? vr / cm : 0.f;
     }
   }
 }
@@ -193,10 +197,10 @@ __global__ __launch_bounds__(128) void finalize_kernel(const float* __restrict__
                                                        const float* __restrict__ part_max, int N,
                                                        int nchunks, float* __restrict__ k_mean,
                                                        float* __restrict__ v_scale,
-                                                       float* __restrict__ v_recip) {
+                                                       float* __restrict__ v_recip, float vr) {
   for (int c = threadIdx.x; c < D; c += blockDim.x)
     finalize_channel<D, DO_K, DO_V>(part_sum, part_max, N, nchunks, k_mean, v_scale, v_recip,
-                                    blockIdx.x, c);
+                                    vr, blockIdx.x, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -367,7 +371,7 @@ __device__ __forceinline__ void prep_v_tile(const uint16_t* __restrict__ v,
       *reinterpret_cast<uint4*>(out + (size_t)g * 16) = uint4{w[0], w[1], w[2], w[3]};
     }
   } else {
-    const float* rc = v_recip;   // this head's 448/colmax, d entries
+    const float* rc = v_recip;   // this head's range/colmax, d entries
     for (int g = threadIdx.x; g < D * 4; g += 256) {
       const int c = g >> 2;
       const int lq = (g & 3) ^ row_swizzle<64>(c);
@@ -382,7 +386,8 @@ __device__ __forceinline__ void prep_v_tile(const uint16_t* __restrict__ v,
           const int key = 32 * ((p >> 4) & 1) + 8 * ((p & 15) >> 2) + 4 * (p >> 5) + (p & 3);
           f[u] = in_to_f32<DT>(tile[key * LD + c]) * r;
         }
-        w[e >> 2] = pack_fp8x4(f[0], f[1], f[2], f[3]);
+        w[e >> 2] = PV == kPvFp8 ? pack_fp8x4(f[0], f[1], f[2], f[3])
+                                 : pack_i8x4_sym(f[0], f[1], f[2], f[3]);
       }
       *reinterpret_cast<uint4*>(out + (size_t)g * 16) = uint4{w[0], w[1], w[2], w[3]};
     }
@@ -395,8 +400,8 @@ __global__ __launch_bounds__(256) void prep_v_kernel(const uint16_t* __restrict_
                                                      int H, int nhd, int ntiles,
                                                      uint8_t* __restrict__ v_out) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[PrepVTile<D>::HALVES];
-  prep_v_tile<DT, D, PV>(v, PV == kPvFp8 ? v_recip + (size_t)blockIdx.y * D : nullptr, N, H, nhd,
-                         ntiles, v_out, blockIdx.y, blockIdx.x, tile);
+  prep_v_tile<DT, D, PV>(v, PV != kPvFp16 ? v_recip + (size_t)blockIdx.y * D : nullptr, N, H,
+                         nhd, ntiles, v_out, blockIdx.y, blockIdx.x, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -558,7 +563,7 @@ __global__ __launch_bounds__(256) void prepass_roles_kernel(
       __syncthreads();
       for (int c = threadIdx.x; c < D; c += 256)
         finalize_channel<D, true, false>(part_sum, nullptr, N, nch, k_mean, nullptr, nullptr,
-                                         bh, c);
+                                         0.f, bh, c);
       __syncthreads();
       const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
       for (int blk = wave; blk < nkb; blk += 4)
@@ -576,14 +581,15 @@ __global__ __launch_bounds__(256) void prepass_roles_kernel(
   }
   if constexpr (DO_V) {
     if (role >= ntiles) return;
-    if constexpr (PV == kPvFp8) {
+    if constexpr (PV != kPvFp16) {
+      constexpr float VR = PV == kPvInt8 ? 127.f : 448.f;
       __shared__ float part[4 * D], vrc[D];
       head_colmax<DT, D>(v, bh, N, H, nhd, part, vrc);
       // the same expressions as the finalisation of the multi-kernel path
       for (int c = threadIdx.x; c < D; c += 256) {
         const float cm = vrc[c];
-        if (role == 0) v_scale[(size_t)bh * D + c] = cm / 448.f;
-        vrc[c] = cm > 0.f ? 448.f / cm : 0.f;
+        if (role == 0) v_scale[(size_t)bh * D + c] = cm / VR;
+        vrc[c] = cm > 0.f ? VR / cm : 0.f;
       }
       __syncthreads();
       prep_v_tile<DT, D, PV>(v, vrc, N, H, nhd, ntiles, v_out, bh, role, tile);
@@ -596,7 +602,7 @@ __global__ __launch_bounds__(256) void prepass_roles_kernel(
 // ---------------------------------------------------------------------------
 // Launchers.
 template <int DT, int D, bool ROPE>
-static hipError_t colstats_dispatch(const void* k, const void* v, int B, int H, int N,
+static hipError_t colstats_dispatch(const void* k, const void* v, int B, int H, int N, float vr,
                                     const InLayout& in, float* part_sum, float* part_max,
                                     float* k_mean, float* v_scale, float* v_recip,
                                     hipStream_t s) {
@@ -611,7 +617,7 @@ static hipError_t colstats_dispatch(const void* k, const void* v, int B, int H, 
                                                             in.rope_cos, in.rope_sin, part_sum, \
                                                             part_max);                          \
   finalize_kernel<D, DK, DV><<<B * H, 128, 0, s>>>(part_sum, part_max, N, nch, k_mean, v_scale, \
-                                                   v_recip);
+                                                   v_recip, vr);
   if (dk && dv) {
     SAGE_COLSTATS(true, true)
   } else if (dk) {
@@ -624,15 +630,16 @@ static hipError_t colstats_dispatch(const void* k, const void* v, int B, int H, 
 }
 
 hipError_t launch_colstats(const void* k, const void* v, int dtype, int B, int H, int N, int d,
-                           const InLayout& in, float* part_sum, float* part_max, float* k_mean,
-                           float* v_scale, float* v_recip, hipStream_t s) {
+                           int pv_mode, const InLayout& in, float* part_sum, float* part_max,
+                           float* k_mean, float* v_scale, float* v_recip, hipStream_t s) {
   // RoPE rotates K only; V statistics never see it
   const bool rope = in.rope_cos != nullptr && k != nullptr;
+  const float vr = pv_mode == kPvInt8 ? 127.f : 448.f;
 #define SAGE_CS(DT, D)                                                                        \
   if (dtype == DT && d == D)                                                                  \
-    return rope ? colstats_dispatch<DT, D, true>(k, v, B, H, N, in, part_sum, part_max, k_mean, \
-                                                 v_scale, v_recip, s)                            \
-                : colstats_dispatch<DT, D, false>(k, v, B, H, N, in, part_sum, part_max,        \
+    return rope ? colstats_dispatch<DT, D, true>(k, v, B, H, N, vr, in, part_sum, part_max,     \
+                                                 k_mean, v_scale, v_recip, s)                    \
+                : colstats_dispatch<DT, D, false>(k, v, B, H, N, vr, in, part_sum, part_max,    \
                                                   k_mean, v_scale, v_recip, s);
   SAGE_CS(0, 64) SAGE_CS(0, 128) SAGE_CS(1, 64) SAGE_CS(1, 128)
 #undef SAGE_CS
@@ -685,8 +692,10 @@ hipError_t launch_prep_v(const void* v, const float* v_recip, int dtype, int B, 
 #define SAGE_PV_CASE(DT, D, PV)                                              \
   if (dtype == DT && d == D && pv_mode == PV)                                \
     return prep_v_dispatch<DT, D, PV>(v, v_recip, B, H, N, nhd, v_out, s);
-  SAGE_PV_CASE(0, 64, 0) SAGE_PV_CASE(0, 64, 1) SAGE_PV_CASE(0, 128, 0) SAGE_PV_CASE(0, 128, 1)
-  SAGE_PV_CASE(1, 64, 0) SAGE_PV_CASE(1, 64, 1) SAGE_PV_CASE(1, 128, 0) SAGE_PV_CASE(1, 128, 1)
+  SAGE_PV_CASE(0, 64, 0) SAGE_PV_CASE(0, 64, 1) SAGE_PV_CASE(0, 64, 2)
+  SAGE_PV_CASE(0, 128, 0) SAGE_PV_CASE(0, 128, 1) SAGE_PV_CASE(0, 128, 2)
+  SAGE_PV_CASE(1, 64, 0) SAGE_PV_CASE(1, 64, 1) SAGE_PV_CASE(1, 64, 2)
+  SAGE_PV_CASE(1, 128, 0) SAGE_PV_CASE(1, 128, 1) SAGE_PV_CASE(1, 128, 2)
 #undef SAGE_PV_CASE
   return hipErrorInvalidValue;
 }
@@ -725,8 +734,10 @@ hipError_t launch_prepass_head(const void* q, const void* k, const void* v, int 
 #define SAGE_PH(DT, D, PV)                                                     \
   if (dtype == DT && d == D && pv_mode == PV)                                  \
     return prepass_head_dispatch<DT, D, PV>(q, k, v, B, H, N, in, o, s);
-  SAGE_PH(0, 64, 0) SAGE_PH(0, 64, 1) SAGE_PH(0, 128, 0) SAGE_PH(0, 128, 1)
-  SAGE_PH(1, 64, 0) SAGE_PH(1, 64, 1) SAGE_PH(1, 128, 0) SAGE_PH(1, 128, 1)
+  SAGE_PH(0, 64, 0) SAGE_PH(0, 64, 1) SAGE_PH(0, 64, 2)
+  SAGE_PH(0, 128, 0) SAGE_PH(0, 128, 1) SAGE_PH(0, 128, 2)
+  SAGE_PH(1, 64, 0) SAGE_PH(1, 64, 1) SAGE_PH(1, 64, 2)
+  SAGE_PH(1, 128, 0) SAGE_PH(1, 128, 1) SAGE_PH(1, 128, 2)
 #undef SAGE_PH
   return hipErrorInvalidValue;
 }

@@ -53,7 +53,7 @@ Layout make_layout(int B, int H, int N, int d, int pv_mode) {
   L.v_scale = take(bh * d * 4);
   L.v_recip = take(bh * d * 4);
   L.part_sum = take(bh * nch * d * 4);
-  L.part_max = take(pv_mode == sage::kPvFp8 ? bh * nch * d * 4 : 0);
+  L.part_max = take(sage::v_quantised(pv_mode) ? bh * nch * d * 4 : 0);
   L.total = off;
   return L;
 }
@@ -95,7 +95,7 @@ int validate_fwd(const void* q, const void* k, const void* v, const void* o, int
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SAGE_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return SAGE_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return SAGE_ERR_INVALID_ARG;
+  if (!sage::pv_valid(pv_mode)) return SAGE_ERR_INVALID_ARG;
   if (dtype != SAGE_DT_F16 && dtype != SAGE_DT_BF16) return SAGE_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
@@ -120,7 +120,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, 
   int8_t* k_i8 = reinterpret_cast<int8_t*>(w + L.k_i8);
   uint8_t* v_t = w + L.v_t;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fp8 = pv_mode == SAGE_PV_FP8;
+  const bool qv = sage::v_quantised(pv_mode);
   hipError_t e;
   if (N <= sage::kHeadPrepassMaxN) {
     const sage::PrepassOut po{F(L.part_sum), F(L.k_mean), F(L.v_scale), q_i8, k_i8,
@@ -128,9 +128,9 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, 
     e = sage::launch_prepass_head(q, k, v, dtype, B, H, N, d, pv_mode, in, po, s);
     if (e != hipSuccess) return SAGE_ERR_HIP;
   } else {
-    e = sage::launch_colstats(k, fp8 ? v : nullptr, dtype, B, H, N, d, in, F(L.part_sum),
-                              fp8 ? F(L.part_max) : nullptr, F(L.k_mean), F(L.v_scale),
-                              F(L.v_recip), s);
+    e = sage::launch_colstats(k, qv ? v : nullptr, dtype, B, H, N, d, pv_mode, in,
+                              F(L.part_sum), qv ? F(L.part_max) : nullptr, F(L.k_mean),
+                              F(L.v_scale), F(L.v_recip), s);
     if (e != hipSuccess) return SAGE_ERR_HIP;
     e = sage::launch_quant_qk(q, k, F(L.k_mean), dtype, B, H, N, d, in, q_i8, k_i8,
                               F(L.q_scale), F(L.k_scale), s);
@@ -163,7 +163,7 @@ int sage_attn_get_tiling(int d, int causal, int pv_mode, int* q_block, int* k_bl
                          int* kv_tile, int* mean_chunk) {
   (void)causal;
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return SAGE_ERR_UNSUPPORTED;
+  if (!sage::pv_valid(pv_mode)) return SAGE_ERR_UNSUPPORTED;
   if (q_block) *q_block = sage::kQBlock;
   if (k_block) *k_block = sage::kKBlock;
   if (kv_tile) *kv_tile = sage::kKvTile;
@@ -173,7 +173,7 @@ int sage_attn_get_tiling(int d, int causal, int pv_mode, int* q_block, int* k_bl
 
 size_t sage_attn_workspace_bytes(int B, int H, int N, int d, int pv_mode) {
   if (!shape_ok(B, H, N, d)) return 0;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return 0;
+  if (!sage::pv_valid(pv_mode)) return 0;
   return make_layout(B, H, N, d, pv_mode).total;
 }
 
@@ -238,7 +238,7 @@ int sage_smooth_quant_qk_ex(const void* q, const void* k, int dtype, int layout,
     return hip_status(sage::launch_prepass_head(q, k, nullptr, dtype, B, H, N, d, SAGE_PV_FP16,
                                                 in, po, s));
   }
-  hipError_t e = sage::launch_colstats(k, nullptr, dtype, B, H, N, d, in,
+  hipError_t e = sage::launch_colstats(k, nullptr, dtype, B, H, N, d, SAGE_PV_FP16, in,
                                        static_cast<float*>(scratch), nullptr, k_mean, nullptr,
                                        nullptr, s);
   if (e != hipSuccess) return SAGE_ERR_HIP;
@@ -248,13 +248,13 @@ int sage_smooth_quant_qk_ex(const void* q, const void* k, int dtype, int layout,
 
 size_t sage_quant_v_bytes(int B, int H, int N, int d, int pv_mode) {
   if (!shape_ok(B, H, N, d)) return 0;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return 0;
+  if (!sage::pv_valid(pv_mode)) return 0;
   return (size_t)B * H * ceil_div(N, sage::kKvTile) * sage::v_tile_bytes(d, pv_mode);
 }
 
 size_t sage_quant_v_scratch_bytes(int B, int H, int N, int d, int pv_mode) {
   if (!shape_ok(B, H, N, d)) return 0;
-  if (pv_mode != SAGE_PV_FP8) return 0;
+  if (!sage::v_quantised(pv_mode)) return 0;
   // partial maxima + reciprocal scales
   return align_up((size_t)B * H * ceil_div(N, sage::kMeanChunk) * d * 4) + (size_t)B * H * d * 4;
 }
@@ -272,11 +272,11 @@ int sage_quant_v_ex(const void* v, int dtype, int layout, int B, int H, int N, i
   if (!v || !v_out) return SAGE_ERR_INVALID_ARG;
   if (!aligned16(v) || !aligned16(v_out)) return SAGE_ERR_INVALID_ARG;
   if (dtype != SAGE_DT_F16 && dtype != SAGE_DT_BF16) return SAGE_ERR_INVALID_ARG;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return SAGE_ERR_INVALID_ARG;
+  if (!sage::pv_valid(pv_mode)) return SAGE_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
   if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
-  const bool fp8 = pv_mode == SAGE_PV_FP8;
-  if (fp8 && (!v_scale || !scratch || !aligned16(scratch) ||
+  const bool qv = sage::v_quantised(pv_mode);
+  if (qv && (!v_scale || !scratch || !aligned16(scratch) ||
               (reinterpret_cast<uintptr_t>(v_scale) & 7u)))
     return SAGE_ERR_INVALID_ARG;
   if (scratch_bytes < sage_quant_v_scratch_bytes(B, H, N, d, pv_mode)) return SAGE_ERR_WORKSPACE;
@@ -285,7 +285,7 @@ int sage_quant_v_ex(const void* v, int dtype, int layout, int B, int H, int N, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* v_recip = nullptr;
   float* part_max = nullptr;
-  if (fp8) {
+  if (qv) {
     part_max = static_cast<float*>(scratch);
     v_recip = reinterpret_cast<float*>(
         static_cast<uint8_t*>(scratch) +
@@ -298,10 +298,10 @@ int sage_quant_v_ex(const void* v, int dtype, int layout, int B, int H, int N, i
     return hip_status(sage::launch_prepass_head(nullptr, nullptr, v, dtype, B, H, N, d, pv_mode,
                                                 in, po, s));
   }
-  if (fp8) {
+  if (qv) {
     const sage::InLayout in{layout, nullptr, nullptr};
-    hipError_t e = sage::launch_colstats(nullptr, v, dtype, B, H, N, d, in, nullptr, part_max,
-                                         nullptr, v_scale, v_recip, s);
+    hipError_t e = sage::launch_colstats(nullptr, v, dtype, B, H, N, d, pv_mode, in, nullptr,
+                                         part_max, nullptr, v_scale, v_recip, s);
     if (e != hipSuccess) return SAGE_ERR_HIP;
   }
   return hip_status(sage::launch_prep_v(v, v_recip, dtype, B, H, N, d, pv_mode, layout,
@@ -317,10 +317,10 @@ int sage_attn_fwd_quantized(const int8_t* q_i8, const int8_t* k_i8, const void* 
       (reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u))
     return SAGE_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return SAGE_ERR_INVALID_ARG;
+  if (!sage::pv_valid(pv_mode)) return SAGE_ERR_INVALID_ARG;
   if (out_dtype != SAGE_DT_F16 && out_dtype != SAGE_DT_BF16 && out_dtype != SAGE_OUT_F32)
     return SAGE_ERR_INVALID_ARG;
-  if (pv_mode == SAGE_PV_FP8 && (!v_scale || (reinterpret_cast<uintptr_t>(v_scale) & 3u)))
+  if (sage::v_quantised(pv_mode) && (!v_scale || (reinterpret_cast<uintptr_t>(v_scale) & 3u)))
     return SAGE_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
   if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;

@@ -50,6 +50,19 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return (uint32_t)w;
 }
 
+// Four floats -> four symmetric INT8 codes, clamp(rne(x), -127, 127), packed
+// little-endian (first value in the low byte).
+__device__ __forceinline__ uint32_t pack_i8x4_sym(float a, float b, float c, float d) {
+  const float x[4] = {a, b, c, d};
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = (int)fminf(fmaxf(__builtin_rintf(x[i]), -127.f), 127.f);
+    w |= ((uint32_t)q & 0xffu) << (8 * i);
+  }
+  return w;
+}
+
 // LDS swizzles.  gfx950's LDS serves a ds_read_b128 sixteen lanes at a time
 // (256 bytes = all 64 banks).  The 16-byte chunk `k` of row `r` is stored at
 // chunk k ^ swz(r): for 128-byte rows, rows r and r+1 share a 256-byte bank

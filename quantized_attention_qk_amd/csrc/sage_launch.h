@@ -22,6 +22,11 @@ static_assert(kKvTile == kKBlock, "one delta_K per KV tile");
 
 constexpr int kPvFp16 = 0;
 constexpr int kPvFp8 = 1;
+constexpr int kPvInt8 = 2;
+
+inline bool pv_valid(int pv) { return pv == kPvFp16 || pv == kPvFp8 || pv == kPvInt8; }
+// FP8 and INT8 P~V quantise V per channel (delta_V = colmax|V| / range).
+inline bool v_quantised(int pv) { return pv == kPvFp8 || pv == kPvInt8; }
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -39,11 +44,12 @@ struct InLayout {
 };
 
 // Prepass: column statistics of K (float32 partial sums per 256-token chunk)
-// and, if part_max != nullptr, of |V| (partial maxima), then the finalised
-// mean (and V scale / reciprocal when v_scale != nullptr).
+// and, if v != nullptr, of |V| (partial maxima into part_max), then the
+// finalised mean and, for V, delta_V and its reciprocal in the range of
+// pv_mode (FP8 448, INT8 127).
 hipError_t launch_colstats(const void* k, const void* v, int dtype, int B, int H, int N, int d,
-                           const InLayout& in, float* part_sum, float* part_max, float* k_mean,
-                           float* v_scale, float* v_recip, hipStream_t s);
+                           int pv_mode, const InLayout& in, float* part_sum, float* part_max,
+                           float* k_mean, float* v_scale, float* v_recip, hipStream_t s);
 
 // Prepass: INT8 quantisation of Q/sqrt(d) (128-token blocks) and of K - mean
 // (64-token blocks).  Either q or k may be null to skip that tensor.
@@ -51,7 +57,7 @@ hipError_t launch_quant_qk(const void* q, const void* k, const float* k_mean, in
                            int H, int N, int d, const InLayout& in, int8_t* q_i8, int8_t* k_i8,
                            float* q_scale, float* k_scale, hipStream_t s);
 
-// Prepass: V -> fp16 or E4M3 in the tiled layout of the attention kernel.
+// Prepass: V -> fp16, E4M3 or INT8 in the tiled layout of the attention kernel.
 hipError_t launch_prep_v(const void* v, const float* v_recip, int dtype, int B, int H, int N,
                          int d, int pv_mode, int nhd, uint8_t* v_out, hipStream_t s);
 

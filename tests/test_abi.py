@@ -48,7 +48,7 @@ def test_tiling_contract_matches_oracle():
     import oracle
     vals = [ctypes.c_int() for _ in range(4)]
     for d in (64, 128):
-        for pv in (0, 1):
+        for pv in (0, 1, 2):
             assert lib().sage_attn_get_tiling(d, 0, pv, *[ctypes.byref(v) for v in vals]) == OK
             assert [v.value for v in vals] == [oracle.Q_BLOCK, oracle.K_BLOCK, oracle.KV_TILE,
                                                oracle.MEAN_CHUNK]
@@ -61,16 +61,20 @@ def test_workspace_sizes():
     B, H, N, d = 1, 24, 16384, 128
     w16 = h.sage_attn_workspace_bytes(B, H, N, d, 0)
     w8 = h.sage_attn_workspace_bytes(B, H, N, d, 1)
+    wi8 = h.sage_attn_workspace_bytes(B, H, N, d, 2)
     elems = B * H * N * d
     # Q^ + K^ (int8) + V' (fp16) at least; V^ (e4m3) is half of V'
     assert w16 >= 2 * elems + 2 * elems
     assert w8 >= 2 * elems + elems and w8 < w16
+    assert wi8 == w8                      # INT8 V^ has the FP8 layout and size
     assert h.sage_attn_workspace_bytes(1, 1, 0, 64, 0) == 0
     assert h.sage_attn_workspace_bytes(1, 1, 10, 96, 0) == 0
     assert h.sage_attn_workspace_bytes(1, 1, 10, 64, 3) == 0
     assert h.sage_quant_v_bytes(1, 2, 65, 64, 0) == 2 * 2 * 64 * 128
     assert h.sage_quant_v_bytes(1, 2, 65, 64, 1) == 2 * 2 * 64 * 64
+    assert h.sage_quant_v_bytes(1, 2, 65, 64, 2) == 2 * 2 * 64 * 64
     assert h.sage_quant_v_scratch_bytes(1, 2, 65, 64, 0) == 0
+    assert h.sage_quant_v_scratch_bytes(1, 2, 65, 64, 2) == h.sage_quant_v_scratch_bytes(1, 2, 65, 64, 1) > 0
     assert h.sage_smooth_quant_qk_scratch_bytes(2, 3, 257, 128) == 2 * 3 * 2 * 128 * 4
 
 
@@ -85,7 +89,8 @@ def fwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(ws=None), INVALID),
     (dict(q=P + 8), INVALID), (dict(o=P + 2), INVALID), (dict(ws=P + 16), INVALID),
-    (dict(causal=2), INVALID), (dict(pv=2), INVALID), (dict(dtype=5), INVALID),
+    (dict(causal=2), INVALID), (dict(pv=3), INVALID), (dict(pv=-1), INVALID),
+    (dict(dtype=5), INVALID),
     (dict(N=0), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID),
     (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(N=(1 << 24) + 1), UNSUPPORTED),
     (dict(o=P), INVALID), (dict(wsb=1000), WORKSPACE),

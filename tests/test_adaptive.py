@@ -22,6 +22,19 @@ def test_choose_mode(cos, mode):
     assert choose_mode(cos) == mode
 
 
+def test_choose_mode_candidates():
+    # the page's own pair (all-INT8 kernel or FP16) and the ordered 3-way choice
+    assert choose_mode(0.9985, candidates=("int8",)) == "int8"
+    assert choose_mode(0.9975, candidates=("int8",)) == "fp16"
+    cos = {"fp8": 0.9990, "int8": 0.9970}
+    assert choose_mode(cos, candidates=("fp8", "int8")) == "fp8"
+    assert choose_mode(cos, candidates=("int8", "fp8")) == "fp8"
+    assert choose_mode({"fp8": 0.99, "int8": 0.999}, candidates=("fp8", "int8")) == "int8"
+    assert choose_mode({"fp8": 0.99, "int8": 0.99}, candidates=("fp8", "int8")) == "fp16"
+    with pytest.raises(ValueError):
+        choose_mode(0.999, candidates=("fp16",))
+
+
 def test_sample_rows_seeded_and_bounded():
     a = sample_rows(1000, 64, seed=3)
     b = sample_rows(1000, 64, seed=3)
@@ -39,6 +52,9 @@ def test_modes_round_trip(tmp_path):
     p = tmp_path / "modes.json"
     save_modes(t, str(p))
     assert load_modes(str(p)) == t
+    t2 = {"a": {"pv_mode": "int8", "cos_int8": 0.999}}
+    save_modes(t2, str(p))
+    assert load_modes(str(p)) == t2
     p.write_text(json.dumps({"x": {"pv_mode": "int4"}}))
     with pytest.raises(ValueError):
         load_modes(str(p))

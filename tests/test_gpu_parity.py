@@ -7,9 +7,10 @@ Bar (each check names it):
   oracle's own codes;
 * O (float32 output of the same kernels): max |O - O_oracle| <= 2e-3 and
   cosine >= 0.9999; O in the 16-bit input dtype additionally within one ulp
-  of that dtype (the final rounding).  FP8 P~V: each element may exceed 2e-3
-  by the oracle's bound for 448 P~ values that lie, to float32 accuracy, on an
-  E4M3 rounding boundary (reading C-s; the count is reported).
+  of that dtype (the final rounding).  FP8 and INT8 P~V: each element may
+  exceed 2e-3 by the oracle's bound for 448 P~ (127 P~) values that lie, to
+  float32 accuracy, on a rounding boundary of E4M3 (of the integers) (reading
+  C-s; the count is reported).
 Small cases compare every element; the five full workloads compare the whole
 prepass and sampled query rows of O (first, last, ragged tail, diagonal and
 seeded rows of several heads), computed by the oracle row by row.
@@ -21,7 +22,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import WORKLOADS, make_inputs, small
+from workloads import WORKLOADS, make_inputs, named, small
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +68,14 @@ SMALL = [
     small("r2000b", N=2000, d=128, dtype="bf16", extras="ramp"),
     small("r1500c", N=1500, d=128, causal=True, extras="ramp"),
     small("r1000f8", N=1000, d=64, pv_mode="fp8", extras="ramp"),
+    # INT8 P~V (all-INT8 variant): both d, causal, bf16, several heads, the
+    # multi-kernel prepass and rising scores
+    small("i197", N=197, d=64, pv_mode="int8"),
+    small("i300c", N=300, d=128, causal=True, dtype="bf16", pv_mode="int8"),
+    small("i640", B=2, H=3, N=640, d=128, dtype="bf16", pv_mode="int8", extras="q8_kbias5"),
+    small("i2113", B=1, H=2, N=2113, d=128, pv_mode="int8", extras="kbias4"),
+    small("i1105c", N=1105, d=64, H=1, causal=True, pv_mode="int8", extras="kchan20"),
+    small("r1000i8", N=1000, d=64, pv_mode="int8", extras="ramp"),
 ]
 
 
@@ -99,7 +108,7 @@ def check_prepass(inp, res, vt, vs, heads=None):
         gs = to_np(vs) if heads is None else to_np(vs)[:, heads]
         np.testing.assert_array_equal(gs.view(np.uint32), vscale.view(np.uint32),
                                       err_msg="delta_V bits")
-        np.testing.assert_array_equal(vv, codes, err_msg="V^ E4M3 codes")
+        np.testing.assert_array_equal(vv, codes, err_msg=f"V^ {wl.pv_mode} codes")
     return pq
 
 
@@ -132,16 +141,16 @@ def test_debug_s_bit_exact(wl):
 
 
 def compare_o(o_gpu, o_ref, what, allow=None):
-    """max |O - O_oracle| <= 2e-3 and cosine >= 0.9999.  FP8 P~V: `allow` is
-    the oracle's per-element bound on O's move from 448 P~ values that lie, to
-    float32 accuracy, on an E4M3 rounding boundary (reading C-s); the elements
-    that need it are reported."""
+    """max |O - O_oracle| <= 2e-3 and cosine >= 0.9999.  FP8 and INT8 P~V:
+    `allow` is the oracle's per-element bound on O's move from P~ / delta_P
+    values that lie, to float32 accuracy, on a rounding boundary of P^'s codes
+    (reading C-s); the elements that need it are reported."""
     err = np.abs(o_gpu.astype(np.float64) - o_ref)
     cos = oracle.cos_sim(o_gpu, o_ref)
     extra = ""
     if allow is not None:
         over = err > O_MAX_ABS
-        extra = f"  beyond 2e-3 (E4M3 boundary cases): {int(over.sum())}"
+        extra = f"  beyond 2e-3 (P^ boundary cases): {int(over.sum())}"
         assert np.all(err <= O_MAX_ABS + allow), \
             f"{what}: max excess {float((err - O_MAX_ABS - allow).max())}"
     note(f"{what}: max|dO| = {err.max():.3e}  cos = {cos:.7f}{extra}")
@@ -219,9 +228,9 @@ def sample_rows(N, causal, seed):
     return np.array(sorted(r for r in rows if 0 <= r < N))
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c3i8", "c4i8"])
 def test_full_workload(name):
-    wl = WORKLOADS[name]
+    wl = named(name)
     note(f"full workload {name}: {wl}")
     inp = make_inputs(wl)
     q, k, v = gpu_inputs(inp)

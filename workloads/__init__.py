@@ -28,7 +28,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "TABLE7", "SHARDS", "named", "make_inputs", "round_to_bf16_bits",
+__all__ = ["Workload", "WORKLOADS", "TABLE7", "SHARDS", "PV_INT8", "named", "make_inputs", "round_to_bf16_bits",
            "round_to_fp16", "bf16_bits_to_f32", "Inputs", "rope_tables", "to_nhd"]
 
 
@@ -41,7 +41,7 @@ class Workload:
     d: int
     dtype: str          # "fp16" or "bf16": element type of q, k, v and o
     causal: bool
-    pv_mode: str        # "fp16" or "fp8"
+    pv_mode: str        # "fp16", "fp8" or "int8"
     seed: int
     extras: str         # which outlier recipe to apply (see _apply_extras)
     note: str = ""
@@ -96,9 +96,20 @@ SHARDS = {
 }
 
 
+# The all-INT8 variant (INT8 P~V) of "SageAttention ..." detail page, §3
+# Figure 5, on the headline shape and on the FP8 workload's shape (same
+# inputs as c3 and c4, only the P~V precision differs).
+PV_INT8 = {
+    "c3i8": WORKLOADS["c3"].with_(name="c3i8", pv_mode="int8",
+                                  note="c3 with INT8 P~V (static delta_P = 1/127)"),
+    "c4i8": WORKLOADS["c4"].with_(name="c4i8", pv_mode="int8",
+                                  note="c4 with INT8 P~V (static delta_P = 1/127)"),
+}
+
+
 def named(name: str) -> Workload:
-    """A workload of WORKLOADS, TABLE7 or SHARDS by name."""
-    for table in (WORKLOADS, TABLE7, SHARDS):
+    """A workload of WORKLOADS, TABLE7, SHARDS or PV_INT8 by name."""
+    for table in (WORKLOADS, TABLE7, SHARDS, PV_INT8):
         if name in table:
             return table[name]
     raise KeyError(name)
