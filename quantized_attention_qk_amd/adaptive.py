@@ -40,14 +40,20 @@ def sample_rows(N: int, rows: int, seed: int) -> torch.Tensor:
 def layer_cosine(q, k, v, causal: bool = False, pv_mode: str = "fp8", rows: int = 512,
                  seed: int = 0) -> float:
     """Cosine similarity between the quantised output (pv_mode) and the
-    float32 reference, over a seeded subsample of query rows of all heads."""
+    float32 reference, over a seeded subsample of query rows of all heads.
+    An all-zero output (INT8 V can quantise every value of a channel whose
+    range one outlier token sets to 0) counts as cosine 0 against a nonzero
+    reference, and two all-zero outputs as 1."""
     N = q.shape[2]
     idx = sample_rows(N, rows, seed)
     out = sage_attn(q, k, v, causal=causal, pv_mode=pv_mode, out_f32=True)
     ref = ref_rows(q, k, v, idx.to(q.device), causal=causal)
     got = out[:, :, idx.to(q.device).long()].double().flatten()
     ref = ref.double().flatten()
-    return float((got @ ref) / (got.norm() * ref.norm()))
+    ng, nr = float(got.norm()), float(ref.norm())
+    if ng == 0.0 or nr == 0.0:
+        return 1.0 if ng == nr else 0.0
+    return float((got @ ref) / (ng * nr))
 
 
 FAST_MODES = ("fp8", "int8")

@@ -34,7 +34,7 @@ def note(msg):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("name", ["c3", "c4", "c5", "t7_cogvideox"])
+@pytest.mark.parametrize("name", ["c3", "c4", "c5", "t7_cogvideox", "c3i8", "c4i8"])
 def test_accuracy_against_full_precision(name):
     import quantized_attention_qk_amd as qa
     wl = named(name)
@@ -59,7 +59,8 @@ def test_accuracy_against_full_precision(name):
     got, meth, ref = np.stack(got), np.stack(meth), np.stack(ref)
     m_gpu = (oracle.cos_sim(got, ref), oracle.rel_l1(got, ref), oracle.rmse(got, ref))
     m_orc = (oracle.cos_sim(meth, ref), oracle.rel_l1(meth, ref), oracle.rmse(meth, ref))
-    key = "table2_int8_fp16" if wl.pv_mode == "fp16" else "table2_int8_e4m3"
+    key = {"fp16": "table2_int8_fp16", "fp8": "table2_int8_e4m3",
+           "int8": "table2_int8_int8"}[wl.pv_mode]
     g = GOLD[key]
     note(f"{name} ({wl.pv_mode.upper()} P~V) vs exact: GPU CosSim {m_gpu[0]:.6f} RelL1 "
          f"{m_gpu[1]:.4f} RMSE {m_gpu[2]:.3e} | oracle (method) CosSim {m_orc[0]:.6f} RelL1 "

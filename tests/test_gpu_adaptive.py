@@ -54,3 +54,14 @@ def test_adaptive_choice():
     note(f"table {table}")
     assert table["benign"]["pv_mode"] == "fp8" and table["benign"]["cos_fp8"] > 0.9985
     assert table["vout"]["pv_mode"] == "fp16" and table["vout"]["cos_fp8"] < 0.998
+    # the pages' own pair, all-INT8 kernel or FP16: the benign layer keeps
+    # INT8 P~V; on "vout" every ordinary V value quantises to 0 in INT8 (the
+    # outlier token sets each channel's range) and the output is all zero
+    note("select_pv_modes candidates int8, then fp8+int8")
+    t8 = qa.select_pv_modes(layers, rows=256, seed=0, candidates=("int8",))
+    note(f"table {t8}")
+    assert t8["benign"]["pv_mode"] == "int8" and t8["benign"]["cos_int8"] > 0.999
+    assert t8["vout"]["pv_mode"] == "fp16" and t8["vout"]["cos_int8"] == 0.0
+    t3 = qa.select_pv_modes(layers, rows=256, seed=0, candidates=("fp8", "int8"))
+    assert t3["benign"]["pv_mode"] == "fp8" and t3["vout"]["pv_mode"] == "fp16"
+    assert t3["benign"]["cos_int8"] == t8["benign"]["cos_int8"]

@@ -218,6 +218,24 @@ def test_fwd_deterministic_and_guard_bands(wl):
     assert torch.all(ws[:pad] == 0xA5) and torch.all(ws[-pad:] == 0xA5)
 
 
+@pytest.mark.parametrize("wl", [w for w in SMALL if w.name in ("s63", "s300c", "i300c", "i2113",
+                                                                "s2177")],
+                         ids=lambda w: w.name)
+def test_stages_equal_whole_pass(wl):
+    # sage_smooth_quant_qk + sage_quant_v + sage_attn_fwd_quantized on the
+    # prepared operands give the whole pass's output bit for bit
+    note(f"stages {wl}")
+    inp = make_inputs(wl)
+    q, k, v = gpu_inputs(inp)
+    whole = qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out_f32=True)
+    qk = qa().smooth_quant_qk(q, k)
+    vp, vs = qa().quant_v(v, wl.pv_mode)
+    staged = qa().sage_attn_quantized(qk, vp, vs, causal=wl.causal, pv_mode=wl.pv_mode,
+                                      out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(staged.view(torch.int32), whole.view(torch.int32))
+
+
 # ---------------------------------------------------------------------------
 # The five full workloads, at their real sizes and in the launch configuration
 # the benchmark times.

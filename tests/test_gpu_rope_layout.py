@@ -54,6 +54,8 @@ CASES = [
     small("r300", B=2, H=3, N=300, d=128, dtype="bf16", extras="q8_kbias5"),
     small("r640c8", N=640, d=128, causal=True, dtype="bf16", pv_mode="fp8", extras="kchan20"),
     small("r2113c8", N=2113, d=64, pv_mode="fp8", extras="kbias4"),
+    small("r300i8", B=2, H=3, N=300, d=128, dtype="bf16", pv_mode="int8", extras="q8_kbias5"),
+    small("r2113ci8", N=2113, d=64, causal=True, pv_mode="int8", extras="kbias4"),
 ]
 
 
