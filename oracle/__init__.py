@@ -7,7 +7,8 @@ HIP path.
 """
 from .sage_oracle import (  # noqa: F401
     Q_BLOCK, K_BLOCK, KV_TILE, MEAN_CHUNK, P_STATIC_FP8, P_STATIC_INT8,
-    column_mean, quantize_int8_blocks, smooth_quant_qk, prep_v, attention,
+    column_mean, quantize_int8_blocks, smooth_quant_qk, prep_v, attention, q_block_mean,
+    smooth_quantize_q_blocks, q_compensation, SQ_LIMIT, SQ_FRAC_BITS,
     sage_attention, brute_attention, cos_sim, rel_l1, rmse, s_int32_tile,
     inv_sqrt_d, rope_rotate_half,
 )

@@ -33,6 +33,24 @@ FP8 "8+8" P~V variant of [SA2pp] "三、技术架构"):
    (O = diag(exp(m_old - m_new)) O_prev + delta_P delta_V P^ V^).
 5. O = diag(l)^-1 O ([SA] §3 Algorithm 1).
 
+Optionally (smooth_q), Q is smoothed per block as SageAttention2 does ("SageAttention2"
+abstract page: smoothing Q improves the accuracy of the quantised QK^T; the
+SageAttention2++ review page, "三", smooths Q and K before quantising).  The
+pages give no formula; the reading here (parity pinned by exact constructions
+and integer brute force in tests/test_oracle_smooth_q.py):
+* per 128-token block, qbar = the block's token mean of Q' = Q/sqrt(d)
+  (float32, sequential in token order, one IEEE division by the block's token
+  count), Q~ = fp32(Q' - qbar), quantised as any block (a = max|Q~|,
+  r = fp32(127/a), codes, delta = fp32(a/127));
+* the mean is kept per channel as an integer on a grid 2^8 times finer than
+  the codes', w = rne(fp32(qbar r) 2^8), and its product with each key is
+  rounded once to the codes' grid: the compensation
+  C[t] = rne((w . K^[t]) / 2^8) (exact integer product, ties to even) is one
+  integer per query block and key, and S = delta_Q delta_K (Q~^ K^^T + C);
+* a block is smoothed only if a > 0 and 127 sum_c |w_c| <= 2^29 (so |C| stays
+  at most 2^21, like |Q^ K^^T| <= 127^2 d); any other block is quantised as
+  without smoothing (w = 0, C = 0).
+
 Readings where the pages leave a step open (each listed in the design notes):
 
 * Block sizes b_q, b_kv are not given: Q blocks of 128 tokens, K blocks of 64
@@ -148,11 +166,85 @@ def quantize_int8_blocks(x: np.ndarray, block: int):
     return np.ascontiguousarray(codes), delta
 
 
-def smooth_quant_qk(qf: np.ndarray, kf: np.ndarray, smooth: bool = True):
+SQ_FRAC_BITS = 8     # smooth Q: w is kept on a grid 2^8 times finer than the codes
+SQ_LIMIT = 2 ** 29   # smooth-Q guard: 127 * sum_c |w_c| must not exceed it
+
+
+def q_block_mean(qs: np.ndarray) -> np.ndarray:
+    """Per-(b, h, 128-token block, channel) mean of qs (float32 [B,H,N,d]):
+    float32 sum starting at 0.0f in increasing token order over the block's
+    tokens, then one IEEE division by their count (the last block may be
+    short).  Returns float32 [B, H, ceil(N/128), d]."""
+    qs = np.asarray(qs, dtype=np.float32)
+    B, H, N, d = qs.shape
+    nb = -(-N // Q_BLOCK)
+    pad = nb * Q_BLOCK - N
+    qp = np.concatenate([qs, np.zeros((B, H, pad, d), np.float32)], axis=2) if pad else qs
+    qp = qp.reshape(B, H, nb, Q_BLOCK, d)
+    acc = np.zeros((B, H, nb, d), np.float32)
+    for t in range(Q_BLOCK):
+        acc = acc + qp[:, :, :, t, :]            # padding adds +0.0: no change
+    cnt = np.minimum(Q_BLOCK, N - Q_BLOCK * np.arange(nb)).astype(np.float32)
+    return acc / cnt[None, None, :, None]
+
+
+def smooth_quantize_q_blocks(qs: np.ndarray):
+    """Smoothed per-block INT8 quantisation of Q' (reading in the module
+    docstring).  Returns (codes int8 [B,H,N,d], delta float32 [B,H,nb],
+    qbar float32 [B,H,nb,d] (0 for blocks left unsmoothed), w int32 [B,H,nb,d],
+    smoothed bool [B,H,nb])."""
+    qs = np.asarray(qs, dtype=np.float32)
+    B, H, N, d = qs.shape
+    nb = -(-N // Q_BLOCK)
+    pad = nb * Q_BLOCK - N
+    qbar = q_block_mean(qs)
+    qp = np.concatenate([qs, np.zeros((B, H, pad, d), np.float32)], axis=2) if pad else qs
+    qp = qp.reshape(B, H, nb, Q_BLOCK, d)
+    valid = (Q_BLOCK * np.arange(nb)[:, None] + np.arange(Q_BLOCK)[None, :]) < N   # [nb, 128]
+    qt = np.where(valid[None, None, :, :, None], (qp - qbar[:, :, :, None, :]).astype(np.float32),
+                  np.float32(0.0))
+    a = np.abs(qt).reshape(B, H, nb, -1).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        r = np.where(a > 0, INT8_RANGE / a, np.float32(0.0)).astype(np.float32)
+    w = np.rint((qbar * r[..., None]).astype(np.float32).astype(np.float64)
+                * 2.0 ** SQ_FRAC_BITS).astype(np.int64)
+    ok = (a > 0) & (127 * np.abs(w).sum(axis=-1) <= SQ_LIMIT)
+    # smoothed blocks
+    codes_s = np.clip(np.rint((qt * r[..., None, None]).astype(np.float32)), -127, 127)
+    # blocks left unsmoothed: the plain quantiser of Q'
+    plain, delta_p = quantize_int8_blocks(qs, Q_BLOCK)
+    plain = np.concatenate([plain, np.zeros((B, H, pad, d), np.int8)], axis=2) if pad else plain
+    plain = plain.reshape(B, H, nb, Q_BLOCK, d)
+    codes = np.where(ok[..., None, None], codes_s, plain).astype(np.int8)
+    codes = codes.reshape(B, H, nb * Q_BLOCK, d)[:, :, :N, :]
+    delta = np.where(ok, (a / INT8_RANGE).astype(np.float32), delta_p).astype(np.float32)
+    w = np.where(ok[..., None], w, 0).astype(np.int32)
+    qbar = np.where(ok[..., None], qbar, np.float32(0.0)).astype(np.float32)
+    return np.ascontiguousarray(codes), delta, qbar, w, ok
+
+
+def q_compensation(q_w: np.ndarray, k_i8: np.ndarray) -> np.ndarray:
+    """The compensation of smoothed Q blocks, C = rne((w K^^T) / 2^8): int32
+    [B, H, nb, N].  The product is exact (a float64 product of integers below
+    2^53); the division rounds to nearest, ties to even."""
+    p = np.einsum("bhqc,bhtc->bhqt", q_w.astype(np.float64),
+                  k_i8.astype(np.float64)).astype(np.int64)
+    q = p >> SQ_FRAC_BITS                                  # floor
+    rem = p - (q << SQ_FRAC_BITS)                          # in [0, 2^8)
+    half = 1 << (SQ_FRAC_BITS - 1)
+    q = q + ((rem > half) | ((rem == half) & (q & 1 == 1))).astype(np.int64)
+    return q.astype(np.int32)
+
+
+def smooth_quant_qk(qf: np.ndarray, kf: np.ndarray, smooth: bool = True,
+                    smooth_q: bool = False):
     """The prepass of [SA] §3 Algorithm 1: smooth K, quantise Q/sqrt(d) and K.
 
     Returns a dict with k_mean [B,H,d], q_i8, k_i8 [B,H,N,d],
-    q_scale [B,H,ceil(N/128)], k_scale [B,H,ceil(N/64)] (float32).
+    q_scale [B,H,ceil(N/128)], k_scale [B,H,ceil(N/64)] (float32).  With
+    smooth_q, Q is smoothed per block (module docstring) and the dict also
+    holds q_mean [B,H,nb,d] float32, q_w [B,H,nb,d] int32, q_smoothed [B,H,nb]
+    and q_comp [B,H,nb,N] int32 (w K^^T).
     """
     qf = np.asarray(qf, dtype=np.float32)
     kf = np.asarray(kf, dtype=np.float32)
@@ -164,9 +256,13 @@ def smooth_quant_qk(qf: np.ndarray, kf: np.ndarray, smooth: bool = True):
         mean = np.zeros(kf.shape[:2] + (d,), np.float32)
         ks = kf
     qs = (qf * inv_sqrt_d(d)).astype(np.float32)
-    q_i8, q_scale = quantize_int8_blocks(qs, Q_BLOCK)
     k_i8, k_scale = quantize_int8_blocks(ks, K_BLOCK)
-    return dict(k_mean=mean, q_i8=q_i8, k_i8=k_i8, q_scale=q_scale, k_scale=k_scale)
+    if not smooth_q:
+        q_i8, q_scale = quantize_int8_blocks(qs, Q_BLOCK)
+        return dict(k_mean=mean, q_i8=q_i8, k_i8=k_i8, q_scale=q_scale, k_scale=k_scale)
+    q_i8, q_scale, q_mean, q_w, ok = smooth_quantize_q_blocks(qs)
+    return dict(k_mean=mean, q_i8=q_i8, k_i8=k_i8, q_scale=q_scale, k_scale=k_scale,
+                q_mean=q_mean, q_w=q_w, q_smoothed=ok, q_comp=q_compensation(q_w, k_i8))
 
 
 # ---------------------------------------------------------------------------
@@ -238,7 +334,7 @@ def s_int32_tile(q_i8, k_i8, b, h, q0, nq, k0, nk) -> np.ndarray:
 
 
 def attention(q_op, q_rowscale, k_op, k_keyscale, v_op, v_chanscale, *, causal,
-              p_round, rows=None, record=False, p_flip=False, p_codec="fp8"):
+              p_round, rows=None, record=False, p_flip=False, p_codec="fp8", s_add=None):
     """Tiled attention with an online softmax for one (b, h).
 
     [SA] §3 Algorithm 1 and §4 Eq. 4-5, in float64:
@@ -258,6 +354,8 @@ def attention(q_op, q_rowscale, k_op, k_keyscale, v_op, v_chanscale, *, causal,
 
     q_op [R, d], q_rowscale [R], k_op [N, d], k_keyscale [N], v_op [N, d],
     v_chanscale [d]; rows = the query positions of the R rows (default 0..R-1).
+    s_add: optional [R, N] addend of the product Q_op K_op^T before scaling
+    (the smoothed-Q compensation C of each row's block).
     When `record`, also returns the per-tile P~ row maxima and the final m, l.
 
     p_flip (quantised P~, reading C-s): also return, per output element, a
@@ -287,7 +385,10 @@ def attention(q_op, q_rowscale, k_op, k_keyscale, v_op, v_chanscale, *, causal,
     pmax_tiles = []
     for k0 in range(0, N, KV_TILE):
         k1 = min(k0 + KV_TILE, N)
-        s = (q_op @ k_op[k0:k1].T) * qrs * kks[None, k0:k1]
+        prod = q_op @ k_op[k0:k1].T
+        if s_add is not None:
+            prod = prod + np.asarray(s_add[:, k0:k1], dtype=np.float64)
+        s = prod * qrs * kks[None, k0:k1]
         if causal:
             keys = np.arange(k0, k1)
             s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
@@ -341,7 +442,8 @@ def _p_round_for(pv_mode: str):
 
 
 def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
-                   rows=None, heads=None, record=False, prep=None, p_flip=False):
+                   rows=None, heads=None, record=False, prep=None, p_flip=False,
+                   smooth_q=False):
     """The whole forward pass on float32 inputs [B, H, N, d].
 
     quant="int8": the method.  quant="none": identity quantiser (Q/sqrt(d) and
@@ -350,6 +452,8 @@ def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
     rows: optional query positions to evaluate (same for every head).
     heads: optional list of (b, h) to evaluate; default all.
     prep: optionally a precomputed smooth_quant_qk dict (quant="int8").
+    smooth_q: smooth Q per block (module docstring); the compensation C of
+    each row's block is added to the integer product.
     Returns O float64 [B, H, R, d] (R = N or len(rows)); heads not evaluated
     are left NaN.  With `record`, also a dict of per-head intermediates.
     p_flip (pv_mode "fp8" or "int8", quant "int8", not with `record`): also
@@ -369,20 +473,23 @@ def sage_attention(qf, kf, vf, *, causal, pv_mode, quant="int8", smooth=True,
     flips = np.full(out.shape, np.nan) if p_flip else None
 
     if quant == "int8":
-        pq = prep if prep is not None else smooth_quant_qk(qf, kf, smooth=smooth)
+        pq = prep if prep is not None else smooth_quant_qk(qf, kf, smooth=smooth,
+                                                            smooth_q=smooth_q)
         if pv_mode == "none":
             vvals, vscale = vf.astype(np.float64), None
         else:
             vvals, _, vscale = prep_v(vf, pv_mode)
         for (b, h) in heads:
             q_op = pq["q_i8"][b, h, rows_arr].astype(np.float64)
+            s_add = pq["q_comp"][b, h, rows_arr // Q_BLOCK] if "q_comp" in pq else None
             qrs = pq["q_scale"][b, h, rows_arr // Q_BLOCK]
             k_op = pq["k_i8"][b, h].astype(np.float64)
             kks = pq["k_scale"][b, h, np.arange(N) // K_BLOCK]
             vcs = vscale[b, h].astype(np.float64) if vscale is not None else np.ones(d)
             res = attention(q_op, qrs, k_op, kks, vvals[b, h], vcs, causal=causal,
                             p_round=_p_round_for(pv_mode), rows=rows_arr, record=record,
-                            p_flip=p_flip, p_codec=pv_mode if p_flip else "fp8")
+                            p_flip=p_flip, p_codec=pv_mode if p_flip else "fp8",
+                            s_add=s_add)
             if record:
                 out[b, h], recs[(b, h)] = res
             elif p_flip:

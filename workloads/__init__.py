@@ -171,6 +171,13 @@ def _apply_extras(wl: Workload, rng, q, k, v):
         qch = rng.choice(d, 2, replace=False)
         q[..., qch] *= np.float32(8.0)
         k += (rng.standard_normal((B, H, 1, d), dtype=np.float32) * np.float32(5.0))
+    elif e.startswith("qbias"):
+        # "qbiasA_kbiasB": Q and K each carry a per-channel bias shared by all
+        # tokens, ~ N(0, A^2) and N(0, B^2) (the case that smoothing Q, on top
+        # of smoothing K, is for)
+        qa_, kb_ = e[len("qbias"):].split("_kbias")
+        q += (rng.standard_normal((B, H, 1, d), dtype=np.float32) * np.float32(float(qa_)))
+        k += (rng.standard_normal((B, H, 1, d), dtype=np.float32) * np.float32(float(kb_)))
     elif e == "vout":
         # one V token per (b, h) with value 6e4 in every channel, which queries
         # avoid (a shared query-channel bias against a large negative key
