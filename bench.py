@@ -95,7 +95,7 @@ def cpu_baseline(wl, min_seconds: float):
     while done < 4 and (t_total < min_seconds or done == 0):
         inp = make_inputs(one.with_(seed=wl.seed + 1000 + done))
         t0 = time.perf_counter()
-        pq = oracle.smooth_quant_qk(inp.qf, inp.kf)
+        pq = oracle.smooth_quant_qk(inp.qf, inp.kf, smooth_q=wl.smooth_q)
         oracle.sage_attention(inp.qf, inp.kf, inp.vf, causal=wl.causal, pv_mode=wl.pv_mode,
                               prep=pq)
         t_total += time.perf_counter() - t0
@@ -136,11 +136,12 @@ def main():
         from workloads import rope_tables
         rope = tuple(torch.from_numpy(t).cuda() for t in rope_tables(N, d))
     out = torch.empty_like(q)
-    ws = torch.empty(qa.workspace_bytes(B, H, N, d, wl.pv_mode), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(qa.workspace_bytes(B, H, N, d, wl.pv_mode, wl.smooth_q), dtype=torch.uint8,
+                     device="cuda")
 
     def step():
         qa.sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out=out, workspace=ws,
-                     layout=args.layout, rope=rope)
+                     layout=args.layout, rope=rope, smooth_q=wl.smooth_q)
 
     for _ in range(args.warmup):
         step()
@@ -160,16 +161,24 @@ def main():
     # The attention kernel alone, on prepared operands, on the same stream.
     qk = qa.smooth_quant_qk(q, k, layout=args.layout, rope=rope)
     vp, vs = qa.quant_v(v, wl.pv_mode, layout=args.layout)
+    seed = None
+    if wl.smooth_q:   # smoothed Q^ and the accumulator seeds (HND layout)
+        sq = qa.smooth_q(q, qk["k_i8"], seed_pv_mode=wl.pv_mode)
+        qk = dict(qk, q_i8=sq["q_i8"], q_scale=sq["q_scale"])
+        seed = sq["q_comp"]
     out2 = torch.empty((B, H, N, d), dtype=q.dtype, device="cuda")
-    for _ in range(max(2, args.warmup)):
+
+    def kernel_only():
         qa.sage_attn_quantized(qk, vp, vs, causal=wl.causal, pv_mode=wl.pv_mode,
-                               out_dtype=q.dtype, out=out2)
+                               out_dtype=q.dtype, out=out2, q_seed=seed)
+
+    for _ in range(max(2, args.warmup)):
+        kernel_only()
     torch.cuda.synchronize()
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     k0.record(stream)
     for _ in range(args.steps):
-        qa.sage_attn_quantized(qk, vp, vs, causal=wl.causal, pv_mode=wl.pv_mode,
-                               out_dtype=q.dtype, out=out2)
+        kernel_only()
     k1.record(stream)
     torch.cuda.synchronize()
     kms = k0.elapsed_time(k1) / args.steps
@@ -178,7 +187,8 @@ def main():
     assert torch.equal(o_hnd, out2), "attention-only path must reproduce the full pass"
 
     traffic = traffic_from_profiles(wl.name)
-    mixed_peak = INT8_PEAK_TOPS if wl.pv_mode == "fp8" else \
+    # FP8 and INT8 P~V run at the INT8 MFMA rate; FP16 P~V at half of it
+    mixed_peak = INT8_PEAK_TOPS if wl.pv_mode in ("fp8", "int8") else \
         1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / FP16_PEAK_TFLOPS)
     res = {
         "metric": "attention TOPS at N=16K,d=128 (1 MI355X) and % of INT8 MFMA peak",
@@ -191,14 +201,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8+f16" if wl.pv_mode == "fp16" else "i8+fp8e4m3",
+        "dtype": {"fp16": "i8+f16", "fp8": "i8+fp8e4m3", "int8": "i8"}[wl.pv_mode],
         "data": "synthetic (seeded numpy draws, see workloads/)",
         "config": {"workload": f"{wl.name}: B={B},H={H},N={N},d={d} "
                                f"{'causal' if wl.causal else 'non-causal'} {wl.dtype}, "
-                               f"INT8 QK^T + {wl.pv_mode.upper()} P~V",
+                               f"INT8 QK^T + {wl.pv_mode.upper()} P~V"
+                               f"{', Q smoothed' if wl.smooth_q else ''}",
                    "B": B, "H": H, "N": N, "d": d, "causal": wl.causal,
                    "pv_mode": wl.pv_mode, "in_dtype": wl.dtype, "layout": args.layout,
-                   "rope": bool(args.rope)},
+                   "rope": bool(args.rope), "smooth_q": wl.smooth_q},
         "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
         "roofline": {"kernel": "attn_fwd_kernel", "bound": "mfma",
                      "achieved": round(ktops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",

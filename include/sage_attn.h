@@ -138,6 +138,32 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
                      int layout, const float* rope_cos, const float* rope_sin, int out_f32,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The forward pass with Q smoothed per 128-token block as well as K
+ * (SageAttention2's smoothing of Q: "SageAttention2" abstract page, Q
+ * smoothing improves the quantised QK^T; [SA2pp] 三 smooths Q and K before
+ * quantising).  The pages print no formula; this build's reading, step 2 of
+ * sage_attn_fwd replaced for Q by:
+ *   qbar = the block's token mean of Q' = fp32(Q * fp32(1/sqrt(d))) (float32,
+ *          tokens in order from 0.0f, one IEEE division by their count);
+ *   Q~ = fp32(Q' - qbar), a = max|Q~|, r = fp32(127/a),
+ *   Q~^ = clamp(rne(fp32(Q~ r)), -127, 127), delta_Q = fp32(a/127);
+ *   w = rne(fp32(qbar r) * 2^8) per channel (the mean on a grid 2^8 finer);
+ *   C[t] = rne((w . K^[t]) / 2^8) per block and key (exact integer product,
+ *          ties to even), and step 3 uses S = (Q~^ K^^T + C) delta_Q delta_K.
+ * A block is smoothed only if a > 0 and 127 sum_c |w_c| <= 2^29 (so that
+ * |C| <= 2^21); any other block is quantised as in sage_attn_fwd (w = 0).
+ * Arguments as sage_attn_fwd_ex without RoPE (layout SAGE_LAYOUT_HND or
+ * SAGE_LAYOUT_NHD; out_f32 0/1); the workspace must hold
+ * sage_attn_sq_workspace_bytes(...) bytes (it adds ceil(N/128) * ceil(N/64)
+ * * 64 int32 compensation values per head).
+ */
+size_t sage_attn_sq_workspace_bytes(int B, int H, int N, int d, int pv_mode);
+int sage_attn_fwd_sq(const void* q, const void* k, const void* v, void* o,
+                     int B, int H, int N, int d, int causal, int pv_mode, int dtype,
+                     int layout, int out_f32, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* ---- The stages of the pass, exposed for testing and reuse -------------- */
 
 /* Scratch bytes sage_smooth_quant_qk needs (float32 partial column sums). */
@@ -166,6 +192,24 @@ int sage_smooth_quant_qk_ex(const void* q, const void* k, int dtype, int layout,
                             const float* rope_cos, const float* rope_sin, int B, int H, int N,
                             int d, int8_t* q_i8, int8_t* k_i8, float* q_scale, float* k_scale,
                             float* k_mean, void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * The smoothed-Q stage of sage_attn_fwd_sq on [B,H,N,d] q and the K^ codes of
+ * sage_smooth_quant_qk (k_i8 int8 [B,H,N,d]): q_i8 int8 [B,H,N,d] (Q~^, or the
+ * unsmoothed codes of a block left unsmoothed), q_scale float32
+ * [B,H,ceil(N/128)], q_mean float32 and q_w int32 [B,H,ceil(N/128),d] (qbar
+ * and w; 0 for a block left unsmoothed), and q_comp:
+ *   seed_pv_mode = -1: C itself, int32 [B,H,ceil(N/128),N];
+ *   seed_pv_mode = a SAGE_PV_* mode: the attention kernel's INT32 accumulator
+ *     seeds for that mode, int32 [B,H,ceil(N/128),ceil(N/64)*64] (keys >= N
+ *     get C = 0): C plus the bit pattern of 1.5 * 2^23 (0x4B400000) in
+ *     SAGE_PV_FP16 mode, whose kernel reads the accumulator as a float; C
+ *     itself in the other modes.  Input of sage_attn_fwd_quantized_sq.
+ * q, k_i8, q_i8, q_w, q_comp 16-byte aligned; the others 4-byte aligned.
+ */
+int sage_smooth_q(const void* q, const int8_t* k_i8, int dtype, int B, int H, int N, int d,
+                  int seed_pv_mode, int8_t* q_i8, float* q_scale, float* q_mean, int32_t* q_w,
+                  int32_t* q_comp, void* stream);
 
 /* Bytes of the prepared V (v_out of sage_quant_v) and of its scratch. */
 size_t sage_quant_v_bytes(int B, int H, int N, int d, int pv_mode);
@@ -217,6 +261,15 @@ int sage_attn_fwd_quantized(const int8_t* q_i8, const int8_t* k_i8, const void* 
                             const float* q_scale, const float* k_scale, const float* v_scale,
                             void* o, int B, int H, int N, int d, int causal, int pv_mode,
                             int out_dtype, void* stream);
+
+/* sage_attn_fwd_quantized with Q smoothed per block: q_i8 and q_scale from
+ * sage_smooth_q, q_seed its q_comp for the same pv_mode (16-byte aligned);
+ * the other operands as for sage_attn_fwd_quantized.  Same numerics as
+ * sage_attn_fwd_sq. */
+int sage_attn_fwd_quantized_sq(const int8_t* q_i8, const int8_t* k_i8, const void* v_prep,
+                               const float* q_scale, const float* k_scale, const float* v_scale,
+                               const int32_t* q_seed, void* o, int B, int H, int N, int d,
+                               int causal, int pv_mode, int out_dtype, void* stream);
 
 /*
  * Full-precision reference for selected query rows: float32 softmax

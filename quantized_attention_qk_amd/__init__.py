@@ -5,6 +5,6 @@ Importing this package does not require a GPU; calling into it does, and it
 fails loudly (RuntimeError) when the HIP library is missing or no device is
 visible.  There is no CPU fallback.
 """
-from .api import (debug_s_i32, quant_v, ref_rows, sage_attn, sage_attn_quantized,  # noqa: F401
+from .api import (debug_s_i32, quant_v, ref_rows, sage_attn, sage_attn_quantized, smooth_q,  # noqa: F401
                   smooth_quant_qk, tiling, untile_v, workspace_bytes)
 from .adaptive import choose_mode, load_modes, save_modes, select_pv_modes  # noqa: F401

@@ -38,6 +38,10 @@ _SIGNATURES = {
     "sage_attn_fwd_quantized": (_c_int, [_vp] * 7 + [_c_int] * 7 + [_vp]),
     "sage_attn_ref_rows_f32": (_c_int, [_vp] * 3 + [_c_int] * 6 + [_vp, _c_int, _vp, _vp]),
     "sage_attn_debug_s_i32": (_c_int, [_vp, _vp] + [_c_int] * 10 + [_vp, _vp]),
+    "sage_attn_sq_workspace_bytes": (_c_size, [_c_int] * 5),
+    "sage_attn_fwd_sq": (_c_int, [_vp] * 4 + [_c_int] * 9 + [_vp, _c_size, _vp]),
+    "sage_smooth_q": (_c_int, [_vp, _vp] + [_c_int] * 6 + [_vp] * 5 + [_vp]),
+    "sage_attn_fwd_quantized_sq": (_c_int, [_vp] * 8 + [_c_int] * 7 + [_vp]),
 }
 
 _lib = None

@@ -61,26 +61,33 @@ def tiling(d: int = 128, causal: bool = False, pv_mode: str = "fp16") -> dict:
     return dict(zip(("q_block", "k_block", "kv_tile", "mean_chunk"), (v.value for v in vals)))
 
 
-def workspace_bytes(B: int, H: int, N: int, d: int, pv_mode: str = "fp16") -> int:
+def workspace_bytes(B: int, H: int, N: int, d: int, pv_mode: str = "fp16",
+                    smooth_q: bool = False) -> int:
+    if smooth_q:
+        return int(lib().sage_attn_sq_workspace_bytes(B, H, N, d, SAGE_PV[pv_mode]))
     return int(lib().sage_attn_workspace_bytes(B, H, N, d, SAGE_PV[pv_mode]))
 
 
 def sage_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
               pv_mode: str = "fp16", out: torch.Tensor | None = None,
               workspace: torch.Tensor | None = None, out_f32: bool = False,
-              layout: str = "HND", rope=None) -> torch.Tensor:
+              layout: str = "HND", rope=None, smooth_q: bool = False) -> torch.Tensor:
     """SageAttention forward: O = softmax(Q K^T / sqrt(d)) V with smoothed INT8
     Q K^T and FP16 or FP8 P~V.  q, k, v: contiguous fp16/bf16 tensors, [B, H, N,
     d] (layout "HND") or [B, N, H, d] ("NHD"); O has the same layout.
 
     rope: optional (cos, sin) float32 [N, d/2] device tables; Q and K are then
     rotated (rotate-half form) inside the quantisation prepass.
+    smooth_q: smooth Q per 128-token block as well as K (sage_attn_fwd_sq);
+    not combined with rope.
     Returns O in the input dtype, or float32 when `out_f32`.  `workspace` may
     be a preallocated uint8 device tensor of workspace_bytes(...) bytes.
     """
     B, H, N, d = _check_qkv(q, k, v, layout=layout)
     mode = SAGE_PV[pv_mode]
-    need = workspace_bytes(B, H, N, d, pv_mode)
+    if smooth_q and rope is not None:
+        raise ValueError("smooth_q is not combined with rope")
+    need = workspace_bytes(B, H, N, d, pv_mode, smooth_q)
     if need == 0:
         raise ValueError(f"unsupported shape {(B, H, N, d)}")
     if workspace is None:
@@ -91,7 +98,13 @@ def sage_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     elif out.dtype != odt or out.shape != q.shape or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor of q's shape and the output dtype")
     pc, ps, keep = _rope_ptrs(rope, N, d, q.device)
-    if layout == "HND" and rope is None:
+    if smooth_q:
+        check(lib().sage_attn_fwd_sq(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B,
+                                     H, N, d, int(causal), mode, SAGE_DT[q.dtype],
+                                     SAGE_LAYOUT[layout], int(out_f32), workspace.data_ptr(),
+                                     workspace.numel(), _stream_ptr(q.device)),
+              "sage_attn_fwd_sq")
+    elif layout == "HND" and rope is None:
         fn = lib().sage_attn_fwd_f32out if out_f32 else lib().sage_attn_fwd
         check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
                  int(causal), mode, SAGE_DT[q.dtype], workspace.data_ptr(), workspace.numel(),
@@ -129,6 +142,30 @@ def smooth_quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND", rope=
     return res
 
 
+def smooth_q(q: torch.Tensor, k_i8: torch.Tensor, seed_pv_mode: str | None = None) -> dict:
+    """The smoothed-Q stage (sage_smooth_q) on [B,H,N,d] q and the K^ codes of
+    smooth_quant_qk: q_i8, q_scale, q_mean, q_w and q_comp (C [B,H,nqb,N]; or,
+    with seed_pv_mode, the attention kernel's seeds for that P~V mode,
+    [B,H,nqb,ceil(N/64)*64], the input of sage_attn_quantized's q_seed)."""
+    B, H, N, d = _check_qkv(q)
+    dev = q.device
+    nqb = -(-N // 128)
+    ncomp = N if seed_pv_mode is None else -(-N // 64) * 64
+    res = dict(q_i8=torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
+               q_scale=torch.empty((B, H, nqb), dtype=torch.float32, device=dev),
+               q_mean=torch.empty((B, H, nqb, d), dtype=torch.float32, device=dev),
+               q_w=torch.empty((B, H, nqb, d), dtype=torch.int32, device=dev),
+               q_comp=torch.empty((B, H, nqb, ncomp), dtype=torch.int32, device=dev))
+    if tuple(k_i8.shape) != (B, H, N, d) or k_i8.dtype != torch.int8 or not k_i8.is_contiguous():
+        raise ValueError("k_i8 must be a contiguous int8 tensor of q's shape")
+    check(lib().sage_smooth_q(q.data_ptr(), k_i8.data_ptr(), SAGE_DT[q.dtype], B, H, N, d,
+                              -1 if seed_pv_mode is None else SAGE_PV[seed_pv_mode],
+                              res["q_i8"].data_ptr(), res["q_scale"].data_ptr(),
+                              res["q_mean"].data_ptr(), res["q_w"].data_ptr(),
+                              res["q_comp"].data_ptr(), _stream_ptr(dev)), "sage_smooth_q")
+    return res
+
+
 def quant_v(v: torch.Tensor, pv_mode: str = "fp16", layout: str = "HND"):
     """Prepare V for P~V: (tiled uint8 tensor, per-channel scale or None)."""
     B, H, N, d = _check_qkv(v, layout=layout)
@@ -150,16 +187,27 @@ def quant_v(v: torch.Tensor, pv_mode: str = "fp16", layout: str = "HND"):
 def sage_attn_quantized(qk: dict, v_prep: torch.Tensor, v_scale: torch.Tensor | None,
                         causal: bool = False, pv_mode: str = "fp16",
                         out_dtype: torch.dtype = torch.bfloat16,
-                        out: torch.Tensor | None = None) -> torch.Tensor:
-    """The attention kernel alone, on the outputs of smooth_quant_qk/quant_v."""
+                        out: torch.Tensor | None = None,
+                        q_seed: torch.Tensor | None = None) -> torch.Tensor:
+    """The attention kernel alone, on the outputs of smooth_quant_qk/quant_v
+    (with Q smoothed: q_i8, q_scale from smooth_q and q_seed = its q_comp
+    for the same pv_mode)."""
     q_i8 = qk["q_i8"]
     B, H, N, d = q_i8.shape
     odt = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}[out_dtype]
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
+    vsp = v_scale.data_ptr() if v_scale is not None else None
+    if q_seed is not None:
+        check(lib().sage_attn_fwd_quantized_sq(
+            q_i8.data_ptr(), qk["k_i8"].data_ptr(), v_prep.data_ptr(), qk["q_scale"].data_ptr(),
+            qk["k_scale"].data_ptr(), vsp, q_seed.data_ptr(), out.data_ptr(), B, H, N, d,
+            int(causal), SAGE_PV[pv_mode], odt, _stream_ptr(q_i8.device)),
+            "sage_attn_fwd_quantized_sq")
+        return out
     check(lib().sage_attn_fwd_quantized(
         q_i8.data_ptr(), qk["k_i8"].data_ptr(), v_prep.data_ptr(), qk["q_scale"].data_ptr(),
-        qk["k_scale"].data_ptr(), v_scale.data_ptr() if v_scale is not None else None,
+        qk["k_scale"].data_ptr(), vsp,
         out.data_ptr(), B, H, N, d, int(causal), SAGE_PV[pv_mode], odt,
         _stream_ptr(q_i8.device)), "sage_attn_fwd_quantized")
     return out

@@ -30,6 +30,7 @@ SOURCES = {
     # prepass decisions must be reproducible bit for bit: no FP contraction
     "prepass.hip": ["-ffp-contract=off"],
     "attn_fwd.hip": ["-ffp-contract=off"],
+    "smooth_q.hip": ["-ffp-contract=off"],
     "ref_rows.hip": [],
     "sage_api.cpp": [],
 }

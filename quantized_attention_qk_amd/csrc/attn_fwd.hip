@@ -42,6 +42,9 @@
 //   the row sum checks them (a rare recompute otherwise).
 // * The output rescale by alpha is skipped when no row of the wavefront has a
 //   new maximum (alpha == 1 exactly), which is bit-identical.
+// * With Q smoothed per block (SQ, see smooth_q.hip), each K^ tile carries the
+//   block's 64 compensation values C (INT32, 256 bytes) in its LDS slot, and
+//   the INT32 accumulation of S starts from them instead of from a constant.
 #include <type_traits>
 #include <utility>
 
@@ -262,12 +265,29 @@ __device__ __forceinline__ uint32_t pack_u8x4(float a, float b, float c, float d
   return __builtin_amdgcn_cvt_pk_u8_f32(d, 3u, w);
 }
 
-// S^T = K^ Q^T for one 64-key tile: two 32x32 INT32 blocks.
+// Smoothed Q: the compensation values of a tile follow its K^ in the LDS
+// slot (64 INT32, already carrying FP16 mode's magic bias).  The start value
+// of 32-key block blk in the accumulator layout: register r holds key
+// 32 blk + 8 (r/4) + 4 hh + r%4.
+constexpr int kSqTileBytes = kKvTile * 4;
 template <int D>
+__device__ __forceinline__ v16i sq_init(const uint8_t* kb, int blk, int hh) {
+  const int32_t* c = reinterpret_cast<const int32_t*>(kb + KTile<D>::BYTES) + 32 * blk + 4 * hh;
+  v16i r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const v4i x = *reinterpret_cast<const v4i*>(c + 8 * j);
+    r[4 * j] = x[0]; r[4 * j + 1] = x[1]; r[4 * j + 2] = x[2]; r[4 * j + 3] = x[3];
+  }
+  return r;
+}
+
+// S^T = K^ Q^T for one 64-key tile: two 32x32 INT32 blocks.
+template <int D, bool SQ>
 __device__ __forceinline__ void qk_tile(v16i (&s)[2], const v4i (&qf)[D / 32], const uint8_t* kb,
                                         int n, int hh, const v16i& init) {
-  s[0] = qk_block<D>(qf, kb, 0, n, hh, init);
-  s[1] = qk_block<D>(qf, kb, 1, n, hh, init);
+  s[0] = qk_block<D>(qf, kb, 0, n, hh, SQ ? sq_init<D>(kb, 0, hh) : init);
+  s[1] = qk_block<D>(qf, kb, 1, n, hh, SQ ? sq_init<D>(kb, 1, hh) : init);
 }
 
 // FP16 mode converts scores to float without an instruction: the INT32
@@ -551,7 +571,7 @@ struct StepPlan {
 template <int D, int PV>
 using OpReg = std::conditional_t<PV == kPvFp16, v4i, v8i>;
 
-template <int D, int PV>
+template <int D, int PV, bool SQ>
 __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D / 32],
                                             v16i (&s_cur)[2], v16i (&s_new)[2],
                                             const PTile<PV>& p_cur, PTile<PV>& p_new,
@@ -563,6 +583,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
   using Op = OpReg<D, PV>;
   constexpr int LA = 2;   // operand read lookahead (slots)
   Op ops[LA + 1];
+  v16i cin[2];            // SQ: start values of the two 32-key blocks of S(j+2)
 
   // ---- MFMA side
   auto read_op = [&]<int K>() __attribute__((always_inline)) {
@@ -573,6 +594,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
       const v4i a = *reinterpret_cast<const v4i*>(kb + KTile<D>::lds_off(32 * blk + n, 2 * t + hh));
       if constexpr (PV == kPvFp16) r = a;
       else r = Op{a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+      if constexpr (SQ && t == 0) cin[blk] = sq_init<D>(kb, blk, hh);
     } else if constexpr (PV == kPvFp16) {
       constexpr int S = i / Plan::NCB, cb = i % Plan::NCB;
       const int row = 32 * cb + n;
@@ -595,8 +617,8 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
       v4i a;
       if constexpr (PV == kPvFp16) a = r;
       else a = v4i{r[0], r[1], r[2], r[3]};
-      s_new[blk] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[t], t == 0 ? init : s_new[blk],
-                                                          0, 0, 0);
+      s_new[blk] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+          a, qf[t], t == 0 ? (SQ ? cin[blk] : init) : s_new[blk], 0, 0, 0);
     } else if constexpr (PV == kPvFp16) {
       constexpr int S = i / Plan::NCB, cb = i % Plan::NCB;
       o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, r),
@@ -710,7 +732,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
     if (__builtin_amdgcn_ballot_w64(!(lsum - l_run <= kOptimisticSum))) {
       // rare: recompute the tile's scores (into the registers they came in,
       // free by now) and take the max-based rule
-      qk_tile<D>(s_cur, qf, kb_prev, n, hh, init);
+      qk_tile<D, SQ>(s_cur, qf, kb_prev, n, hh, init);
       rescale<D>(o, softmax_tile<PV, false, false>(s_cur, m_run, l_run, p_new, ts, grid, 0, 0,
                                                    0, hh));
     } else {
@@ -733,14 +755,15 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
 // one barrier per step).  All wavefronts run every step of the workgroup; a
 // causal tile beyond a wavefront's last row is fully masked and changes
 // nothing.
-template <int D, int PV, int OUT, bool CAUSAL>
+template <int D, int PV, int OUT, bool CAUSAL, bool SQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__ k_i8,
                      const uint8_t* __restrict__ v_t, const float* __restrict__ q_scale,
                      const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-                     int BH, int N, int nqb, int ntiles, int xcd_remap, int H, int nhd,
-                     void* __restrict__ out) {
-  constexpr int KB = KTile<D>::BYTES;
+                     const int32_t* __restrict__ comp, int BH, int N, int nqb, int ntiles,
+                     int xcd_remap, int H, int nhd, void* __restrict__ out) {
+  // K^ slot: the tile, then (SQ) its 64 compensation values
+  constexpr int KB = KTile<D>::BYTES + (SQ ? kSqTileBytes : 0);
   constexpr int VB = VTile<D, PV>::BYTES;
   constexpr int NCB = D / 32;   // 32-channel blocks of the output
   constexpr int NKS = kKSlots<PV>;
@@ -808,6 +831,22 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   using VL = VLoader<D, PV, kWaves>;
   const v4i krs = buffer_rsrc(k_bh, N * D);
   const v4i vrs = buffer_rsrc(v_bh, ntiles * VB);
+  // SQ: this block's row of compensation values, ntiles * 64 INT32
+  v4i crs = {0, 0, 0, 0};
+  if constexpr (SQ) crs = buffer_rsrc(comp + ((size_t)bh * nqb + qb) * ntiles * kKvTile,
+                                      ntiles * kSqTileBytes);
+  // K^ tile `tile` into the slot at LDS address `dst`, with (SQ) its
+  // compensation values behind it (wavefront 0, lanes 0..15, 16 bytes each)
+  auto issue_k = [&]<bool CLAMP>(int tile, uint32_t dst) __attribute__((always_inline)) {
+    kld.template issue<CLAMP>(krs, tile * kKvTile, N, dst, wave);
+    if constexpr (SQ) {
+      if (wave == 0 && lane < 16) {
+        const uint32_t m0[1] = {dst + KTile<D>::BYTES};
+        const int vo[1] = {lane * 16};
+        lds_copy_x4<1>(crs, tile * kSqTileBytes, m0, vo);
+      }
+    }
+  };
   // K^ tile t lives in slot t % NKS (tile indices here are wavefront-uniform;
   // with two slots and an even j, the slot of tile j + u + c is (u + c) & 1)
   auto kslot = [&](int t, int u_plus_c) __attribute__((always_inline)) {
@@ -835,16 +874,16 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   };
 
   // Prologue: S(0), S(1), P~(0); then K^(2) into the slot of K^(0).
-  kld.template issue<true>(krs, 0, N, kl0, wave);
+  issue_k.template operator()<true>(0, kl0);
   VL::issue(vrs, 0, vl[0], wave, lane);
-  if (nt > 1) kld.template issue<true>(krs, kKvTile, N, kl0 + KB, wave);
+  if (nt > 1) issue_k.template operator()<true>(1, kl0 + KB);
   wait_lds_loads();
   __syncthreads();
-  qk_tile<D>(sA, qf, kbuf[0], n, hh, init);
-  if (nt > 1) qk_tile<D>(sB, qf, kbuf[1], n, hh, init);
+  qk_tile<D, SQ>(sA, qf, kbuf[0], n, hh, init);
+  if (nt > 1) qk_tile<D, SQ>(sB, qf, kbuf[1], n, hh, init);
   softmax_any(sA, pA, 0);   // alpha irrelevant: O is still zero
   __syncthreads();          // every wave has read K^(0)
-  if (nt > 2) kld.template issue<true>(krs, 2 * kKvTile, N, kl0 + kslot(2, 2) * KB, wave);
+  if (nt > 2) issue_k.template operator()<true>(2, kl0 + kslot(2, 2) * KB);
   wait_lds_loads();
   __syncthreads();
 
@@ -858,7 +897,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   // the end of the step instead, where no LDS read is outstanding.
   float dk_next = ks_bh[min(1, ntiles - 1)];
   auto steady = [&]<int U>(int jj, int sw, int sr, int sp) __attribute__((always_inline)) {
-    kld.template issue<false>(krs, (jj + 3) * kKvTile, N, kl0 + sw * KB, wave);
+    issue_k.template operator()<false>(jj + 3, kl0 + sw * KB);
     VL::issue(vrs, jj + 1, vl[1 - (U & 1)], wave, lane);
     v16i(&s_cur)[2] = (U & 1) == 0 ? sB : sA;
     v16i(&s_new)[2] = (U & 1) == 0 ? sA : sB;
@@ -868,8 +907,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     dk_next = ks_bh[jj + 2];   // jj + 2 < nt: in range
     // FP16: keep the accumulator start value resident (not rebuilt every
     // step); in FP8 mode it is zero, an inline constant
-    if constexpr (PV == kPvFp16) asm volatile("" : "+v"(init));
-    fused_step<D, PV>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[sr], kbuf[sp], vbuf[U & 1], m_run,
+    if constexpr (PV == kPvFp16 && !SQ) asm volatile("" : "+v"(init));
+    fused_step<D, PV, SQ>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[sr], kbuf[sp], vbuf[U & 1], m_run,
                       l_run, tile_scale<PV>(cq, dk), grid, init, n, hh);
     asm volatile("" ::"s"(dk_next));
     wait_lds_loads();
@@ -899,7 +938,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     // source order (P^ V^(jj), S(jj+2), softmax(S(jj+1))), the rescale of each
     // tile folded into the next tile's product
     auto plain = [&]<int U>(int jj) __attribute__((always_inline)) {
-      kld.template issue<false>(krs, (jj + 3) * kKvTile, N, kl0 + ((U + 3) & 1) * KB, wave);
+      issue_k.template operator()<false>(jj + 3, kl0 + ((U + 3) & 1) * KB);
       VL::issue(vrs, jj + 1, vl[1 - U], wave, lane);
       v16i(&s_cur)[2] = U == 0 ? sB : sA;
       v16i(&s_new)[2] = U == 0 ? sA : sB;
@@ -910,7 +949,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
       pv_tile<D, PV>(o, p_cur, vbuf[U], n, hh, alpha_pend);
       alpha_pend = softmax_tile<PV, CAUSAL, false>(s_cur, m_run, l_run, p_new,
                                                    tile_scale<PV>(cq, dk), grid, 0, N, 0, hh);
-      qk_tile<D>(s_new, qf, kbuf[U], n, hh, init);
+      qk_tile<D, SQ>(s_new, qf, kbuf[U], n, hh, init);
       asm volatile("" ::"s"(dk_next));
       wait_lds_loads();
       __syncthreads();
@@ -927,8 +966,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
       const int jj = j + u;
       if (jj < nt) {
         if (jj + 3 < nt)
-          kld.template issue<true>(krs, (jj + 3) * kKvTile, N, kl0 + kslot(jj + 3, u + 3) * KB,
-                                   wave);
+          issue_k.template operator()<true>(jj + 3, kl0 + kslot(jj + 3, u + 3) * KB);
         if (jj + 1 < nt) VL::issue(vrs, jj + 1, vl[1 - u], wave, lane);
         v16i(&s_cur)[2] = u == 0 ? sB : sA;
         v16i(&s_new)[2] = u == 0 ? sA : sB;
@@ -939,9 +977,9 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
           // never live at once (the INT32 product needs the registers)
           pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh, alpha_pend);
           if (jj + 1 < nt) alpha_pend = softmax_any(s_cur, p_new, jj + 1);
-          if (jj + 2 < nt) qk_tile<D>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init);
+          if (jj + 2 < nt) qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init);
         } else {
-          if (jj + 2 < nt) qk_tile<D>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init);
+          if (jj + 2 < nt) qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init);
           pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh, alpha_pend);
           if (jj + 1 < nt) rescale<D>(o, softmax_any(s_cur, p_new, jj + 1));
         }
@@ -1010,41 +1048,45 @@ __global__ __launch_bounds__(64) void debug_s_kernel(const int8_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-template <int D, int PV, int OUT, bool CAUSAL>
+template <int D, int PV, int OUT, bool CAUSAL, bool SQ>
 static hipError_t attn_dispatch(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
                                 const float* q_scale, const float* k_scale,
-                                const float* v_scale, int B, int H, int N, int nhd, void* out,
-                                hipStream_t s) {
+                                const float* v_scale, const int32_t* comp, int B, int H, int N,
+                                int nhd, void* out, hipStream_t s) {
   const int nqb = ceil_div(N, kBlockQ);
   const int ntiles = ceil_div(N, kKvTile);
   const int BH = B * H;
   const long long grid = (long long)BH * nqb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  attn_fwd_kernel<D, PV, OUT, CAUSAL><<<dim3((unsigned)grid), 256, 0, s>>>(
-      q_i8, k_i8, v_t, q_scale, k_scale, v_scale, BH, N, nqb, ntiles, CAUSAL ? 0 : 1, H, nhd,
-      out);
+  attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ><<<dim3((unsigned)grid), 256, 0, s>>>(
+      q_i8, k_i8, v_t, q_scale, k_scale, v_scale, comp, BH, N, nqb, ntiles, CAUSAL ? 0 : 1, H,
+      nhd, out);
   return hipGetLastError();
 }
 
 template <int D, int PV, int OUT>
 static hipError_t attn_dispatch_c(int causal, const int8_t* q_i8, const int8_t* k_i8,
                                   const uint8_t* v_t, const float* q_scale, const float* k_scale,
-                                  const float* v_scale, int B, int H, int N, int nhd, void* out,
-                                  hipStream_t s) {
-  return causal ? attn_dispatch<D, PV, OUT, true>(q_i8, k_i8, v_t, q_scale, k_scale, v_scale, B,
-                                                  H, N, nhd, out, s)
-                : attn_dispatch<D, PV, OUT, false>(q_i8, k_i8, v_t, q_scale, k_scale, v_scale,
-                                                   B, H, N, nhd, out, s);
+                                  const float* v_scale, const int32_t* comp, int B, int H, int N,
+                                  int nhd, void* out, hipStream_t s) {
+#define SAGE_DISPATCH(C, SQ)                                                                   \
+  return attn_dispatch<D, PV, OUT, C, SQ>(q_i8, k_i8, v_t, q_scale, k_scale, v_scale, comp, B, \
+                                          H, N, nhd, out, s);
+  if (comp) {
+    if (causal) { SAGE_DISPATCH(true, true) } else { SAGE_DISPATCH(false, true) }
+  }
+  if (causal) { SAGE_DISPATCH(true, false) } else { SAGE_DISPATCH(false, false) }
+#undef SAGE_DISPATCH
 }
 
 hipError_t launch_attn(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
-                       const float* q_scale, const float* k_scale, const float* v_scale, int B,
-                       int H, int N, int d, int causal, int pv_mode, int out_kind, int nhd,
-                       void* out, hipStream_t s) {
+                       const float* q_scale, const float* k_scale, const float* v_scale,
+                       const int32_t* comp, int B, int H, int N, int d, int causal, int pv_mode,
+                       int out_kind, int nhd, void* out, hipStream_t s) {
 #define SAGE_ATTN_CASE(D, PV, OUT)                                                          \
   if (d == D && pv_mode == PV && out_kind == OUT)                                          \
     return attn_dispatch_c<D, PV, OUT>(causal, q_i8, k_i8, v_t, q_scale, k_scale, v_scale, \
-                                       B, H, N, nhd, out, s);
+                                       comp, B, H, N, nhd, out, s);
   SAGE_ATTN_CASE(64, 0, 0) SAGE_ATTN_CASE(64, 0, 1) SAGE_ATTN_CASE(64, 0, 2)
   SAGE_ATTN_CASE(64, 1, 0) SAGE_ATTN_CASE(64, 1, 1) SAGE_ATTN_CASE(64, 1, 2)
   SAGE_ATTN_CASE(64, 2, 0) SAGE_ATTN_CASE(64, 2, 1) SAGE_ATTN_CASE(64, 2, 2)

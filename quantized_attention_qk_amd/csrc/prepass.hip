@@ -17,15 +17,6 @@
 namespace sage {
 
 // ---------------------------------------------------------------------------
-// Element offset of token t of head bh = b*H + h in a [B,H,N,d] tensor
-// (nhd = 0) or a token-major [B,N,H,d] tensor (nhd = 1).
-template <int D>
-__device__ __forceinline__ size_t row_off(int bh, int t, int H, int N, int nhd) {
-  if (!nhd) return ((size_t)bh * N + t) * D;
-  const int b = bh / H, h = bh - b * H;
-  return (((size_t)b * N + t) * H + h) * D;
-}
-
 // Rotate-half RoPE of one channel pair (x_i, x_{i+d/2}) with c = cos, s = sin:
 // (x_i c - x_{i+d/2} s, x_{i+d/2} c + x_i s), every product and sum rounded
 // to float32 (this file is compiled without FP contraction).

@@ -32,12 +32,14 @@ bool shape_ok(int B, int H, int N, int d) {
   return true;
 }
 
-// Workspace carve-up of sage_attn_fwd (private layout).
+// Workspace carve-up of sage_attn_fwd (private layout); with smoothed Q also
+// the block means, the integer means w and the compensation values.
 struct Layout {
-  size_t q_i8, k_i8, v_t, q_scale, k_scale, k_mean, v_scale, v_recip, part_sum, part_max, total;
+  size_t q_i8, k_i8, v_t, q_scale, k_scale, k_mean, v_scale, v_recip, part_sum, part_max;
+  size_t q_mean, q_w, comp, total;
 };
 
-Layout make_layout(int B, int H, int N, int d, int pv_mode) {
+Layout make_layout(int B, int H, int N, int d, int pv_mode, bool sq = false) {
   const size_t bh = (size_t)B * H;
   const size_t nqb = ceil_div(N, sage::kQBlock), nkb = ceil_div(N, sage::kKBlock);
   const size_t nt = ceil_div(N, sage::kKvTile), nch = ceil_div(N, sage::kMeanChunk);
@@ -54,6 +56,9 @@ Layout make_layout(int B, int H, int N, int d, int pv_mode) {
   L.v_recip = take(bh * d * 4);
   L.part_sum = take(bh * nch * d * 4);
   L.part_max = take(sage::v_quantised(pv_mode) ? bh * nch * d * 4 : 0);
+  L.q_mean = take(sq ? bh * nqb * d * 4 : 0);
+  L.q_w = take(sq ? bh * nqb * d * 4 : 0);
+  L.comp = take(sq ? bh * nqb * nt * sage::kKvTile * 4 : 0);
   L.total = off;
   return L;
 }
@@ -81,6 +86,13 @@ int device_check() {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
 
+// The attention kernel alone on prepared operands (q_seed: null, or the
+// smoothed-Q accumulator seeds); defined with the stage entry points.
+int fwd_quantized(const int8_t* q_i8, const int8_t* k_i8, const void* v_prep,
+                  const float* q_scale, const float* k_scale, const float* v_scale,
+                  const int32_t* q_seed, void* o, int B, int H, int N, int d, int causal,
+                  int pv_mode, int out_dtype, void* stream);
+
 // Layout flag and RoPE tables: both tables or neither, 16-byte aligned.
 int validate_in(int layout, const float* rope_cos, const float* rope_sin) {
   if (layout != SAGE_LAYOUT_HND && layout != SAGE_LAYOUT_NHD) return SAGE_ERR_INVALID_ARG;
@@ -90,7 +102,8 @@ int validate_in(int layout, const float* rope_cos, const float* rope_sin) {
 }
 
 int validate_fwd(const void* q, const void* k, const void* v, const void* o, int B, int H, int N,
-                 int d, int causal, int pv_mode, int dtype, const void* ws, size_t ws_bytes) {
+                 int d, int causal, int pv_mode, int dtype, const void* ws, size_t ws_bytes,
+                 bool sq = false) {
   if (!q || !k || !v || !o || !ws) return SAGE_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SAGE_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return SAGE_ERR_INVALID_ARG;
@@ -101,7 +114,7 @@ int validate_fwd(const void* q, const void* k, const void* v, const void* o, int
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
   if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
   if (o == q || o == k || o == v) return SAGE_ERR_INVALID_ARG;
-  if (ws_bytes < make_layout(B, H, N, d, pv_mode).total) return SAGE_ERR_WORKSPACE;
+  if (ws_bytes < make_layout(B, H, N, d, pv_mode, sq).total) return SAGE_ERR_WORKSPACE;
   return SAGE_OK;
 }
 
@@ -138,8 +151,49 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, 
     e = sage::launch_prep_v(v, F(L.v_recip), dtype, B, H, N, d, pv_mode, layout, v_t, s);
     if (e != hipSuccess) return SAGE_ERR_HIP;
   }
-  e = sage::launch_attn(q_i8, k_i8, v_t, F(L.q_scale), F(L.k_scale), F(L.v_scale), B, H, N, d,
-                        causal, pv_mode, out_kind, layout, o, s);
+  e = sage::launch_attn(q_i8, k_i8, v_t, F(L.q_scale), F(L.k_scale), F(L.v_scale), nullptr, B,
+                        H, N, d, causal, pv_mode, out_kind, layout, o, s);
+  return hip_status(e);
+}
+
+// The pass with Q smoothed per block: K statistics and K^, V, then the
+// smoothed Q^ with its integer means, the compensation values (with FP16
+// mode's accumulator bias), and the attention kernel seeded with them.
+int run_fwd_sq(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+               int causal, int pv_mode, int dtype, int layout, void* ws, size_t ws_bytes,
+               void* stream, int out_kind) {
+  int st = validate_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, ws, ws_bytes, true);
+  if (st != SAGE_OK) return st;
+  if ((st = validate_in(layout, nullptr, nullptr)) != SAGE_OK) return st;
+  const sage::InLayout in{layout, nullptr, nullptr};
+  if ((st = device_check()) != SAGE_OK) return st;
+  const Layout L = make_layout(B, H, N, d, pv_mode, true);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+  int8_t* q_i8 = reinterpret_cast<int8_t*>(w + L.q_i8);
+  int8_t* k_i8 = reinterpret_cast<int8_t*>(w + L.k_i8);
+  int32_t* q_w = reinterpret_cast<int32_t*>(w + L.q_w);
+  int32_t* comp = reinterpret_cast<int32_t*>(w + L.comp);
+  uint8_t* v_t = w + L.v_t;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool qv = sage::v_quantised(pv_mode);
+  hipError_t e = sage::launch_colstats(k, qv ? v : nullptr, dtype, B, H, N, d, pv_mode, in,
+                                       F(L.part_sum), qv ? F(L.part_max) : nullptr, F(L.k_mean),
+                                       F(L.v_scale), F(L.v_recip), s);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_quant_qk(nullptr, k, F(L.k_mean), dtype, B, H, N, d, in, nullptr, k_i8,
+                            nullptr, F(L.k_scale), s);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_prep_v(v, F(L.v_recip), dtype, B, H, N, d, pv_mode, layout, v_t, s);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_smooth_q(q, dtype, B, H, N, d, layout, q_i8, F(L.q_scale), F(L.q_mean), q_w,
+                            s);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_sq_comp(k_i8, q_w, B, H, N, d, ceil_div(N, sage::kKvTile) * sage::kKvTile,
+                           pv_mode == SAGE_PV_FP16 ? sage::kSqBiasFp16 : 0, comp, s);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_attn(q_i8, k_i8, v_t, F(L.q_scale), F(L.k_scale), F(L.v_scale), comp, B, H,
+                        N, d, causal, pv_mode, out_kind, layout, o, s);
   return hip_status(e);
 }
 
@@ -199,6 +253,52 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B
   return run_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, layout, rope_cos, rope_sin,
                  workspace, workspace_bytes, stream,
                  out_f32 ? 2 : (dtype == SAGE_DT_BF16 ? 1 : 0));
+}
+
+size_t sage_attn_sq_workspace_bytes(int B, int H, int N, int d, int pv_mode) {
+  if (!shape_ok(B, H, N, d)) return 0;
+  if (!sage::pv_valid(pv_mode)) return 0;
+  return make_layout(B, H, N, d, pv_mode, true).total;
+}
+
+int sage_attn_fwd_sq(const void* q, const void* k, const void* v, void* o, int B, int H, int N,
+                     int d, int causal, int pv_mode, int dtype, int layout, int out_f32,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (out_f32 != 0 && out_f32 != 1) return SAGE_ERR_INVALID_ARG;
+  return run_fwd_sq(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, layout, workspace,
+                    workspace_bytes, stream, out_f32 ? 2 : (dtype == SAGE_DT_BF16 ? 1 : 0));
+}
+
+int sage_smooth_q(const void* q, const int8_t* k_i8, int dtype, int B, int H, int N, int d,
+                  int seed_pv_mode, int8_t* q_i8, float* q_scale, float* q_mean, int32_t* q_w,
+                  int32_t* q_comp, void* stream) {
+  if (!q || !k_i8 || !q_i8 || !q_scale || !q_mean || !q_w || !q_comp) return SAGE_ERR_INVALID_ARG;
+  if (seed_pv_mode != -1 && !sage::pv_valid(seed_pv_mode)) return SAGE_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_i8) || !aligned16(q_i8) || !aligned16(q_w) ||
+      (reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(q_mean) & 3u) ||
+      (reinterpret_cast<uintptr_t>(q_comp) & 3u))
+    return SAGE_ERR_INVALID_ARG;
+  if (dtype != SAGE_DT_F16 && dtype != SAGE_DT_BF16) return SAGE_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
+  if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
+  int st = device_check();
+  if (st != SAGE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = sage::launch_smooth_q(q, dtype, B, H, N, d, SAGE_LAYOUT_HND, q_i8, q_scale,
+                                       q_mean, q_w, s);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  const int ld = seed_pv_mode < 0 ? N : ceil_div(N, sage::kKvTile) * sage::kKvTile;
+  const int bias = seed_pv_mode == SAGE_PV_FP16 ? sage::kSqBiasFp16 : 0;
+  return hip_status(sage::launch_sq_comp(k_i8, q_w, B, H, N, d, ld, bias, q_comp, s));
+}
+
+int sage_attn_fwd_quantized_sq(const int8_t* q_i8, const int8_t* k_i8, const void* v_prep,
+                               const float* q_scale, const float* k_scale, const float* v_scale,
+                               const int32_t* q_seed, void* o, int B, int H, int N, int d,
+                               int causal, int pv_mode, int out_dtype, void* stream) {
+  if (!q_seed || (reinterpret_cast<uintptr_t>(q_seed) & 15u)) return SAGE_ERR_INVALID_ARG;
+  return fwd_quantized(q_i8, k_i8, v_prep, q_scale, k_scale, v_scale, q_seed, o, B, H, N, d,
+                       causal, pv_mode, out_dtype, stream);
 }
 
 size_t sage_smooth_quant_qk_scratch_bytes(int B, int H, int N, int d) {
@@ -312,6 +412,18 @@ int sage_attn_fwd_quantized(const int8_t* q_i8, const int8_t* k_i8, const void* 
                             const float* q_scale, const float* k_scale, const float* v_scale,
                             void* o, int B, int H, int N, int d, int causal, int pv_mode,
                             int out_dtype, void* stream) {
+  return fwd_quantized(q_i8, k_i8, v_prep, q_scale, k_scale, v_scale, nullptr, o, B, H, N, d,
+                       causal, pv_mode, out_dtype, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int fwd_quantized(const int8_t* q_i8, const int8_t* k_i8, const void* v_prep,
+                  const float* q_scale, const float* k_scale, const float* v_scale,
+                  const int32_t* q_seed, void* o, int B, int H, int N, int d, int causal,
+                  int pv_mode, int out_dtype, void* stream) {
   if (!q_i8 || !k_i8 || !v_prep || !q_scale || !k_scale || !o) return SAGE_ERR_INVALID_ARG;
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_prep) || !aligned16(o) ||
       (reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u))
@@ -327,9 +439,14 @@ int sage_attn_fwd_quantized(const int8_t* q_i8, const int8_t* k_i8, const void* 
   int st = device_check();
   if (st != SAGE_OK) return st;
   return hip_status(sage::launch_attn(q_i8, k_i8, static_cast<const uint8_t*>(v_prep), q_scale,
-                                      k_scale, v_scale, B, H, N, d, causal, pv_mode, out_dtype,
-                                      SAGE_LAYOUT_HND, o, static_cast<hipStream_t>(stream)));
+                                      k_scale, v_scale, q_seed, B, H, N, d, causal, pv_mode,
+                                      out_dtype, SAGE_LAYOUT_HND, o,
+                                      static_cast<hipStream_t>(stream)));
 }
+
+}  // namespace
+
+extern "C" {
 
 int sage_attn_ref_rows_f32(const void* q, const void* k, const void* v, int dtype, int B, int H,
                            int N, int d, int causal, const int32_t* rows, int nrows, float* o,

@@ -31,6 +31,15 @@ __device__ __forceinline__ float in_to_f32(uint16_t b) {
   return DT == 0 ? f16_bits_to_f32(b) : bf16_bits_to_f32(b);
 }
 
+// Element offset of token t of head bh = b*H + h in a [B,H,N,d] tensor
+// (nhd = 0) or a token-major [B,N,H,d] tensor (nhd = 1).
+template <int D>
+__device__ __forceinline__ size_t row_off(int bh, int t, int H, int N, int nhd) {
+  if (!nhd) return ((size_t)bh * N + t) * D;
+  const int b = bh / H, h = bh - b * H;
+  return (((size_t)b * N + t) * H + h) * D;
+}
+
 // Two floats -> packed fp16 pair (v_cvt_pk_f16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   v2f x = {a, b};

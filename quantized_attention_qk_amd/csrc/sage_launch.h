@@ -83,11 +83,26 @@ hipError_t launch_prepass_head(const void* q, const void* k, const void* v, int 
                                const PrepassOut& o, hipStream_t s);
 
 // Attention kernel.  out_kind: 0 = fp16, 1 = bf16, 2 = float32; nhd: o is
-// token-major [B,N,H,d] instead of [B,H,N,d].
+// token-major [B,N,H,d] instead of [B,H,N,d].  comp: null, or (Q smoothed per
+// block) the compensation values int32 [B*H, ceil(N/128), ceil(N/64)*64],
+// with FP16 mode's magic bias (kSqBiasFp16) already added in FP16 mode.
 hipError_t launch_attn(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
-                       const float* q_scale, const float* k_scale, const float* v_scale, int B,
-                       int H, int N, int d, int causal, int pv_mode, int out_kind, int nhd,
-                       void* out, hipStream_t s);
+                       const float* q_scale, const float* k_scale, const float* v_scale,
+                       const int32_t* comp, int B, int H, int N, int d, int causal, int pv_mode,
+                       int out_kind, int nhd, void* out, hipStream_t s);
+
+// Smoothed Q (smooth_q.hip): per 128-token block the mean qbar is removed
+// before quantisation (q_i8, q_scale as for plain Q; q_mean float32 and q_w
+// int32 [B*H, ceil(N/128), d]); the compensation C = rne((w . K^) / 2^8) + bias
+// is written as int32 [B*H, ceil(N/128), ld] for keys t < ld.
+hipError_t launch_smooth_q(const void* q, int dtype, int B, int H, int N, int d, int nhd,
+                           int8_t* q_i8, float* q_scale, float* q_mean, int32_t* q_w,
+                           hipStream_t s);
+hipError_t launch_sq_comp(const int8_t* k_i8, const int32_t* q_w, int B, int H, int N, int d,
+                          int ld, int bias, int32_t* comp, hipStream_t s);
+// The FP16-mode accumulator start (bit pattern of 1.5 * 2^23) that the
+// compensation carries when it seeds the attention kernel's INT32 product.
+constexpr int kSqBiasFp16 = 0x4B400000;
 
 // Float32 softmax attention on selected query rows (reference for profiling).
 hipError_t launch_ref_rows(const void* q, const void* k, const void* v, int dtype, int B, int H,

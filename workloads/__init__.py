@@ -28,7 +28,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "TABLE7", "SHARDS", "PV_INT8", "named", "make_inputs", "round_to_bf16_bits",
+__all__ = ["Workload", "WORKLOADS", "TABLE7", "SHARDS", "PV_INT8", "SMOOTH_Q", "named", "make_inputs", "round_to_bf16_bits",
            "round_to_fp16", "bf16_bits_to_f32", "Inputs", "rope_tables", "to_nhd"]
 
 
@@ -45,6 +45,7 @@ class Workload:
     seed: int
     extras: str         # which outlier recipe to apply (see _apply_extras)
     note: str = ""
+    smooth_q: bool = False   # also smooth Q per block (the SageAttention2 step)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -107,9 +108,21 @@ PV_INT8 = {
 }
 
 
+# Q smoothed per block as well as K: on the headline shape, and on inputs whose
+# Q carries a per-channel bias shared by all tokens (the case it is for).
+SMOOTH_Q = {
+    "c3sq": WORKLOADS["c3"].with_(name="c3sq", smooth_q=True,
+                                  note="c3 with Q smoothed per 128-token block"),
+    "qb_sq": Workload("qb_sq", 2, 16, 4096, 128, "bf16", False, "fp16", 5, "qbias4_kbias4",
+                      "Q and K with per-channel biases ~ N(0, 4^2), Q smoothed", True),
+    "qb_plain": Workload("qb_plain", 2, 16, 4096, 128, "bf16", False, "fp16", 5, "qbias4_kbias4",
+                         "the inputs of qb_sq without smoothing Q"),
+}
+
+
 def named(name: str) -> Workload:
-    """A workload of WORKLOADS, TABLE7, SHARDS or PV_INT8 by name."""
-    for table in (WORKLOADS, TABLE7, SHARDS, PV_INT8):
+    """A workload of WORKLOADS, TABLE7, SHARDS, PV_INT8 or SMOOTH_Q by name."""
+    for table in (WORKLOADS, TABLE7, SHARDS, PV_INT8, SMOOTH_Q):
         if name in table:
             return table[name]
     raise KeyError(name)
