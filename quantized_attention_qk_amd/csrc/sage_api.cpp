@@ -275,8 +275,8 @@ int sage_smooth_q(const void* q, const int8_t* k_i8, int dtype, int B, int H, in
   if (!q || !k_i8 || !q_i8 || !q_scale || !q_mean || !q_w || !q_comp) return SAGE_ERR_INVALID_ARG;
   if (seed_pv_mode != -1 && !sage::pv_valid(seed_pv_mode)) return SAGE_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_i8) || !aligned16(q_i8) || !aligned16(q_w) ||
-      (reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(q_mean) & 3u) ||
-      (reinterpret_cast<uintptr_t>(q_comp) & 3u))
+      !aligned16(q_comp) || (reinterpret_cast<uintptr_t>(q_scale) & 3u) ||
+      (reinterpret_cast<uintptr_t>(q_mean) & 3u))
     return SAGE_ERR_INVALID_ARG;
   if (dtype != SAGE_DT_F16 && dtype != SAGE_DT_BF16) return SAGE_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;

@@ -55,6 +55,7 @@ __global__ __launch_bounds__(256) void smooth_q_kernel(
   // one IEEE division by the token count
   if (tid < D) {
     float acc = 0.f;
+#pragma unroll 16
     for (int t = 0; t < ntok; ++t) acc += in_to_f32<DT>(tile[t * D + tid]) * inv_sqrt_d;
     qbar[tid] = acc / (float)ntok;
   }
@@ -132,66 +133,101 @@ __global__ __launch_bounds__(256) void smooth_q_kernel(
 // 2^22 leaves the top digit in [-2, 2]), each digit plane multiplied with K^
 // (v_mfma_i32_32x32x32_i8, A = 32 keys of K^, B = 32 blocks' digits), and the
 // planes combined with weights 1, 2^7, 2^14, 2^21 in wrapping 32-bit
-// arithmetic, which is exact because |w . K^| <= 2^29.  Workgroup = 4
-// wavefronts = 128 keys x 32 Q blocks of one (b, h).
+// arithmetic, which is exact because |w . K^| <= 2^29.  Workgroup = one
+// (b, h) and a chunk of kSqChunk keys; its four wavefronts take four groups
+// of 32 Q blocks (more groups in turn when there are more than 128 blocks),
+// build their blocks' digit operands once and walk the chunk's 32-key tiles,
+// so each K^ tile comes from HBM once and is shared in L2 by the wavefronts.
+constexpr int kSqChunk = 256;
 template <int D>
 __global__ __launch_bounds__(256) void sq_comp_kernel(const int8_t* __restrict__ k_i8,
                                                       const int32_t* __restrict__ q_w, int N,
                                                       int nqb, int ld, int bias,
                                                       int32_t* __restrict__ comp) {
-  const int bh = blockIdx.z;
+  constexpr int KT = D / 32;
+  const int bh = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, hh = lane >> 5;
-  const int t0 = blockIdx.x * 128 + wave * 32;
-  const int qb0 = blockIdx.y * 32;
-  if (t0 >= ld) return;
-  const int key = t0 + n;          // A row of this lane
-  const int qb = qb0 + n;          // B column of this lane
-  const int8_t* krow = k_i8 + ((size_t)bh * N + key) * D + 16 * hh;
-  const int32_t* wrow = q_w + ((size_t)bh * nqb + qb) * D + 16 * hh;
-  v16i acc[4] = {};
+  const int c0 = blockIdx.x * kSqChunk;
+  const int c1 = min(c0 + kSqChunk, ld);
+  const bool vec = (ld & 3) == 0;   // rows 16-byte aligned: 16-byte stores
+  for (int g = wave; g * 32 < nqb; g += 4) {
+    const int qb = g * 32 + n;      // B column of this lane
+    // the digit operands of this lane's block: plane p, d-step kt
+    v4i dig[4][KT];
 #pragma unroll
-  for (int kt = 0; kt < D / 32; ++kt) {
-    const v4i a = key < N ? *reinterpret_cast<const v4i*>(krow + 32 * kt) : v4i{0, 0, 0, 0};
-    int w[16];
+    for (int kt = 0; kt < KT; ++kt) {
+      uint32_t dd[4][4] = {};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4i x = qb < nqb ? *reinterpret_cast<const v4i*>(wrow + 32 * kt + 4 * j)
-                             : v4i{0, 0, 0, 0};
-      w[4 * j] = x[0]; w[4 * j + 1] = x[1]; w[4 * j + 2] = x[2]; w[4 * j + 3] = x[3];
-    }
-    uint32_t dig[4][4] = {};
+      for (int j = 0; j < 4; ++j) {
+        const v4i x = qb < nqb ? *reinterpret_cast<const v4i*>(
+                                     q_w + ((size_t)bh * nqb + qb) * D + 32 * kt + 16 * hh + 4 * j)
+                               : v4i{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int x = w[i];
+        for (int u = 0; u < 4; ++u) {
+          int v = x[u];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int dp = p < 3 ? ((x + 64) & 127) - 64 : x;
-        x = (x - dp) >> 7;
-        dig[p][i >> 2] |= ((uint32_t)(uint8_t)(int8_t)dp) << (8 * (i & 3));
+          for (int p = 0; p < 4; ++p) {
+            const int dp = p < 3 ? ((v + 64) & 127) - 64 : v;
+            v = (v - dp) >> 7;
+            dd[p][j] |= ((uint32_t)(uint8_t)(int8_t)dp) << (8 * u);
+          }
+        }
       }
-    }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const v4i b = {(int)dig[p][0], (int)dig[p][1], (int)dig[p][2], (int)dig[p][3]};
-      acc[p] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[p], 0, 0, 0);
+      for (int p = 0; p < 4; ++p)
+        dig[p][kt] = v4i{(int)dd[p][0], (int)dd[p][1], (int)dd[p][2], (int)dd[p][3]};
     }
-  }
-  if (qb >= nqb) return;
-  int32_t* out = comp + ((size_t)bh * nqb + qb) * ld;
+    int32_t* out = comp + ((size_t)bh * nqb + qb) * ld;
+    // A operand (this lane's key row of K^) of a 32-key tile; the next
+    // tile's is loaded while the current one is multiplied
+    auto load_a = [&](int t0, v4i (&a)[KT]) __attribute__((always_inline)) {
+      const int key = t0 + n;
+      const int8_t* krow = k_i8 + ((size_t)bh * N + key) * D + 16 * hh;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int t = t0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-    if (t < ld) {
-      // copy the elements to scalars first (clang mis-lowers some
-      // ext_vector element uses)
-      const uint32_t p0 = (uint32_t)acc[0][r], p1 = (uint32_t)acc[1][r];
-      const uint32_t p2 = (uint32_t)acc[2][r], p3 = (uint32_t)acc[3][r];
-      const int P = (int)(p0 + (p1 << 7) + (p2 << 14) + (p3 << 21));
-      int c = P >> kSqFracBits;                           // floor
-      const int rem = P - (c << kSqFracBits);             // 0 .. 255
-      c += (rem > 128 || (rem == 128 && (c & 1))) ? 1 : 0;
-      out[t] = c + bias;
+      for (int kt = 0; kt < KT; ++kt)
+        a[kt] = key < N ? *reinterpret_cast<const v4i*>(krow + 32 * kt) : v4i{0, 0, 0, 0};
+    };
+    v4i a_next[KT];
+    load_a(c0, a_next);
+    for (int t0 = c0; t0 < c1; t0 += 32) {
+      v4i a[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) a[kt] = a_next[kt];
+      if (t0 + 32 < c1) load_a(t0 + 32, a_next);
+      v16i acc[4] = {};
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          acc[p] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[kt], dig[p][kt], acc[p], 0, 0, 0);
+      if (qb >= nqb) continue;
+      int cv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // copy the elements to scalars first (clang mis-lowers some
+        // ext_vector element uses)
+        const uint32_t p0 = (uint32_t)acc[0][r], p1 = (uint32_t)acc[1][r];
+        const uint32_t p2 = (uint32_t)acc[2][r], p3 = (uint32_t)acc[3][r];
+        const int P = (int)(p0 + (p1 << 7) + (p2 << 14) + (p3 << 21));
+        int c = P >> kSqFracBits;                           // floor
+        const int rem = P - (c << kSqFracBits);             // 0 .. 255
+        c += (rem > 128 || (rem == 128 && (c & 1))) ? 1 : 0;
+        cv[r] = c + bias;
+      }
+      // register r holds key t0 + 8 (r/4) + 4 hh + r%4
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t0 + 8 * j + 4 * hh;
+        if (vec && t + 3 < ld) {
+          *reinterpret_cast<v4i*>(out + t) = v4i{cv[4 * j], cv[4 * j + 1], cv[4 * j + 2],
+                                                 cv[4 * j + 3]};
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (t + u < ld) out[t + u] = cv[4 * j + u];
+        }
+      }
     }
   }
 }
@@ -217,7 +253,7 @@ hipError_t launch_smooth_q(const void* q, int dtype, int B, int H, int N, int d,
 hipError_t launch_sq_comp(const int8_t* k_i8, const int32_t* q_w, int B, int H, int N, int d,
                           int ld, int bias, int32_t* comp, hipStream_t s) {
   const int nqb = ceil_div(N, kQBlock);
-  dim3 grid(ceil_div(ld, 128), ceil_div(nqb, 32), B * H);
+  dim3 grid(ceil_div(ld, kSqChunk), B * H);
   if (d == 64)
     sq_comp_kernel<64><<<grid, 256, 0, s>>>(k_i8, q_w, N, nqb, ld, bias, comp);
   else if (d == 128)
