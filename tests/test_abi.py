@@ -224,3 +224,42 @@ def test_layout_and_rope_validation():
         assert h.sage_smooth_quant_qk_ex(P, P, 0, 1, P, P, 1, 1, 300, 64, P, P, P, P, P, P,
                                          1 << 30, None) == NO_DEVICE
         assert h.sage_quant_v_ex(P, 0, 1, 1, 1, 300, 64, 0, P, None, P, 1 << 30, None) == NO_DEVICE
+
+
+def test_smooth_q_entries_validation():
+    # sage_attn_fwd_sq: q, k, v, o, B, H, N, d, causal, pv, dtype, layout, out_f32, ws, bytes, stream
+    h = lib()
+    ws = P + 0x100000
+    need = h.sage_attn_sq_workspace_bytes(1, 2, 100, 64, 0)
+    assert need > h.sage_attn_workspace_bytes(1, 2, 100, 64, 0)   # + means, w, compensation
+    assert h.sage_attn_sq_workspace_bytes(1, 2, 100, 96, 0) == 0
+    assert h.sage_attn_sq_workspace_bytes(1, 2, 100, 64, 3) == 0
+    base = [P, P, P, P + 0x1000, 1, 2, 100, 64, 0, 0, 0]
+    assert h.sage_attn_fwd_sq(*base, 0, 2, ws, 1 << 40, None) == INVALID        # out_f32
+    assert h.sage_attn_fwd_sq(*base, 2, 0, ws, 1 << 40, None) == INVALID        # layout
+    assert h.sage_attn_fwd_sq(*base, 0, 0, ws, need - 1, None) == WORKSPACE
+    assert h.sage_attn_fwd_sq(P, P, P, P, *base[4:], 0, 0, ws, 1 << 40, None) == INVALID  # o aliases q
+    if not torch.cuda.is_available():
+        assert h.sage_attn_fwd_sq(*base, 0, 0, ws, need, None) == NO_DEVICE
+    # sage_smooth_q: q, k_i8, dtype, B, H, N, d, seed_pv_mode, q_i8, q_scale, q_mean, q_w, q_comp
+    args = [P, P, 0, 1, 2, 100, 64, -1, P, P, P, P, P, None]
+    bad = list(args)
+    bad[7] = 5                      # seed mode
+    assert h.sage_smooth_q(*bad) == INVALID
+    bad = list(args)
+    bad[12] = P + 4                 # q_comp not 16-byte aligned
+    assert h.sage_smooth_q(*bad) == INVALID
+    bad = list(args)
+    bad[6] = 96
+    assert h.sage_smooth_q(*bad) == UNSUPPORTED
+    # sage_attn_fwd_quantized_sq: the seeds are required and 16-byte aligned
+    qargs = [P] * 6 + [P, P] + [1, 2, 100, 64, 0, 0, 0, None]
+    bad = list(qargs)
+    bad[6] = None
+    assert h.sage_attn_fwd_quantized_sq(*bad) == INVALID
+    bad = list(qargs)
+    bad[6] = P + 8
+    assert h.sage_attn_fwd_quantized_sq(*bad) == INVALID
+    if not torch.cuda.is_available():
+        assert h.sage_smooth_q(*args) == NO_DEVICE
+        assert h.sage_attn_fwd_quantized_sq(*qargs) == NO_DEVICE
