@@ -155,8 +155,9 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
  * |C| <= 2^21); any other block is quantised as in sage_attn_fwd (w = 0).
  * Arguments as sage_attn_fwd_ex without RoPE (layout SAGE_LAYOUT_HND or
  * SAGE_LAYOUT_NHD; out_f32 0/1); the workspace must hold
- * sage_attn_sq_workspace_bytes(...) bytes (it adds ceil(N/128) * ceil(N/64)
- * * 64 int32 compensation values per head).
+ * sage_attn_sq_workspace_bytes(...) bytes.  It adds ceil(N/128) * ceil(N/64)
+ * * 64 int32 compensation values per head, about N^2/32 bytes: 8 MiB at
+ * N = 16384, 512 MiB at N = 131072, so this pass suits moderate N.
  */
 size_t sage_attn_sq_workspace_bytes(int B, int H, int N, int d, int pv_mode);
 int sage_attn_fwd_sq(const void* q, const void* k, const void* v, void* o,
