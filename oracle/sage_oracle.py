@@ -227,8 +227,8 @@ def q_compensation(q_w: np.ndarray, k_i8: np.ndarray) -> np.ndarray:
     """The compensation of smoothed Q blocks, C = rne((w K^^T) / 2^8): int32
     [B, H, nb, N].  The product is exact (a float64 product of integers below
     2^53); the division rounds to nearest, ties to even."""
-    p = np.einsum("bhqc,bhtc->bhqt", q_w.astype(np.float64),
-                  k_i8.astype(np.float64)).astype(np.int64)
+    p = np.matmul(q_w.astype(np.float64),
+                  np.swapaxes(k_i8.astype(np.float64), -1, -2)).astype(np.int64)
     q = p >> SQ_FRAC_BITS                                  # floor
     rem = p - (q << SQ_FRAC_BITS)                          # in [0, 2^8)
     half = 1 << (SQ_FRAC_BITS - 1)

@@ -76,6 +76,8 @@ SMALL = [
     small("i2113", B=1, H=2, N=2113, d=128, pv_mode="int8", extras="kbias4"),
     small("i1105c", N=1105, d=64, H=1, causal=True, pv_mode="int8", extras="kchan20"),
     small("r1000i8", N=1000, d=64, pv_mode="int8", extras="ramp"),
+    small("i1", N=1, d=128, pv_mode="int8"), small("i65c", N=65, d=64, causal=True,
+                                                   pv_mode="int8", dtype="bf16"),
 ]
 
 
@@ -310,6 +312,8 @@ def test_table7_shapes(name):
 @pytest.mark.parametrize("wl", [
     small("long1m", B=1, H=1, N=(1 << 20) + 37, d=128, dtype="bf16", pv_mode="fp16", seed=31),
     small("long512kc8", B=1, H=1, N=(1 << 19) + 5, d=64, causal=True, pv_mode="fp8", seed=32),
+    small("long512kci8", B=1, H=1, N=(1 << 19) + 3, d=128, causal=True, pv_mode="int8",
+          seed=33),
 ], ids=lambda w: w.name)
 def test_long_sequence(wl):
     note(f"long sequence {wl}")

@@ -171,6 +171,50 @@ def test_smooth_q_stages_equal_whole_pass(wl):
     assert torch.equal(staged.view(torch.int32), whole.view(torch.int32))
 
 
+@pytest.mark.parametrize("wl", [small("e1", N=1, d=64, extras="qbias4_kbias4"),
+                                small("e65", N=65, d=128, dtype="bf16", causal=True,
+                                      pv_mode="fp8", extras="qbias4_kbias4"),
+                                small("e129i8", N=129, d=64, pv_mode="int8",
+                                      extras="qbias4_kbias4")],
+                         ids=lambda w: w.name)
+def test_smooth_q_edge_lengths(wl):
+    # one token (a single-token block: Q~ = 0, so the block stays unsmoothed),
+    # a 65-token block, a 1-token last block
+    note(f"edge {wl}")
+    inp = make_inputs(wl)
+    q, k, v = inp.torch_tensors("cuda")
+    res = qa().smooth_quant_qk(q, k)
+    sq = qa().smooth_q(q, res["k_i8"])
+    o32 = to_np(qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out_f32=True,
+                               smooth_q=True))
+    torch.cuda.synchronize()
+    pq = oracle.smooth_quant_qk(inp.qf, inp.kf, smooth_q=True)
+    for key in ("q_i8", "q_w", "q_comp"):
+        np.testing.assert_array_equal(to_np(sq[key]), pq[key], err_msg=key)
+    np.testing.assert_array_equal(to_np(sq["q_scale"]).view(np.uint32),
+                                  pq["q_scale"].view(np.uint32))
+    if wl.N == 1:
+        assert not pq["q_smoothed"].any()
+    ref, allow = oracle_o(wl, inp.qf, inp.kf, inp.vf)
+    compare(o32, ref, allow, f"{wl.name} O f32")
+
+
+def test_smooth_q_long_head():
+    # one head of 2^17 + 17 tokens: the seed table is 1025 blocks x 131136 keys
+    # (512 MiB); stage bit-exact on sampled blocks, O on sampled rows
+    wl = small("sqlong", B=1, H=1, N=(1 << 17) + 17, d=128, dtype="bf16", causal=True,
+               extras="qbias4_kbias4", seed=34)
+    note(f"long {wl}")
+    inp = make_inputs(wl)
+    q, k, v = inp.torch_tensors("cuda")
+    o32 = qa().sage_attn(q, k, v, causal=True, pv_mode="fp16", out_f32=True, smooth_q=True)
+    torch.cuda.synchronize()
+    N = wl.N
+    rows = np.array(sorted({0, 1, 127, 128, 65536, N - 18, N - 17, N - 1}))
+    ref, _ = oracle_o(wl, inp.qf, inp.kf, inp.vf, rows=rows)
+    compare(to_np(o32[0, 0, torch.from_numpy(rows).cuda()]), ref[0, 0], None, "sqlong O f32")
+
+
 @pytest.mark.parametrize("name", ["c3sq", "qb_sq"])
 def test_smooth_q_full_size(name):
     wl = named(name)
