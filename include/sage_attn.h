@@ -87,7 +87,7 @@ size_t sage_attn_workspace_bytes(int B, int H, int N, int d, int pv_mode);
  *   4. pv_mode SAGE_PV_FP16: O += fp16(P~) V'_j with V' = fp16(V);
  *      pv_mode SAGE_PV_FP8:  O += E4M3(448 P~) V^_j with the static delta_P = 1/448
  *      and V^ = E4M3(V * 448/colmax|V|), delta_V = colmax|V|/448 per channel;
- *      FP32 accumulation in both modes;
+ *      FP32 accumulation in both these modes;
  *      pv_mode SAGE_PV_INT8: O = alpha O + (P^ V^_j as INT32) with P^ =
  *      rne(127 P~) in [0, 127] (static delta_P = 1/127, [SA] §7 key
  *      implementation details) and V^ = clamp(rne(V * 127/colmax|V|), -127,

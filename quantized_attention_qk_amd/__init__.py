@@ -1,5 +1,6 @@
 """MI355X (gfx950) SageAttention forward pass: smoothed per-block INT8 Q K^T,
-online softmax, FP16 or FP8 E4M3 P~V, behind a C ABI (include/sage_attn.h).
+online softmax, FP16, FP8 E4M3 or INT8 P~V, optionally with Q smoothed per
+block too, behind a C ABI (include/sage_attn.h).
 
 Importing this package does not require a GPU; calling into it does, and it
 fails loudly (RuntimeError) when the HIP library is missing or no device is

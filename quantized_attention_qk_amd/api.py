@@ -73,7 +73,7 @@ def sage_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
               workspace: torch.Tensor | None = None, out_f32: bool = False,
               layout: str = "HND", rope=None, smooth_q: bool = False) -> torch.Tensor:
     """SageAttention forward: O = softmax(Q K^T / sqrt(d)) V with smoothed INT8
-    Q K^T and FP16 or FP8 P~V.  q, k, v: contiguous fp16/bf16 tensors, [B, H, N,
+    Q K^T and FP16, FP8 or INT8 P~V.  q, k, v: contiguous fp16/bf16 tensors, [B, H, N,
     d] (layout "HND") or [B, N, H, d] ("NHD"); O has the same layout.
 
     rope: optional (cos, sin) float32 [N, d/2] device tables; Q and K are then
