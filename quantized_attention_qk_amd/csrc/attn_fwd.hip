@@ -343,28 +343,35 @@ constexpr float kOptimisticSum = 16384.0f;
 template <int PV>
 constexpr int kKSlots = PV == kPvFp16 ? 3 : 2;
 
+// Visibility bits of a lane's 32 scores of a tile (bit 16 blk + r: key
+// key0 + 32 blk + 8 (r/4) + 4 hh + r%4) for the keys at most `last`.
+__device__ __forceinline__ uint32_t key_mask(int key0, int hh, int last) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      m |= (uint32_t)(key0 + 32 * blk + 8 * (r >> 2) + 4 * hh + (r & 3) <= last) << (16 * blk + r);
+  return m;
+}
+
 // Online softmax of one tile: returns alpha = exp2(m_old - m_new) and writes
-// P~ (FP8: 448 P~; INT8: round(127 P~)) into the MFMA operand.  MASK selects the variant that
-// masks keys >= N and (causal) keys > query; a fully masked tile leaves the
+// P~ (FP8: 448 P~; INT8: round(127 P~)) into the MFMA operand.  MASK selects
+// the variant that hides the keys whose bit in `keep` (key_mask layout) is
+// clear (keys >= N, causal keys > query); a fully masked tile leaves the
 // state unchanged (P~ = 0, alpha = 1).
-template <int PV, bool CAUSAL, bool MASK>
+template <int PV, bool MASK>
 __device__ __forceinline__ float softmax_tile(v16i (&s)[2], float& m_run, float& l_run,
-                                              PTile<PV>& pt, TileScale ts, MaxGrid grid, int key0,
-                                              int N, int qrow, int hh) {
+                                              PTile<PV>& pt, TileScale ts, MaxGrid grid,
+                                              uint32_t keep, int hh) {
   constexpr bool F16 = PV == kPvFp16;
-  uint32_t keep = 0xffffffffu;   // bit 16*blk + r: key visible
   if constexpr (MASK) {
-    keep = 0u;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 32 * blk + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const bool ok = key < N && (!CAUSAL || key <= qrow);
-        keep |= (uint32_t)ok << (16 * blk + r);
+      for (int r = 0; r < 16; ++r)
         // FP16: the biased scores are positive floats, 0 is below all of them
-        if (!ok) s[blk][r] = F16 ? 0 : INT32_MIN;
-      }
+        if (!((keep >> (16 * blk + r)) & 1u)) s[blk][r] = F16 ? 0 : INT32_MIN;
   }
   // row max: chain of 3-input maxima over the lane's 32 scores, then the pair
   // (in FP16 mode on the bit patterns of positive floats, which order alike)
@@ -733,8 +740,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
       // rare: recompute the tile's scores (into the registers they came in,
       // free by now) and take the max-based rule
       qk_tile<D, SQ>(s_cur, qf, kb_prev, n, hh, init);
-      rescale<D>(o, softmax_tile<PV, false, false>(s_cur, m_run, l_run, p_new, ts, grid, 0, 0,
-                                                   0, hh));
+      rescale<D>(o, softmax_tile<PV, false>(s_cur, m_run, l_run, p_new, ts, grid, ~0u, hh));
     } else {
       l_run = lsum;
     }
@@ -865,12 +871,29 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   // the same fused multiply-add that adds the product
   float alpha_pend = 1.f;
 
+  // Masks of the tiles that need one.  Causal: the two tiles on the diagonal
+  // of query block qb (2 qb + dd, dd = 0, 1) show key 64 dd + off of the tile
+  // to row 32 wave + n of the block iff 64 dd + off <= 32 wave + n, the same
+  // for every block, so both masks are formed once.  The tile holding key
+  // N - 1 of a ragged N also hides the keys >= N.
+  uint32_t kdiag0 = ~0u, kdiag1 = ~0u;
+  if constexpr (CAUSAL) {
+    kdiag0 = key_mask(0, hh, kWaveQ * wave + n);
+    kdiag1 = key_mask(kKvTile, hh, kWaveQ * wave + n);
+  }
+  auto tile_keep = [&](int t) __attribute__((always_inline)) {
+    uint32_t keep = ~0u;
+    if constexpr (CAUSAL) {
+      const int dd = t - 2 * qb;   // 0 or 1 for a masked tile of a causal block
+      if (dd >= 0) keep = dd == 0 ? kdiag0 : kdiag1;
+    }
+    if ((t + 1) * kKvTile > N) keep &= key_mask(t * kKvTile, hh, N - 1);
+    return keep;
+  };
   auto softmax_any = [&](v16i (&sc)[2], PTile<PV>& pn, int t) __attribute__((always_inline)) {
     const TileScale ts = tile_scale<PV>(cq, ks_bh[t]);
-    return t < nt_full ? softmax_tile<PV, CAUSAL, false>(sc, m_run, l_run, pn, ts, grid,
-                                                         t * kKvTile, N, qrow, hh)
-                       : softmax_tile<PV, CAUSAL, true>(sc, m_run, l_run, pn, ts, grid,
-                                                        t * kKvTile, N, qrow, hh);
+    return t < nt_full ? softmax_tile<PV, false>(sc, m_run, l_run, pn, ts, grid, ~0u, hh)
+                       : softmax_tile<PV, true>(sc, m_run, l_run, pn, ts, grid, tile_keep(t), hh);
   };
 
   // Prologue: S(0), S(1), P~(0); then K^(2) into the slot of K^(0).
@@ -947,8 +970,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
       const float dk = dk_next;
       dk_next = ks_bh[jj + 2];
       pv_tile<D, PV>(o, p_cur, vbuf[U], n, hh, alpha_pend);
-      alpha_pend = softmax_tile<PV, CAUSAL, false>(s_cur, m_run, l_run, p_new,
-                                                   tile_scale<PV>(cq, dk), grid, 0, N, 0, hh);
+      alpha_pend = softmax_tile<PV, false>(s_cur, m_run, l_run, p_new, tile_scale<PV>(cq, dk),
+                                           grid, ~0u, hh);
       qk_tile<D, SQ>(s_new, qf, kbuf[U], n, hh, init);
       asm volatile("" ::"s"(dk_next));
       wait_lds_loads();
