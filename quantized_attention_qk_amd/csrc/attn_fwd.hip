@@ -484,19 +484,27 @@ __device__ __forceinline__ void pv_tile(v16f (&o)[D / 32], const PTile<PV>& pt,
   } else {
     const v4i plo = {pt.w[0], pt.w[1], pt.w[2], pt.w[3]};
     const v4i phi = {pt.w[4], pt.w[5], pt.w[6], pt.w[7]};
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
+    // two channel blocks in flight: the MFMA pair of block cb + 1 is issued
+    // before block cb's product is converted and added
+    v16i acc[2];
+    auto product = [&](int cb) __attribute__((always_inline)) {
       const int row = 32 * cb + n;
       const int sw = row_swizzle<64>(row);
       const v4i a0 = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh) ^ sw) << 4));
       const v4i a1 = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh + 1) ^ sw) << 4));
-      v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, plo, v16i{}, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, phi, acc, 0, 0, 0);
+      v16i& r = acc[cb & 1];
+      r = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, plo, v16i{}, 0, 0, 0);
+      r = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, phi, r, 0, 0, 0);
+    };
+    product(0);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      if (cb + 1 < NCB) product(cb + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         // copy the element to a scalar first (see softmax_tile)
-        const int pr = acc[r];
+        const int pr = acc[cb & 1][r];
         o[cb][r] = __builtin_fmaf(o[cb][r], alpha, (float)pr);
       }
       __builtin_amdgcn_sched_barrier(0);
