@@ -78,6 +78,10 @@ SMALL = [
     small("r1000i8", N=1000, d=64, pv_mode="int8", extras="ramp"),
     small("i1", N=1, d=128, pv_mode="int8"), small("i65c", N=65, d=64, causal=True,
                                                    pv_mode="int8", dtype="bf16"),
+    # the two sides of the one-launch prepass limit (2048 tokens)
+    small("b2048f8", N=2048, d=128, pv_mode="fp8", extras="kbias4"),
+    small("b2049ci8", N=2049, d=64, causal=True, dtype="bf16", pv_mode="int8",
+          extras="kchan20"),
 ]
 
 
