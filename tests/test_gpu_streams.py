@@ -29,6 +29,9 @@ def qa():
 
 CASES = [small("g16", B=2, H=3, N=700, d=128, dtype="bf16", causal=True, seed=41),
          small("g8", B=1, H=4, N=2500, d=64, pv_mode="fp8", seed=42)]
+# the INT8 P~V pass with Q smoothed (six kernels, seeds in the workspace)
+GRAPH_CASES = CASES + [small("gi8sq", B=1, H=3, N=1300, d=128, pv_mode="int8", seed=43,
+                             extras="qbias4_kbias4").with_(smooth_q=True)]
 
 
 def test_two_streams_at_once():
@@ -53,26 +56,26 @@ def test_two_streams_at_once():
     note("two streams: 3 concurrent pairs bitwise equal to sequential runs")
 
 
-@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", GRAPH_CASES, ids=lambda w: w.name)
 def test_graph_capture_and_replay(wl):
     inp = make_inputs(wl)
     q, k, v = inp.torch_tensors("cuda")
     B, H, N, d = wl.B, wl.H, wl.N, wl.d
-    ws = torch.empty(qa().workspace_bytes(B, H, N, d, wl.pv_mode), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(qa().workspace_bytes(B, H, N, d, wl.pv_mode, wl.smooth_q),
+                     dtype=torch.uint8, device="cuda")
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     # eager warm-up on a side stream, as graph capture wants
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out=out, workspace=ws,
-                       out_f32=True)
+                       out_f32=True, smooth_q=wl.smooth_q)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out=out, workspace=ws,
-                       out_f32=True)
+                       out_f32=True, smooth_q=wl.smooth_q)
     torch.cuda.synchronize()
     gen = torch.Generator(device="cuda").manual_seed(wl.seed)
     for rep in range(4):
@@ -84,7 +87,8 @@ def test_graph_capture_and_replay(wl):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        ref = qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out_f32=True)
+        ref = qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out_f32=True,
+                             smooth_q=wl.smooth_q)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {rep}"
         del junk
