@@ -396,20 +396,71 @@ __global__ __launch_bounds__(256) void prep_v_kernel(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// One-launch prepass for short sequences.  Workgroups take roles, ordered so
-// that the longest ones start first:
-//   role 0 of a head     K: column sums -> mean -> all K^ blocks of the head,
-//                        each wavefront quantising its own blocks;
-//   roles 1 .. nqb       one Q^ block each (no statistics needed);
-//   then ntiles roles    one V tile each (FP8: the tile's workgroup takes the
-//                        head's column maxima itself).
-// Every value is computed by the same expressions, in the same order, as in
-// the multi-kernel path above (a maximum does not depend on order), so the
+// Two-launch prepass for short sequences.  The first launch's workgroups take
+// roles, ordered so that the longest ones start first:
+//   roles 0 .. nch-1     the column sums of one 256-token chunk of K each
+//                        (the chunk staged in LDS, 128 tokens at a time,
+//                        then every channel summed in token order);
+//   next nqb roles       one Q^ block each (no statistics needed);
+//   then ntiles roles    one V tile each (FP8, INT8: the tile's workgroup
+//                        takes the head's column maxima itself).
+// The second launch has one wavefront per K^ block: the head's mean from the
+// chunk sums (chunks in order, one IEEE division), then the block.  A head of
+// one chunk (N <= 256) needs no second launch: the chunk's workgroup forms
+// the mean from its own sums and its four wavefronts quantise the K^ blocks.  Every
+// value is computed by the same expressions, in the same order, as in the
+// multi-kernel path above (a maximum does not depend on order), so the
 // results are identical bit for bit.
+constexpr int kStageTok = 128;
 
-// K^ block blk of head bh by one wavefront.  Every lane owns the same 8
-// channels in all of its chunks (64 * 8 is a multiple of d); the block is read
-// twice, once for the absmax and once for the encoding, to keep registers low.
+// Column sums of chunk `chunk` of head bh into part_sum (as colstats_chunk),
+// by the whole workgroup: the chunk's rows are staged in `tile` (kStageTok * D
+// halves) and thread c < D adds channel c over the tokens in order.
+// Returns thread c's sum (channel c; 0 for c >= D).
+template <int DT, int D, bool ROPE>
+__device__ __forceinline__ float colstats_chunk_staged(
+    const uint16_t* __restrict__ k, int N, int H, int nhd, int nchunks,
+    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
+    float* __restrict__ part_sum, int bh, int chunk, uint16_t* tile) {
+  constexpr int HD = D / 2;
+  constexpr int CPR = D / 8;
+  const int t0 = chunk * kMeanChunk;
+  const int cnt = min(kMeanChunk, N - t0);
+  const int c = threadIdx.x;
+  float acc = 0.f;
+  for (int s0 = 0; s0 < cnt; s0 += kStageTok) {
+    const int ns = min(kStageTok, cnt - s0);
+    for (int x = threadIdx.x; x < ns * CPR; x += 256)
+      *reinterpret_cast<uint4*>(&tile[x * 8]) = *reinterpret_cast<const uint4*>(
+          k + row_off<D>(bh, t0 + s0 + x / CPR, H, N, nhd) + (x % CPR) * 8);
+    __syncthreads();
+    if (c < D) {
+      if constexpr (!ROPE) {
+#pragma unroll 8
+        for (int t = 0; t < ns; ++t) acc += in_to_f32<DT>(tile[t * D + c]);
+      } else {
+        // rope_pair's arithmetic: the low channel of a pair takes x c - y s,
+        // the high one y c + x s (x low, y high), each rounded to float32
+        const bool low = c < HD;
+        const int pc = low ? c + HD : c - HD;
+        const size_t tb = (size_t)(t0 + s0) * HD + (low ? c : pc);
+#pragma unroll 8
+        for (int t = 0; t < ns; ++t) {
+          const float f = in_to_f32<DT>(tile[t * D + c]);
+          const float g = in_to_f32<DT>(tile[t * D + pc]);
+          const float cs = rope_cos[tb + (size_t)t * HD], sn = rope_sin[tb + (size_t)t * HD];
+          float rl, rh;
+          rope_pair(low ? f : g, low ? g : f, cs, sn, rl, rh);
+          acc += low ? rl : rh;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (c < D) part_sum[((size_t)bh * nchunks + chunk) * D + c] = acc;
+  return acc;
+}
+
 template <int DT, int D, bool ROPE>
 __device__ __forceinline__ void kblock_x8(const uint16_t* __restrict__ k, int bh, int tok, int N,
                                           int H, int nhd, int ch0, const float (&mu)[8],
@@ -445,9 +496,10 @@ __device__ __forceinline__ void kblock_x8(const uint16_t* __restrict__ k, int bh
   }
 }
 
+// K^ block blk of head bh by one wavefront; mean: the head's d channel means.
 template <int DT, int D, bool ROPE>
 __device__ __forceinline__ void quant_kblock_wave(
-    const uint16_t* __restrict__ k, const float* __restrict__ k_mean, int N, int H, int nhd,
+    const uint16_t* __restrict__ k, const float* mean, int N, int H, int nhd,
     int nkb, const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
     int8_t* __restrict__ k_i8, float* __restrict__ k_scale, int bh, int blk, int lane) {
   constexpr int CPR = D / 8;                  // chunks per token row
@@ -455,7 +507,6 @@ __device__ __forceinline__ void quant_kblock_wave(
   const int tok0 = blk * kKBlock;
   const int ntok = min(kKBlock, N - tok0);
   const int ch0 = (lane * 8) % D;
-  const float* mean = k_mean + (size_t)bh * D;
   float mu[8];
   {
     const v4f m0 = *reinterpret_cast<const v4f*>(mean + ch0);
@@ -537,7 +588,9 @@ __global__ __launch_bounds__(256) void prepass_roles_kernel(
     float* __restrict__ part_sum, float* __restrict__ k_mean, float* __restrict__ v_scale,
     int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8, float* __restrict__ q_scale,
     float* __restrict__ k_scale, uint8_t* __restrict__ v_out) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[PrepVTile<D>::HALVES];
+  constexpr int TILE = PrepVTile<D>::HALVES > kStageTok * D ? PrepVTile<D>::HALVES
+                                                            : kStageTok * D;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TILE];
   __shared__ float red[4];
   const int bh = blockIdx.x % BH;
   int role = blockIdx.x / BH;
@@ -545,24 +598,27 @@ __global__ __launch_bounds__(256) void prepass_roles_kernel(
   const int nqb = (N + kQBlock - 1) / kQBlock, nkb = (N + kKBlock - 1) / kKBlock;
   const int ntiles = (N + kKvTile - 1) / kKvTile;
   if constexpr (DO_QK) {
-    if (role == 0) {
-      constexpr int P = ColstatsShape<D, ROPE>::P;
-      for (int w = threadIdx.x; w < nch * P; w += 256)
-        colstats_chunk<DT, D, true, false, ROPE, 32>(k, nullptr, N, H, nhd, nch, rope_cos,
-                                                     rope_sin, part_sum, nullptr, bh, w / P,
-                                                     w % P);
-      __syncthreads();
-      for (int c = threadIdx.x; c < D; c += 256)
-        finalize_channel<D, true, false>(part_sum, nullptr, N, nch, k_mean, nullptr, nullptr,
-                                         0.f, bh, c);
-      __syncthreads();
-      const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-      for (int blk = wave; blk < nkb; blk += 4)
-        quant_kblock_wave<DT, D, ROPE>(k, k_mean, N, H, nhd, nkb, rope_cos, rope_sin, k_i8,
-                                       k_scale, bh, blk, lane);
+    if (role < nch) {   // K column sums of one chunk
+      const float acc = colstats_chunk_staged<DT, D, ROPE>(k, N, H, nhd, nch, rope_cos,
+                                                           rope_sin, part_sum, bh, role, tile);
+      if (nch == 1) {
+        // the whole head: its mean is this chunk's sum over N (0.0f + sum in
+        // the chunk order of finalize_channel is the sum itself), then the
+        // K^ blocks, one wavefront each
+        __shared__ __attribute__((aligned(16))) float mean[D];
+        if (threadIdx.x < D) {
+          mean[threadIdx.x] = acc / (float)N;
+          k_mean[(size_t)bh * D + threadIdx.x] = mean[threadIdx.x];
+        }
+        __syncthreads();
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        for (int blk = wave; blk < nkb; blk += 4)
+          quant_kblock_wave<DT, D, ROPE>(k, mean, N, H, nhd, nkb, rope_cos, rope_sin, k_i8,
+                                         k_scale, bh, blk, lane);
+      }
       return;
     }
-    role -= 1;
+    role -= nch;
     if (role < nqb) {   // a Q block: quant_block's index bx < nqb selects Q
       quant_block<DT, D, ROPE>(q, k, k_mean, N, H, nhd, nqb, nkb, inv_sqrt_d, rope_cos,
                                rope_sin, q_i8, k_i8, q_scale, k_scale, bh, role, red);
@@ -588,6 +644,30 @@ __global__ __launch_bounds__(256) void prepass_roles_kernel(
       prep_v_tile<DT, D, PV>(v, nullptr, N, H, nhd, ntiles, v_out, bh, role, tile);
     }
   }
+}
+
+// Second launch of the short-sequence prepass: one wavefront per (K^ block,
+// head).  The head's mean, as finalize_channel forms it (chunk sums in order
+// from 0.0f, one IEEE division by N), into LDS (block 0 also stores it), then
+// the block.
+template <int DT, int D, bool ROPE>
+__global__ __launch_bounds__(64) void prepass_kblocks_kernel(
+    const uint16_t* __restrict__ k, int N, int H, int nhd, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, const float* __restrict__ part_sum,
+    float* __restrict__ k_mean, int8_t* __restrict__ k_i8, float* __restrict__ k_scale) {
+  __shared__ __attribute__((aligned(16))) float mean[D];
+  const int blk = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+  const int nch = (N + kMeanChunk - 1) / kMeanChunk;
+  const int nkb = (N + kKBlock - 1) / kKBlock;
+  for (int c = lane; c < D; c += 64) {
+    float tot = 0.f;
+    for (int j = 0; j < nch; ++j) tot += part_sum[((size_t)bh * nch + j) * D + c];
+    mean[c] = tot / (float)N;
+    if (blk == 0) k_mean[(size_t)bh * D + c] = mean[c];
+  }
+  __syncthreads();
+  quant_kblock_wave<DT, D, ROPE>(k, mean, N, H, nhd, nkb, rope_cos, rope_sin, k_i8, k_scale, bh,
+                                 blk, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -698,7 +778,8 @@ static hipError_t prepass_head_dispatch(const void* q, const void* k, const void
   const float isd = (float)(1.0 / __builtin_sqrt((double)D));
   const bool qk = q != nullptr, dv = v != nullptr, rope = in.rope_cos != nullptr;
   const int BH = B * H;
-  const int roles = (qk ? 1 + ceil_div(N, kQBlock) : 0) + (dv ? ceil_div(N, kKvTile) : 0);
+  const int roles = (qk ? ceil_div(N, kMeanChunk) + ceil_div(N, kQBlock) : 0) +
+                    (dv ? ceil_div(N, kKvTile) : 0);
   const long long grid = (long long)BH * roles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   auto qp = static_cast<const uint16_t*>(q);
@@ -716,6 +797,19 @@ static hipError_t prepass_head_dispatch(const void* q, const void* k, const void
     SAGE_HEAD(false, false, true)
   }
 #undef SAGE_HEAD
+  if (qk && N > kMeanChunk) {   // heads of one chunk finished their K^ above
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 g2(ceil_div(N, kKBlock), BH);
+    if (rope)
+      prepass_kblocks_kernel<DT, D, true><<<g2, 64, 0, s>>>(kp, N, H, in.nhd, in.rope_cos,
+                                                           in.rope_sin, o.part_sum, o.k_mean,
+                                                           o.k_i8, o.k_scale);
+    else
+      prepass_kblocks_kernel<DT, D, false><<<g2, 64, 0, s>>>(kp, N, H, in.nhd, nullptr, nullptr,
+                                                            o.part_sum, o.k_mean, o.k_i8,
+                                                            o.k_scale);
+  }
   return hipGetLastError();
 }
 
