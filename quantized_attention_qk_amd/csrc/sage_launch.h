@@ -73,9 +73,11 @@ struct PrepassOut {
   uint8_t* v_out;
 };
 
-// Sequences up to this length run the prepass in one launch whose workgroups
-// take roles: one per head for the K statistics and K^ blocks, one per Q^
-// block, one per V tile.
+// Sequences up to this length run the prepass in two launches: the first's
+// workgroups take roles (one per 256-token K chunk for its column sums, one
+// per Q^ block, one per V tile), the second forms each head's K mean and
+// quantises one K^ block per wavefront.  A head of one chunk needs only the
+// first launch.
 constexpr int kHeadPrepassMaxN = 2048;
 
 hipError_t launch_prepass_head(const void* q, const void* k, const void* v, int dtype, int B,
