@@ -9,9 +9,12 @@
 // the "8+8" variant of the "SageAttention2++ ..." review page (section 三) --
 // accumulated in FP32 (gfx950 has no FP16-accumulator MFMA), and finally
 // O = O / l.  The all-INT8 variant (detail page, §3 Figure 5) quantises P~
-// with the static delta_P = 1/127 (§7) and V per channel to INT8; each tile's
-// INT32 product P^ V^ is converted to float and added to the rescaled output,
-// O = alpha O + P^ V^, as Eq. 4-5 write it.
+// with the static delta_P = 1/127 (§7) and V per channel to INT8.  Every
+// tile's product P^ V^ then has the same scale delta_P delta_V, so while a
+// row's max stands the products add up exactly in the INT32 accumulator; when
+// the max grows the accumulator is rescaled by alpha (rounded to an integer),
+// O = alpha O + P^ V^ as Eq. 4-5 write it.  Heads longer than 2^17 keys, where
+// INT32 could overflow, convert each tile's product to float instead.
 //
 // MI355X mapping
 // * Workgroup = 4 wavefronts = 128 query rows = one delta_Q block of one (b, h).
@@ -450,10 +453,12 @@ __device__ __forceinline__ float softmax_tile(v16i (&s)[2], float& m_run, float&
   return alpha;
 }
 
-// O^T += V^T P~^T for one tile, V from LDS.  INT8: O = alpha O + P^ V^ with
-// the INT32 product of the tile converted to float (|P^ V^| <= 64 127^2 <
-// 2^24, exact), alpha being the rescale factor of this tile's softmax.
-template <int D, int PV>
+// O^T += V^T P~^T for one tile, V from LDS.  INT8 with ACC: O holds the INT32
+// sum of the products (bit patterns in the float registers) and the MFMAs add
+// to it directly.  INT8 without ACC: O = alpha O + P^ V^ with the INT32
+// product of the tile converted to float (|P^ V^| <= 64 127^2 < 2^24, exact),
+// alpha being the rescale factor of this tile's softmax.
+template <int D, int PV, bool ACC = false>
 __device__ __forceinline__ void pv_tile(v16f (&o)[D / 32], const PTile<PV>& pt,
                                         const uint8_t* vb, int n, int hh, float alpha = 1.f) {
   constexpr int NCB = D / 32;
@@ -480,6 +485,20 @@ __device__ __forceinline__ void pv_tile(v16f (&o)[D / 32], const PTile<PV>& pt,
       const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       // scale operands 127 = E8M0 exponent of 1.0 (no block scaling)
       o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pt.w, o[cb], 0, 0, 0, 127, 0, 127);
+    }
+  } else if constexpr (ACC) {
+    const v4i plo = {pt.w[0], pt.w[1], pt.w[2], pt.w[3]};
+    const v4i phi = {pt.w[4], pt.w[5], pt.w[6], pt.w[7]};
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int row = 32 * cb + n;
+      const int sw = row_swizzle<64>(row);
+      const v4i a0 = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh) ^ sw) << 4));
+      const v4i a1 = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh + 1) ^ sw) << 4));
+      v16i r = __builtin_bit_cast(v16i, o[cb]);
+      r = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, plo, r, 0, 0, 0);
+      r = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, phi, r, 0, 0, 0);
+      o[cb] = __builtin_bit_cast(v16f, r);
     }
   } else {
     const v4i plo = {pt.w[0], pt.w[1], pt.w[2], pt.w[3]};
@@ -520,6 +539,33 @@ __device__ __forceinline__ void rescale(v16f (&o)[D / 32], float alpha) {
   }
 }
 
+// Nearest integer to f, halves rounded up (v_cvt_rpi_i32_f32: floor(f + 0.5)),
+// one instruction; the compiler has no builtin for it.
+__device__ __forceinline__ int round_half_up_i32(float f) {
+  int r;
+  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(f));
+  return r;
+}
+
+// INT8 with ACC: rescale the INT32 sums by alpha, rounded to the nearest
+// integer.  Exact where alpha == 1 and |sum| < 2^24.  Three instructions per
+// value: a wavefront pays this whenever one of its 32 rows gets a new max.
+template <int D>
+__device__ __forceinline__ void rescale_i32(v16f (&o)[D / 32], float alpha) {
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+      v16i x = __builtin_bit_cast(v16i, o[cb]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int xi = x[r];   // element to a scalar first (see softmax_tile)
+        x[r] = round_half_up_i32((float)xi * alpha);
+      }
+      o[cb] = __builtin_bit_cast(v16f, x);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The steady-state step as an explicit instruction schedule.
 //
@@ -530,13 +576,15 @@ __device__ __forceinline__ void rescale(v16f (&o)[D / 32], float alpha) {
 // micro-ops, and slots are separated by scheduling barriers.  Each wavefront
 // thus alternates MFMA and VALU issue, keeping both units busy.  The order
 // only affects timing: the arithmetic is the same as softmax_tile/qk_tile/
-// pv_tile (unmasked tiles only).
+// pv_tile (unmasked tiles only).  INT8 P~V runs here only with O kept as the
+// INT32 sum (pv_tile's ACC form): two MFMAs per channel block, the 32-key
+// halves, issued for all blocks' first halves before any second half.
 template <int D, int PV>
 struct StepPlan {
   static constexpr int TD = D / 32;                              // d-steps per QK block
   static constexpr int NCB = D / 32;                             // output channel blocks
   static constexpr int NQK = 2 * TD;
-  static constexpr int NPV = PV == kPvFp16 ? 4 * NCB : NCB;
+  static constexpr int NPV = PV == kPvFp16 ? 4 * NCB : PV == kPvInt8 ? 2 * NCB : NCB;
   static constexpr int NM = NQK + NPV;                           // MFMA slots
   // slot k issues a P~V MFMA iff the running PV quota steps up at k
   static constexpr bool is_pv(int k) { return ((k + 1) * NPV) / NM > (k * NPV) / NM; }
@@ -545,7 +593,7 @@ struct StepPlan {
     for (int i = 0; i < k; ++i) c += is_pv(i) == is_pv(k);
     return c;
   }
-  // softmax micro-ops: NPRE maxima with the conversions (FP8 only: FP16
+  // softmax micro-ops: NPRE maxima with the conversions (FP8, INT8: FP16
   // steady-state tiles skip the max), one combine, then the exps and packs,
   // then the finish
   static constexpr int NPRE = PV == kPvFp16 ? 0 : 48;
@@ -584,7 +632,7 @@ struct StepPlan {
 };
 
 template <int D, int PV>
-using OpReg = std::conditional_t<PV == kPvFp16, v4i, v8i>;
+using OpReg = std::conditional_t<PV == kPvFp8, v8i, v4i>;
 
 template <int D, int PV, bool SQ>
 __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D / 32],
@@ -607,7 +655,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
     if constexpr (!Plan::is_pv(K)) {
       constexpr int blk = i % 2, t = i / 2;
       const v4i a = *reinterpret_cast<const v4i*>(kb + KTile<D>::lds_off(32 * blk + n, 2 * t + hh));
-      if constexpr (PV == kPvFp16) r = a;
+      if constexpr (PV != kPvFp8) r = a;
       else r = Op{a[0], a[1], a[2], a[3], 0, 0, 0, 0};
       if constexpr (SQ && t == 0) cin[blk] = sq_init<D>(kb, blk, hh);
     } else if constexpr (PV == kPvFp16) {
@@ -615,6 +663,10 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
       const int row = 32 * cb + n;
       r = *reinterpret_cast<const v4i*>(vb + row * 128 +
                                         (((2 * S + hh) ^ row_swizzle<128>(row)) << 4));
+    } else if constexpr (PV == kPvInt8) {
+      constexpr int cb = i % Plan::NCB, half = i / Plan::NCB;
+      const int row = 32 * cb + n;
+      r = *reinterpret_cast<const v4i*>(vb + row * 64 + (((2 * hh + half) ^ row_swizzle<64>(row)) << 4));
     } else {
       constexpr int cb = i;
       const int row = 32 * cb + n;
@@ -630,7 +682,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
     if constexpr (!Plan::is_pv(K)) {
       constexpr int blk = i % 2, t = i / 2;
       v4i a;
-      if constexpr (PV == kPvFp16) a = r;
+      if constexpr (PV != kPvFp8) a = r;
       else a = v4i{r[0], r[1], r[2], r[3]};
       s_new[blk] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
           a, qf[t], t == 0 ? (SQ ? cin[blk] : init) : s_new[blk], 0, 0, 0);
@@ -639,6 +691,13 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
       o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, r),
                                                      __builtin_bit_cast(v8h, p_cur.w[S]), o[cb],
                                                      0, 0, 0);
+    } else if constexpr (PV == kPvInt8) {
+      constexpr int cb = i % Plan::NCB, half = i / Plan::NCB;
+      const v4i pb = half ? v4i{p_cur.w[4], p_cur.w[5], p_cur.w[6], p_cur.w[7]}
+                          : v4i{p_cur.w[0], p_cur.w[1], p_cur.w[2], p_cur.w[3]};
+      o[cb] = __builtin_bit_cast(
+          v16f, __builtin_amdgcn_mfma_i32_32x32x32_i8(r, pb, __builtin_bit_cast(v16i, o[cb]), 0,
+                                                      0, 0));
     } else {
       constexpr int cb = i;
       // scale operands 127 = E8M0 exponent of 1.0 (no block scaling)
@@ -657,7 +716,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
   auto sc = [&](int i) __attribute__((always_inline)) -> int { return s_cur[i >> 4][i & 15]; };
   auto uop = [&]<int U>() __attribute__((always_inline)) {
     if constexpr (U < NPRE) {
-      // FP8 only: triples of (max of two scores into one of 4 partial
+      // FP8, INT8: triples of (max of two scores into one of 4 partial
       // maxima, two conversions)
       constexpr int g = U / 3, r = U % 3;
       if constexpr (r == 0) {
@@ -677,7 +736,12 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
         mx = pair_max_i32(mx);
         const float mt = (float)mx * ts.c;
         m_new = fmaxf(m_run, mt);
-        nb = kLog2_448 - m_new;
+        nb = (PV == kPvInt8 ? kLog2_127 : kLog2_448) - m_new;
+        if constexpr (PV == kPvInt8) {
+          // the row's largest 127 P~ rounds to at most 127 (see softmax_tile)
+          const float tmax = __builtin_fmaf((float)mx, ts.c, nb);
+          nb -= fmaxf(tmax - kLog2_127, 0.f);
+        }
         alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       }
     } else if constexpr (U < NPRE + 1 + 32 + Plan::NPACK) {
@@ -701,7 +765,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
           lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, pk), one, lsum, false);
         }
       } else {
-        // FP8: exp of score i, and after every 4 scores their pack
+        // FP8, INT8: exp of score i, and after every 4 scores their pack
         constexpr int v = U - NPRE - 1;
         constexpr int grp = v / 5, pos = v % 5;   // 4 exps + pack
         if constexpr (pos < 4) {
@@ -710,7 +774,9 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
           ls[i & 3] += e[i];
         } else {
           constexpr int w = grp;
-          uint32_t pk = pack_fp8x4(e[4 * w], e[4 * w + 1], e[4 * w + 2], e[4 * w + 3]);
+          uint32_t pk = PV == kPvFp8
+                            ? pack_fp8x4(e[4 * w], e[4 * w + 1], e[4 * w + 2], e[4 * w + 3])
+                            : pack_u8x4(e[4 * w], e[4 * w + 1], e[4 * w + 2], e[4 * w + 3]);
           asm volatile("" : "+v"(pk));
           p_new.w[w] = (int)pk;
         }
@@ -752,6 +818,8 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
     } else {
       l_run = lsum;
     }
+  } else if constexpr (PV == kPvInt8) {
+    rescale_i32<D>(o, alpha);
   } else {
     rescale<D>(o, alpha);
   }
@@ -768,8 +836,8 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
 // in FP16 mode, so K^(j+1) is still there if step j must recompute S(j+1);
 // one barrier per step).  All wavefronts run every step of the workgroup; a
 // causal tile beyond a wavefront's last row is fully masked and changes
-// nothing.
-template <int D, int PV, int OUT, bool CAUSAL, bool SQ>
+// nothing.  ACC (INT8 P~V only): O is the INT32 sum of the tiles' P^ V^.
+template <int D, int PV, int OUT, bool CAUSAL, bool SQ, bool ACC>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__ k_i8,
                      const uint8_t* __restrict__ v_t, const float* __restrict__ q_scale,
@@ -875,9 +943,12 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   for (int cb = 0; cb < NCB; ++cb) o[cb] = v16f{};
   v16i sA[2], sB[2];
   PTile<PV> pA, pB;
-  // INT8: the rescale factor of the tile whose P^ V^ comes next, applied in
-  // the same fused multiply-add that adds the product
+  // INT8 outside the fused steps: the rescale factor of the tile whose P^ V^
+  // comes next, applied in the same fused multiply-add that adds the product,
+  // or (ACC) to the INT32 sums just before the product's MFMAs (the fused
+  // steps rescale at their end and leave it at 1)
   float alpha_pend = 1.f;
+  static_assert(!ACC || PV == kPvInt8, "INT32 accumulation is for INT8 P~V only");
 
   // Masks of the tiles that need one.  Causal: the two tiles on the diagonal
   // of query block qb (2 qb + dd, dd = 0, 1) show key 64 dd + off of the tile
@@ -946,7 +1017,6 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     __syncthreads();
   };
   int j = 0;
-  // INT8 P~V runs every step through the generic path below
   if constexpr (NKS == 3) {
     // six steps per trip: with j a multiple of 6 every K^ slot (t % 3) is a
     // constant, so all LDS addresses are immediates
@@ -959,15 +1029,16 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
       steady.template operator()<5>(j + 5, 2, 1, 0);
     }
   }
-  if constexpr (PV != kPvInt8) {
+  if constexpr (PV != kPvInt8 || ACC) {
     for (; j + 4 < nt && j + 2 < nt_full; j += 2) {
       steady.template operator()<0>(j, kslot(j + 3, 3), kslot(j + 2, 2), kslot(j + 1, 1));
       steady.template operator()<1>(j + 1, kslot(j + 4, 4), kslot(j + 3, 3), kslot(j + 2, 2));
     }
   } else {
-    // INT8: the same unmasked steps with every load and MFMA present, in
-    // source order (P^ V^(jj), S(jj+2), softmax(S(jj+1))), the rescale of each
-    // tile folded into the next tile's product
+    // INT8 with O converted per tile: the same unmasked steps with every load
+    // and MFMA present, in source order (P^ V^(jj), softmax(S(jj+1)), S(jj+2)),
+    // so that the two score tiles and the tile's INT32 product are never live
+    // together
     auto plain = [&]<int U>(int jj) __attribute__((always_inline)) {
       issue_k.template operator()<false>(jj + 3, kl0 + ((U + 3) & 1) * KB);
       VL::issue(vrs, jj + 1, vl[1 - U], wave, lane);
@@ -1006,7 +1077,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
         if constexpr (PV == kPvInt8) {
           // P^ V^, softmax, then the next scores: the two score tiles are
           // never live at once (the INT32 product needs the registers)
-          pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh, alpha_pend);
+          if constexpr (ACC) rescale_i32<D>(o, alpha_pend);
+          pv_tile<D, PV, ACC>(o, p_cur, vbuf[u], n, hh, alpha_pend);
           if (jj + 1 < nt) alpha_pend = softmax_any(s_cur, p_new, jj + 1);
           if (jj + 2 < nt) qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init);
         } else {
@@ -1036,7 +1108,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
         float y[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          y[u] = o[cb][4 * j4 + u] * inv;
+          const float ou = o[cb][4 * j4 + u];   // element to a scalar first
+          y[u] = (ACC ? (float)__builtin_bit_cast(int, ou) : ou) * inv;
           if constexpr (PV != kPvFp16) y[u] *= v_scale[(size_t)bh * D + c0 + u];
         }
         store4<OUT>(out, orow + c0, y[0], y[1], y[2], y[3]);
@@ -1079,6 +1152,12 @@ __global__ __launch_bounds__(64) void debug_s_kernel(const int8_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// INT8 P~V keeps O as an INT32 sum of the tiles' products for heads of up to
+// 2^17 keys: one 64-key tile adds at most 64 * 127^2 = 1032256 in magnitude
+// (|P^| <= 127, |V^| <= 127), 2048 tiles at most 2114060288, and each rescale
+// (alpha <= 1) rounds by at most 0.5 + 2^-24 |sum|, so the sum stays below 2^31.
+constexpr int kInt8AccMaxKeys = 1 << 17;
+
 template <int D, int PV, int OUT, bool CAUSAL, bool SQ>
 static hipError_t attn_dispatch(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
                                 const float* q_scale, const float* k_scale,
@@ -1089,7 +1168,15 @@ static hipError_t attn_dispatch(const int8_t* q_i8, const int8_t* k_i8, const ui
   const int BH = B * H;
   const long long grid = (long long)BH * nqb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ><<<dim3((unsigned)grid), 256, 0, s>>>(
+  if constexpr (PV == kPvInt8) {
+    if (N <= kInt8AccMaxKeys) {
+      attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ, true><<<dim3((unsigned)grid), 256, 0, s>>>(
+          q_i8, k_i8, v_t, q_scale, k_scale, v_scale, comp, BH, N, nqb, ntiles, CAUSAL ? 0 : 1,
+          H, nhd, out);
+      return hipGetLastError();
+    }
+  }
+  attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ, false><<<dim3((unsigned)grid), 256, 0, s>>>(
       q_i8, k_i8, v_t, q_scale, k_scale, v_scale, comp, BH, N, nqb, ntiles, CAUSAL ? 0 : 1, H,
       nhd, out);
   return hipGetLastError();

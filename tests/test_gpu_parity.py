@@ -311,6 +311,34 @@ def test_table7_shapes(name):
 
 
 # ---------------------------------------------------------------------------
+# INT8 P~V keeps O as an INT32 sum of the tiles' P^ V^ for heads of up to 2^17
+# keys and converts each tile's product to float beyond.  Q = 0 makes every
+# score equal, so every P^ is 127; V constant per channel makes every V^ +-127.
+# At 2^17 keys each INT32 sum is then +-2^17 127^2 = +-2114060288, the bound
+# the kernel relies on, and O must be V itself (closed form).
+@pytest.mark.parametrize("N,d,causal", [(1 << 17, 128, False), (1 << 17, 64, True),
+                                        ((1 << 17) + 1, 128, False)],
+                         ids=["acc_bound_d128", "acc_bound_d64c", "above_bound_d128"])
+def test_int8_accumulator_bound(N, d, causal):
+    note(f"int8 accumulator bound N={N} d={d} causal={causal}")
+    g = torch.Generator().manual_seed(N + d)
+    q = torch.zeros(1, 1, N, d, dtype=torch.float16)
+    k = torch.randn(1, 1, N, d, generator=g).to(torch.float16)
+    col = (torch.rand(d, generator=g) * 4 + 0.5) * torch.where(torch.arange(d) % 2 == 0, 1.0, -1.0)
+    v = col.to(torch.float16).expand(1, 1, N, d).contiguous()
+    o = qa().sage_attn(q.cuda(), k.cuda(), v.cuda(), causal=causal, pv_mode="int8", out_f32=True)
+    torch.cuda.synchronize()
+    ref = col.to(torch.float16).double().numpy()
+    err = np.abs(to_np(o)[0, 0] - ref[None, :])
+    note(f"  max |O - V| = {err.max():.3e}")
+    # INT32 sums: only the final conversions and the float32 row sum round.
+    # Beyond 2^17 keys each of the N/64 tile products is added to a float32 O
+    # of up to 2^31 units, each addition rounding by half an ulp (2^-24 rel).
+    rel = 1e-5 if N <= (1 << 17) else 1e-5 + (N / 64) * 2.0 ** -24
+    assert err.max() <= rel * np.abs(ref).max()
+
+
+# ---------------------------------------------------------------------------
 # Maximum sizes: one head of about a million tokens (K^ tile index up to
 # 16384, a V' head of 256 MiB), ragged, in both P~V modes.
 @pytest.mark.parametrize("wl", [
