@@ -252,7 +252,7 @@ def sample_rows(N, causal, seed):
     return np.array(sorted(r for r in rows if 0 <= r < N))
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c3i8", "c4i8"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c3i8", "c4i8", "c3_shard8"])
 def test_full_workload(name):
     wl = named(name)
     note(f"full workload {name}: {wl}")
