@@ -837,8 +837,12 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
 // one barrier per step).  All wavefronts run every step of the workgroup; a
 // causal tile beyond a wavefront's last row is fully masked and changes
 // nothing.  ACC (INT8 P~V only): O is the INT32 sum of the tiles' P^ V^.
-template <int D, int PV, int OUT, bool CAUSAL, bool SQ, bool ACC>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+// NW wavefronts per workgroup (32 query rows each): 4, one delta_Q block, or
+// 8 (two blocks; FP16 P~V, d = 128, non-causal, Q not smoothed), where every
+// K^ and V tile copied into LDS serves twice the rows.
+template <int D, int PV, int OUT, bool CAUSAL, bool SQ, bool ACC, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
+                          amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__ k_i8,
                      const uint8_t* __restrict__ v_t, const float* __restrict__ q_scale,
                      const float* __restrict__ k_scale, const float* __restrict__ v_scale,
@@ -849,6 +853,9 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   constexpr int VB = VTile<D, PV>::BYTES;
   constexpr int NCB = D / 32;   // 32-channel blocks of the output
   constexpr int NKS = kKSlots<PV>;
+  static_assert(NW == 4 || (NW == 8 && PV == kPvFp16 && D == 128 && !CAUSAL && !SQ),
+                "8-wavefront workgroups: FP16 P~V, d = 128, non-causal, Q not smoothed");
+  constexpr int BQW = kWaveQ * NW;   // query rows per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[NKS][KB];
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][VB];
 
@@ -875,7 +882,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   const int lane = tid & 63;
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int qrow = qb * kBlockQ + wave * kWaveQ + n;   // this lane's query row
+  const int qrow = qb * BQW + wave * kWaveQ + n;   // this lane's query row
 
   const int8_t* q_bh = q_i8 + (size_t)bh * N * D;
   const int8_t* k_bh = k_i8 + (size_t)bh * N * D;
@@ -884,7 +891,10 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
 
   v4i qf[D / 32];
   load_q_frag<D>(qf, q_bh, qrow, N, hh);
-  const float cq = q_scale[(size_t)bh * nqb + qb] * kLog2e;
+  // delta_Q of this wavefront's 128-row block (rows past N: the last block)
+  const int nq128 = (N + kQBlock - 1) / kQBlock;
+  const int qblk = min((qb * BQW + wave * kWaveQ) / kQBlock, nq128 - 1);
+  const float cq = q_scale[(size_t)bh * nq128 + qblk] * kLog2e;
 
   // FP16 mode: the accumulator start value (magic bias) and the grid of the
   // running max, twice the float spacing at the largest K0 of the head.
@@ -905,12 +915,12 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
 
   // Tiles of the workgroup; tiles [0, nt_full) need no mask for any row, the
   // rest (ragged tail, causal diagonal) run the masked softmax.
-  const int kv_end = CAUSAL ? min(N, (qb + 1) * kBlockQ) : N;
+  const int kv_end = CAUSAL ? min(N, (qb + 1) * BQW) : N;
   const int nt = (kv_end + kKvTile - 1) / kKvTile;
   const int nt_full = CAUSAL ? min(2 * qb, N / kKvTile) : N / kKvTile;
 
-  const KLoader<D, kWaves> kld(wave, lane);
-  using VL = VLoader<D, PV, kWaves>;
+  const KLoader<D, NW> kld(wave, lane);
+  using VL = VLoader<D, PV, NW>;
   const v4i krs = buffer_rsrc(k_bh, N * D);
   const v4i vrs = buffer_rsrc(v_bh, ntiles * VB);
   // SQ: this block's row of compensation values, ntiles * 64 INT32
@@ -1158,25 +1168,30 @@ __global__ __launch_bounds__(64) void debug_s_kernel(const int8_t* __restrict__ 
 // (alpha <= 1) rounds by at most 0.5 + 2^-24 |sum|, so the sum stays below 2^31.
 constexpr int kInt8AccMaxKeys = 1 << 17;
 
+// 8-wavefront workgroups halve the K^/V copies into LDS per query row (on c3
+// the copies cost about a tenth of the kernel).  They pay off in FP16 mode,
+// whose steps rarely rescale; with the exact max of FP8 and INT8 P~V the
+// rescales of single wavefronts hold all eight at each step's barrier.
 template <int D, int PV, int OUT, bool CAUSAL, bool SQ>
 static hipError_t attn_dispatch(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
                                 const float* q_scale, const float* k_scale,
                                 const float* v_scale, const int32_t* comp, int B, int H, int N,
                                 int nhd, void* out, hipStream_t s) {
-  const int nqb = ceil_div(N, kBlockQ);
+  constexpr int NW = PV == kPvFp16 && D == 128 && !CAUSAL && !SQ ? 8 : 4;
+  const int nqb = ceil_div(N, kWaveQ * NW);
   const int ntiles = ceil_div(N, kKvTile);
   const int BH = B * H;
   const long long grid = (long long)BH * nqb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if constexpr (PV == kPvInt8) {
     if (N <= kInt8AccMaxKeys) {
-      attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ, true><<<dim3((unsigned)grid), 256, 0, s>>>(
+      attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ, true, NW><<<dim3((unsigned)grid), 64 * NW, 0, s>>>(
           q_i8, k_i8, v_t, q_scale, k_scale, v_scale, comp, BH, N, nqb, ntiles, CAUSAL ? 0 : 1,
           H, nhd, out);
       return hipGetLastError();
     }
   }
-  attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ, false><<<dim3((unsigned)grid), 256, 0, s>>>(
+  attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ, false, NW><<<dim3((unsigned)grid), 64 * NW, 0, s>>>(
       q_i8, k_i8, v_t, q_scale, k_scale, v_scale, comp, BH, N, nqb, ntiles, CAUSAL ? 0 : 1, H,
       nhd, out);
   return hipGetLastError();
