@@ -269,13 +269,15 @@ __device__ __forceinline__ uint32_t pack_u8x4(float a, float b, float c, float d
 }
 
 // Smoothed Q: the compensation values of a tile follow its K^ in the LDS
-// slot (64 INT32, already carrying FP16 mode's magic bias).  The start value
-// of 32-key block blk in the accumulator layout: register r holds key
-// 32 blk + 8 (r/4) + 4 hh + r%4.
+// slot (64 INT32 per 128-row query block of the workgroup, already carrying
+// FP16 mode's magic bias); sqo is the byte offset of the wavefront's block's
+// values.  The start value of 32-key block blk in the accumulator layout:
+// register r holds key 32 blk + 8 (r/4) + 4 hh + r%4.
 constexpr int kSqTileBytes = kKvTile * 4;
 template <int D>
-__device__ __forceinline__ v16i sq_init(const uint8_t* kb, int blk, int hh) {
-  const int32_t* c = reinterpret_cast<const int32_t*>(kb + KTile<D>::BYTES) + 32 * blk + 4 * hh;
+__device__ __forceinline__ v16i sq_init(const uint8_t* kb, int blk, int hh, int sqo) {
+  const int32_t* c =
+      reinterpret_cast<const int32_t*>(kb + KTile<D>::BYTES + sqo) + 32 * blk + 4 * hh;
   v16i r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -288,9 +290,10 @@ __device__ __forceinline__ v16i sq_init(const uint8_t* kb, int blk, int hh) {
 // S^T = K^ Q^T for one 64-key tile: two 32x32 INT32 blocks.
 template <int D, bool SQ>
 __device__ __forceinline__ void qk_tile(v16i (&s)[2], const v4i (&qf)[D / 32], const uint8_t* kb,
-                                        int n, int hh, const v16i& init) {
-  s[0] = qk_block<D>(qf, kb, 0, n, hh, SQ ? sq_init<D>(kb, 0, hh) : init);
-  s[1] = qk_block<D>(qf, kb, 1, n, hh, SQ ? sq_init<D>(kb, 1, hh) : init);
+                                        int n, int hh, const v16i& init,
+                                        int sqo) {
+  s[0] = qk_block<D>(qf, kb, 0, n, hh, SQ ? sq_init<D>(kb, 0, hh, sqo) : init);
+  s[1] = qk_block<D>(qf, kb, 1, n, hh, SQ ? sq_init<D>(kb, 1, hh, sqo) : init);
 }
 
 // FP16 mode converts scores to float without an instruction: the INT32
@@ -641,7 +644,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
                                             const uint8_t* kb, const uint8_t* kb_prev,
                                             const uint8_t* vb, float& m_run,
                                             float& l_run, TileScale ts, MaxGrid grid,
-                                            const v16i& init, int n, int hh) {
+                                            const v16i& init, int n, int hh, int sqo) {
   using Plan = StepPlan<D, PV>;
   using Op = OpReg<D, PV>;
   constexpr int LA = 2;   // operand read lookahead (slots)
@@ -657,7 +660,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
       const v4i a = *reinterpret_cast<const v4i*>(kb + KTile<D>::lds_off(32 * blk + n, 2 * t + hh));
       if constexpr (PV != kPvFp8) r = a;
       else r = Op{a[0], a[1], a[2], a[3], 0, 0, 0, 0};
-      if constexpr (SQ && t == 0) cin[blk] = sq_init<D>(kb, blk, hh);
+      if constexpr (SQ && t == 0) cin[blk] = sq_init<D>(kb, blk, hh, sqo);
     } else if constexpr (PV == kPvFp16) {
       constexpr int S = i / Plan::NCB, cb = i % Plan::NCB;
       const int row = 32 * cb + n;
@@ -813,7 +816,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
     if (__builtin_amdgcn_ballot_w64(!(lsum - l_run <= kOptimisticSum))) {
       // rare: recompute the tile's scores (into the registers they came in,
       // free by now) and take the max-based rule
-      qk_tile<D, SQ>(s_cur, qf, kb_prev, n, hh, init);
+      qk_tile<D, SQ>(s_cur, qf, kb_prev, n, hh, init, sqo);
       rescale<D>(o, softmax_tile<PV, false>(s_cur, m_run, l_run, p_new, ts, grid, ~0u, hh));
     } else {
       l_run = lsum;
@@ -838,8 +841,8 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
 // causal tile beyond a wavefront's last row is fully masked and changes
 // nothing.  ACC (INT8 P~V only): O is the INT32 sum of the tiles' P^ V^.
 // NW wavefronts per workgroup (32 query rows each): 4, one delta_Q block, or
-// 8 (two blocks; FP16 P~V, d = 128, non-causal, Q not smoothed), where every
-// K^ and V tile copied into LDS serves twice the rows.
+// 8 (two blocks; FP16 P~V, d = 128, non-causal), where every K^ and V tile
+// copied into LDS serves twice the rows.
 template <int D, int PV, int OUT, bool CAUSAL, bool SQ, bool ACC, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu(2, 2)))
@@ -849,12 +852,12 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
                      const int32_t* __restrict__ comp, int BH, int N, int nqb, int ntiles,
                      int xcd_remap, int H, int nhd, void* __restrict__ out) {
   // K^ slot: the tile, then (SQ) its 64 compensation values
-  constexpr int KB = KTile<D>::BYTES + (SQ ? kSqTileBytes : 0);
+  constexpr int KB = KTile<D>::BYTES + (SQ ? kSqTileBytes * (NW / 4) : 0);
   constexpr int VB = VTile<D, PV>::BYTES;
   constexpr int NCB = D / 32;   // 32-channel blocks of the output
   constexpr int NKS = kKSlots<PV>;
-  static_assert(NW == 4 || (NW == 8 && PV == kPvFp16 && D == 128 && !CAUSAL && !SQ),
-                "8-wavefront workgroups: FP16 P~V, d = 128, non-causal, Q not smoothed");
+  static_assert(NW == 4 || (NW == 8 && PV == kPvFp16 && D == 128 && !CAUSAL),
+                "8-wavefront workgroups: FP16 P~V, d = 128, non-causal");
   constexpr int BQW = kWaveQ * NW;   // query rows per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[NKS][KB];
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][VB];
@@ -923,17 +926,20 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   using VL = VLoader<D, PV, NW>;
   const v4i krs = buffer_rsrc(k_bh, N * D);
   const v4i vrs = buffer_rsrc(v_bh, ntiles * VB);
-  // SQ: this block's row of compensation values, ntiles * 64 INT32
+  // SQ: the row of compensation values of this wavefront's 128-row block,
+  // ntiles * 64 INT32, and their place in each K^ slot
   v4i crs = {0, 0, 0, 0};
-  if constexpr (SQ) crs = buffer_rsrc(comp + ((size_t)bh * nqb + qb) * ntiles * kKvTile,
+  if constexpr (SQ) crs = buffer_rsrc(comp + ((size_t)bh * nq128 + qblk) * ntiles * kKvTile,
                                       ntiles * kSqTileBytes);
-  // K^ tile `tile` into the slot at LDS address `dst`, with (SQ) its
-  // compensation values behind it (wavefront 0, lanes 0..15, 16 bytes each)
+  const int sqo = (wave / 4) * kSqTileBytes;
+  // K^ tile `tile` into the slot at LDS address `dst`, with (SQ) the
+  // compensation values of each 128-row block behind it (wavefronts 0 and 4,
+  // lanes 0..15, 16 bytes each)
   auto issue_k = [&]<bool CLAMP>(int tile, uint32_t dst) __attribute__((always_inline)) {
     kld.template issue<CLAMP>(krs, tile * kKvTile, N, dst, wave);
     if constexpr (SQ) {
-      if (wave == 0 && lane < 16) {
-        const uint32_t m0[1] = {dst + KTile<D>::BYTES};
+      if (wave % 4 == 0 && lane < 16) {
+        const uint32_t m0[1] = {dst + KTile<D>::BYTES + sqo};
         const int vo[1] = {lane * 16};
         lds_copy_x4<1>(crs, tile * kSqTileBytes, m0, vo);
       }
@@ -991,8 +997,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   if (nt > 1) issue_k.template operator()<true>(1, kl0 + KB);
   wait_lds_loads();
   __syncthreads();
-  qk_tile<D, SQ>(sA, qf, kbuf[0], n, hh, init);
-  if (nt > 1) qk_tile<D, SQ>(sB, qf, kbuf[1], n, hh, init);
+  qk_tile<D, SQ>(sA, qf, kbuf[0], n, hh, init, sqo);
+  if (nt > 1) qk_tile<D, SQ>(sB, qf, kbuf[1], n, hh, init, sqo);
   softmax_any(sA, pA, 0);   // alpha irrelevant: O is still zero
   __syncthreads();          // every wave has read K^(0)
   if (nt > 2) issue_k.template operator()<true>(2, kl0 + kslot(2, 2) * KB);
@@ -1021,7 +1027,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     // step); in FP8 mode it is zero, an inline constant
     if constexpr (PV == kPvFp16 && !SQ) asm volatile("" : "+v"(init));
     fused_step<D, PV, SQ>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[sr], kbuf[sp], vbuf[U & 1], m_run,
-                      l_run, tile_scale<PV>(cq, dk), grid, init, n, hh);
+                      l_run, tile_scale<PV>(cq, dk), grid, init, n, hh, sqo);
     asm volatile("" ::"s"(dk_next));
     wait_lds_loads();
     __syncthreads();
@@ -1061,7 +1067,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
       pv_tile<D, PV>(o, p_cur, vbuf[U], n, hh, alpha_pend);
       alpha_pend = softmax_tile<PV, false>(s_cur, m_run, l_run, p_new, tile_scale<PV>(cq, dk),
                                            grid, ~0u, hh);
-      qk_tile<D, SQ>(s_new, qf, kbuf[U], n, hh, init);
+      qk_tile<D, SQ>(s_new, qf, kbuf[U], n, hh, init, sqo);
       asm volatile("" ::"s"(dk_next));
       wait_lds_loads();
       __syncthreads();
@@ -1090,9 +1096,9 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
           if constexpr (ACC) rescale_i32<D>(o, alpha_pend);
           pv_tile<D, PV, ACC>(o, p_cur, vbuf[u], n, hh, alpha_pend);
           if (jj + 1 < nt) alpha_pend = softmax_any(s_cur, p_new, jj + 1);
-          if (jj + 2 < nt) qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init);
+          if (jj + 2 < nt) qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init, sqo);
         } else {
-          if (jj + 2 < nt) qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init);
+          if (jj + 2 < nt) qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init, sqo);
           pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh, alpha_pend);
           if (jj + 1 < nt) rescale<D>(o, softmax_any(s_cur, p_new, jj + 1));
         }
@@ -1171,13 +1177,14 @@ constexpr int kInt8AccMaxKeys = 1 << 17;
 // 8-wavefront workgroups halve the K^/V copies into LDS per query row (on c3
 // the copies cost about a tenth of the kernel).  They pay off in FP16 mode,
 // whose steps rarely rescale; with the exact max of FP8 and INT8 P~V the
-// rescales of single wavefronts hold all eight at each step's barrier.
+// rescales of single wavefronts hold all eight at each step's barrier.  With
+// Q smoothed each K^ slot carries the compensation values of both blocks.
 template <int D, int PV, int OUT, bool CAUSAL, bool SQ>
 static hipError_t attn_dispatch(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
                                 const float* q_scale, const float* k_scale,
                                 const float* v_scale, const int32_t* comp, int B, int H, int N,
                                 int nhd, void* out, hipStream_t s) {
-  constexpr int NW = PV == kPvFp16 && D == 128 && !CAUSAL && !SQ ? 8 : 4;
+  constexpr int NW = PV == kPvFp16 && D == 128 && !CAUSAL ? 8 : 4;
   const int nqb = ceil_div(N, kWaveQ * NW);
   const int ntiles = ceil_div(N, kKvTile);
   const int BH = B * H;
