@@ -51,6 +51,9 @@ def gpu_inputs(inp):
 # ---------------------------------------------------------------------------
 SMALL = [
     small("s1", N=1, d=64), small("s63", N=63, d=128, causal=True),
+    # FP16 P~V at d = 128, non-causal, runs 256-row workgroups of 8
+    # wavefronts: one row, and one row past the first delta_Q block
+    small("s1w", N=1, d=128), small("s129", N=129, d=128, dtype="bf16"),
     small("s65", N=65, d=64, dtype="bf16"), small("s197", N=197, d=64, pv_mode="fp8"),
     small("s300c", N=300, d=128, causal=True, dtype="bf16", pv_mode="fp8"),
     small("s1105", N=1105, d=64, H=1, causal=True, extras="kchan20"),
