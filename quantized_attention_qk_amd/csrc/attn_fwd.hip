@@ -17,7 +17,8 @@
 // INT32 could overflow, convert each tile's product to float instead.
 //
 // MI355X mapping
-// * Workgroup = 4 wavefronts = 128 query rows = one delta_Q block of one (b, h).
+// * Workgroup = 4 wavefronts = 128 query rows = one delta_Q block of one (b, h)
+//   (FP16 P~V, non-causal, d = 128: 8 wavefronts, two blocks, sharing tiles).
 //   Each wavefront owns 32 query rows for the whole KV walk.
 // * Scores are computed transposed, S^T = K^ Q^T, with v_mfma_i32_32x32x32_i8:
 //   in the 32x32 accumulator lane l holds query l%32 and keys
@@ -828,7 +829,7 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
   }
 }
 
-// Software pipeline over the KV tiles of one workgroup (4 wavefronts), two
+// Software pipeline over the KV tiles of one workgroup (NW wavefronts), two
 // tiles deep.  Entering step j a wavefront holds P~(j) (MFMA operand) and the
 // INT32 scores S(j+1); step j issues
 //     S(j+2) = K^(j+2) Q^T          [INT8 MFMA]

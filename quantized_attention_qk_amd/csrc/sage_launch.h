@@ -15,9 +15,7 @@ constexpr int kKBlock = 64;      // tokens per delta_K block
 constexpr int kKvTile = 64;      // keys per online-softmax step
 constexpr int kMeanChunk = 256;  // tokens per float32 partial column sum
 constexpr int kWaveQ = 32;       // query rows per wavefront (one 32x32 MFMA column block)
-constexpr int kWaves = 4;        // wavefronts per attention workgroup
-constexpr int kBlockQ = kWaveQ * kWaves;   // 128 query rows per workgroup
-static_assert(kBlockQ == kQBlock, "a workgroup covers exactly one delta_Q block");
+static_assert(kQBlock % kWaveQ == 0, "a delta_Q block is whole wavefronts of rows");
 static_assert(kKvTile == kKBlock, "one delta_K per KV tile");
 
 constexpr int kPvFp16 = 0;
