@@ -7,8 +7,10 @@ others fall back to the more precise one.  The page's faster kernel is the
 all-INT8 one (INT8 P~V), its precise one keeps P~V in FP16; candidates=
 ("int8",) reproduces that choice.  On gfx950 the default fast candidate is
 FP8 E4M3 P~V: the FP8 MFMA runs at the INT8 rate with a float32 accumulator,
-so it needs no per-tile conversion of an INT32 product and is the faster of
-the two.  Several candidates are tried in the order given (fastest first).
+whose rescale at a new row max is one multiply per value, against three
+instructions per value for the INT32 sum of INT8 P~V; FP8 is the faster of
+the two at both head sizes.  Several candidates are tried in the order given
+(fastest first).
 
 Every number is computed on the GPU: the candidate kernel's float32 output
 and a float32 full-precision reference (sage_attn_ref_rows_f32) on a seeded
