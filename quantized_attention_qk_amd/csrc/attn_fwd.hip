@@ -992,19 +992,24 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
                        : softmax_tile<PV, true>(sc, m_run, l_run, pn, ts, grid, tile_keep(t), hh);
   };
 
-  // Prologue: S(0), S(1), P~(0); then K^(2) into the slot of K^(0).
+  // Prologue: S(0), S(1), P~(0).  K^(2) goes to its own third slot with the
+  // first copies (FP16 mode), or into the slot of K^(0) once every wavefront
+  // has read it (two slots).
   issue_k.template operator()<true>(0, kl0);
   VL::issue(vrs, 0, vl[0], wave, lane);
   if (nt > 1) issue_k.template operator()<true>(1, kl0 + KB);
+  if (NKS == 3 && nt > 2) issue_k.template operator()<true>(2, kl0 + 2 * KB);
   wait_lds_loads();
   __syncthreads();
   qk_tile<D, SQ>(sA, qf, kbuf[0], n, hh, init, sqo);
   if (nt > 1) qk_tile<D, SQ>(sB, qf, kbuf[1], n, hh, init, sqo);
   softmax_any(sA, pA, 0);   // alpha irrelevant: O is still zero
   __syncthreads();          // every wave has read K^(0)
-  if (nt > 2) issue_k.template operator()<true>(2, kl0 + kslot(2, 2) * KB);
-  wait_lds_loads();
-  __syncthreads();
+  if (NKS == 2) {
+    if (nt > 2) issue_k.template operator()<true>(2, kl0 + kslot(2, 2) * KB);
+    wait_lds_loads();
+    __syncthreads();
+  }
 
   // Steady state: no masking, every load and MFMA present.  Step jj writes
   // K^(jj+3) and V(jj+1) into the slots read before it (K^ slot sw, V slot
