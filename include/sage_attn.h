@@ -91,8 +91,11 @@ size_t sage_attn_workspace_bytes(int B, int H, int N, int d, int pv_mode);
  *      pv_mode SAGE_PV_INT8: O = alpha O + (P^ V^_j as INT32) with P^ =
  *      rne(127 P~) in [0, 127] (static delta_P = 1/127, [SA] §7 key
  *      implementation details) and V^ = clamp(rne(V * 127/colmax|V|), -127,
- *      127), delta_V = colmax|V|/127 per channel; each tile's INT32 product is
- *      converted to float32 (exactly) and added
+ *      127), delta_V = colmax|V|/127 per channel; every tile's product has
+ *      the scale delta_P delta_V, so while a row's max stands the products add
+ *      up exactly as INT32, and a rescale rounds that sum to the nearest
+ *      integer (heads longer than 2^17 keys, where INT32 could overflow,
+ *      convert each tile's product to float32, exactly, and add it instead)
  *   5. O = O / l (FP8, INT8: times delta_V / 448 or / 127), rounded to the
  *      input dtype (RNE).
  * In FP16 mode the kernel keeps the running max lazily (P~ may reach 2^14
