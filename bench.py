@@ -110,7 +110,7 @@ def cpu_baseline(wl, min_seconds: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": args.gpus}), flush=True)
         sys.exit(2)
 

@@ -41,7 +41,7 @@ extern "C" {
 typedef enum {
   SAGE_OK = 0,
   SAGE_ERR_INVALID_ARG = 1,   /* a pointer, size, flag or alignment is invalid */
-  SAGE_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement (e.g. d = 96, not gfx950) */
+  SAGE_ERR_UNSUPPORTED = 2,   /* valid request this library does not implement (e.g. d = 96, not gfx950) */
   SAGE_ERR_WORKSPACE = 3,     /* workspace / scratch smaller than required */
   SAGE_ERR_HIP = 4,           /* the HIP runtime reported an error */
   SAGE_ERR_NO_DEVICE = 5      /* no HIP device is visible */
@@ -59,7 +59,7 @@ enum { SAGE_LAYOUT_HND = 0,                    /* q, k, v, o as [B,H,N,d] */
 const char* sage_status_str(int status);
 
 /*
- * Blocking constants of this build, which define the numerics of the method
+ * Blocking constants of this library, which define the numerics of the method
  * ([SA] §3 Algorithm 1 leaves the block sizes b_q, b_kv open):
  *   q_block    tokens per delta_Q quantisation block (128)
  *   k_block    tokens per delta_K quantisation block (64)
@@ -145,7 +145,7 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
  * The forward pass with Q smoothed per 128-token block as well as K
  * (SageAttention2's smoothing of Q: "SageAttention2" abstract page, Q
  * smoothing improves the quantised QK^T; [SA2pp] 三 smooths Q and K before
- * quantising).  The pages print no formula; this build's reading, step 2 of
+ * quantising).  The pages print no formula; this library's reading, step 2 of
  * sage_attn_fwd replaced for Q by:
  *   qbar = the block's token mean of Q' = fp32(Q * fp32(1/sqrt(d))) (float32,
  *          tokens in order from 0.0f, one IEEE division by their count);

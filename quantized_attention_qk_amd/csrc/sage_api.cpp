@@ -205,7 +205,7 @@ const char* sage_status_str(int status) {
   switch (status) {
     case SAGE_OK: return "SAGE_OK";
     case SAGE_ERR_INVALID_ARG: return "SAGE_ERR_INVALID_ARG: invalid pointer, size, flag or alignment";
-    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED: request not supported by this build (d, size or device)";
+    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED: request not supported by this library (d, size or device)";
     case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE: workspace or scratch too small";
     case SAGE_ERR_HIP: return "SAGE_ERR_HIP: the HIP runtime reported an error";
     case SAGE_ERR_NO_DEVICE: return "SAGE_ERR_NO_DEVICE: no HIP device visible";
