@@ -130,6 +130,10 @@ FWD = [
     small("f640f8", B=2, H=3, N=640, d=128, dtype="bf16", pv_mode="fp8", extras="qbias4_kbias4"),
     small("f700ci8", N=700, d=64, causal=True, pv_mode="int8", extras="qbias4_kbias4"),
     small("f1500r", N=1500, d=128, extras="ramp"),
+    # FP16 P~V at d = 128, non-causal: 256-row workgroups whose second
+    # delta_Q block is short (its compensation values sit second in each slot)
+    small("f300w", N=300, d=128, dtype="bf16", extras="qbias4_kbias4"),
+    small("f129w", N=129, d=128, extras="qbias4_kbias4"),
 ]
 
 
