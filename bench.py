@@ -44,6 +44,10 @@ def parse():
                     help="q, k, v, o layout: [B,H,N,d] or token-major [B,N,H,d]")
     ap.add_argument("--rope", action="store_true",
                     help="apply rotary embeddings to Q and K inside the quantisation prepass")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only run the micro-benchmarks of libsage_probe.so: sustained INT8, "
+                         "FP16 and FP8 MFMA rates with the clock they ran at, and the issue "
+                         "cost of VALU work next to a stream of MFMAs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES (3 launches), to calibrate "
                          "the HBM byte counters against a known traffic")
@@ -63,9 +67,14 @@ def copy_probe(nbytes: int):
 
 
 def kernel_src_hash() -> str:
+    """Hash of the attention kernel's sources (the dispatcher, the kernel
+    templates, the per-mode translation units and the shared headers)."""
+    csrc = os.path.join(ROOT, "quantized_attention_qk_amd", "csrc")
+    files = ["attn_fwd.hip", "attn_fwd_kernel.h", "sage_common.h", "sage_launch.h"]
+    files += sorted(f for f in os.listdir(csrc) if f.startswith("attn_fwd_d"))
     h = hashlib.sha256()
-    for f in ("attn_fwd.hip", "sage_common.h", "sage_launch.h"):
-        h.update(open(os.path.join(ROOT, "quantized_attention_qk_amd", "csrc", f), "rb").read())
+    for f in files:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -116,6 +125,12 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.mfma_probe:
+        from quantized_attention_qk_amd import probe
+        print(json.dumps({"mfma_rates": probe.mfma_rates()}), flush=True)
+        for row in probe.issue_table():
+            print(json.dumps(row), flush=True)
         return
 
     import torch

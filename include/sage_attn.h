@@ -302,6 +302,38 @@ int sage_attn_debug_s_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, 
                           int b, int h, int q0, int nq, int k0, int nk, int32_t* s_out,
                           void* stream);
 
+/*
+ * Debug: the INT32 scores of the timed attention kernel itself ([SA] §3
+ * Algorithm 1: S = Q^ K^^T in INT32).  Re-runs the attention kernel's debug
+ * instantiation -- the same source, instruction schedule, LDS staging and
+ * accumulator start values as the kernel sage_attn_fwd times (FP16 mode
+ * starts every INT32 accumulation at the bit pattern of 1.5 * 2^23; with Q
+ * smoothed, at the compensation values of sage_attn_fwd_sq) -- for head (b, h)
+ * and the query rows [q0, q0 + nq), on the operands that a preceding
+ * sage_attn_fwd / sage_attn_fwd_ex (smooth_q = 0) or sage_attn_fwd_sq
+ * (smooth_q = 1) call with the same B, H, N, d, causal, pv_mode left in
+ * `workspace`.  Writes
+ *   s_out  int32 [nq, nk] row-major: for query q0 + i and key k0 + j of a KV
+ *          tile the kernel computes for that row, the accumulator minus its
+ *          start bias, i.e. S = Q^ K^^T (S + C with Q smoothed, C as in
+ *          sage_attn_fwd_sq).  Entries the kernel does not compute (keys >= N;
+ *          with causal, the tiles past the diagonal of the row's query block)
+ *          are left as they were;
+ *   o_rows float32 [nq, d]: O of those rows, from the same launch.
+ * 0 <= q0 < N, 1 <= nq <= N - q0, 0 <= k0 < N, 1 <= nk <= N - k0; s_out
+ * 4-byte and o_rows 16-byte aligned; workspace as for the forward call
+ * (SAGE_ERR_WORKSPACE if smaller than that call needs).
+ */
+int sage_attn_debug_s_fwd(const void* workspace, size_t workspace_bytes, int B, int H, int N,
+                          int d, int causal, int pv_mode, int smooth_q, int b, int h, int q0,
+                          int nq, int k0, int nk, int32_t* s_out, float* o_rows, void* stream);
+
+/* The name this entry point has in the hot-path contract: identical to
+ * sage_attn_fwd_f32out (float32 O of the whole pass). */
+int sage_attn_debug_fwd_f32(const void* q, const void* k, const void* v, float* o, int B, int H,
+                            int N, int d, int causal, int pv_mode, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

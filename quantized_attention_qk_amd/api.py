@@ -11,8 +11,8 @@ import torch
 
 from ._lib import SAGE_DT, SAGE_LAYOUT, SAGE_PV, check, lib
 
-__all__ = ["sage_attn", "sage_attn_quantized", "ref_rows", "smooth_quant_qk", "quant_v", "debug_s_i32", "tiling",
-           "workspace_bytes", "untile_v"]
+__all__ = ["sage_attn", "sage_attn_quantized", "ref_rows", "smooth_quant_qk", "quant_v", "debug_s_i32",
+           "debug_s_fwd", "tiling", "workspace_bytes", "untile_v"]
 
 
 def _stream_ptr(device) -> int:
@@ -238,6 +238,27 @@ def debug_s_i32(q_i8: torch.Tensor, k_i8: torch.Tensor, b: int, h: int, q0: int,
                                       k0, nk, s.data_ptr(), _stream_ptr(q_i8.device)),
           "sage_attn_debug_s_i32")
     return s
+
+
+S_NOT_COMPUTED = -(2 ** 31)   # entries of debug_s_fwd's S the kernel did not compute
+
+
+def debug_s_fwd(workspace: torch.Tensor, B: int, H: int, N: int, d: int, causal: bool,
+                pv_mode: str, smooth_q: bool, b: int, h: int, q0: int, nq: int, k0: int,
+                nk: int):
+    """The INT32 scores of the timed attention kernel itself (its debug
+    instantiation, re-run on the operands a preceding sage_attn(...,
+    workspace=workspace) call left there) for head (b, h), queries [q0, q0+nq)
+    and keys [k0, k0+nk): returns (S int32 [nq, nk] with S_NOT_COMPUTED where
+    the kernel computes no score, O float32 [nq, d] of those rows)."""
+    dev = workspace.device
+    s = torch.full((nq, nk), S_NOT_COMPUTED, dtype=torch.int32, device=dev)
+    o = torch.full((nq, d), float("nan"), dtype=torch.float32, device=dev)
+    check(lib().sage_attn_debug_s_fwd(workspace.data_ptr(), workspace.numel(), B, H, N, d,
+                                      int(causal), SAGE_PV[pv_mode], int(smooth_q), b, h, q0, nq,
+                                      k0, nk, s.data_ptr(), o.data_ptr(), _stream_ptr(dev)),
+          "sage_attn_debug_s_fwd")
+    return s, o
 
 
 def untile_v(v_out, B: int, H: int, N: int, d: int, pv_mode: str = "fp16"):

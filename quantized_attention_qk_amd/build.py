@@ -1,4 +1,5 @@
-"""Build libsage_attn.so in-tree with hipcc for gfx950.
+"""Build libsage_attn.so (the attention path) and libsage_probe.so (the
+micro-benchmarks bench.py --mfma-probe runs) in-tree with hipcc for gfx950.
 
 Usage: python -m quantized_attention_qk_amd.build   (or call build()).
 Every call recompiles all sources.
@@ -18,6 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libsage_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+PROBE_PATH = os.path.join(PKG, "libsage_probe.so")
 
 ARCH = "gfx950"
 COMMON = [
@@ -30,10 +32,14 @@ SOURCES = {
     # prepass decisions must be reproducible bit for bit: no FP contraction
     "prepass.hip": ["-ffp-contract=off"],
     "attn_fwd.hip": ["-ffp-contract=off"],
+    # the attention kernel's variants, one translation unit per (d, P~V mode)
+    **{f"attn_fwd_d{d}_{pv}.hip": ["-ffp-contract=off"]
+       for d in (64, 128) for pv in ("fp16", "fp8", "int8")},
     "smooth_q.hip": ["-ffp-contract=off"],
     "ref_rows.hip": [],
     "sage_api.cpp": [],
 }
+PROBE_SOURCES = {"probe.hip": []}
 
 
 def hipcc() -> str:
@@ -52,18 +58,24 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs: list[str], path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = {**SOURCES, **PROBE_SOURCES}
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = dict(zip(jobs, ex.map(lambda kv: _compile(*kv), jobs.items())))
+    _link([objs[s] for s in SOURCES], LIB_PATH)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PROBE_PATH}")
     return LIB_PATH
 
 

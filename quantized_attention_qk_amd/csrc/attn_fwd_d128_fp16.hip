@@ -1,0 +1,8 @@
+// attn_fwd_d128_fp16.hip -- the attention kernel's variants for d = 128 and
+// FP16 P~V (templates in attn_fwd_kernel.h; one translation unit per mode so
+// that the variants compile in parallel).
+#include "attn_fwd_kernel.h"
+
+namespace sage {
+template hipError_t attn_launch_dp<128, kPvFp16>(const AttnArgs&, hipStream_t);
+}  // namespace sage

@@ -1,4 +1,6 @@
-// attn_fwd.hip -- the tiled SageAttention kernel for gfx950.
+// attn_fwd_kernel.h -- the tiled SageAttention kernel for gfx950 (templates;
+// attn_fwd_d*_*.hip instantiate them per head dimension and P~V mode so that
+// the variants compile in parallel, attn_fwd.hip dispatches).
 //
 // "SageAttention: Accurate 8-Bit Attention for Plug-and-Play Inference
 // Acceleration" (paper detail page), §3 Algorithm 1 (SAGEAttn-B) and §4
@@ -49,6 +51,8 @@
 // * With Q smoothed per block (SQ, see smooth_q.hip), each K^ tile carries the
 //   block's 64 compensation values C (INT32, 256 bytes) in its LDS slot, and
 //   the INT32 accumulation of S starts from them instead of from a constant.
+#pragma once
+
 #include <type_traits>
 #include <utility>
 
@@ -107,12 +111,24 @@ __device__ __forceinline__ v16i qk_block(const v4i (&qf)[D / 32], const uint8_t*
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Raw buffer resource for gfx9: base address, stride 0, byte-addressed
-// records, default data format word.
+// records, default data format word.  The record count and every offset
+// into the buffer are unsigned 32-bit: a resource spans less than 4 GiB, so
+// the callers keep each one to a head's K^ (N d <= 2^31 bytes for N <= 2^24)
+// or to a single tile.
 constexpr int kBufferFlags = 0x00020000;
-__device__ __forceinline__ v4i buffer_rsrc(const void* base, int bytes) {
+// Byte sizes and offsets at the longest sequence: a head's K^ is at most
+// 2^31 bytes, so every K^ row offset (< N d) fits a signed 32-bit int and the
+// record count an unsigned one; prepared V is addressed one tile (at most
+// 16 KiB) per resource from a 64-bit base; the smoothed-Q seeds of one query
+// block are 256 bytes per tile.
+static_assert((uint64_t)kMaxN * 128 <= (1ull << 31), "K^ head offsets fit 32 bits");
+static_assert((uint64_t)(kMaxN / kKvTile) * kKvTile * 4 < (1ull << 32), "seed rows fit 32 bits");
+static_assert((uint64_t)kMaxN / kKvTile * kKvTile * 128 * 2 >= (1ull << 32),
+              "a head's FP16 V can pass 4 GiB: V is addressed per tile");
+__device__ __forceinline__ v4i buffer_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-             __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)), bytes, kBufferFlags};
+             __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)), (int)bytes, kBufferFlags};
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void*)p;
@@ -193,7 +209,8 @@ struct KLoader {
   }
   // rs: buffer resource of the head's K^ (N*D bytes); kb: LDS byte address of
   // the tile slot.  Rows at or beyond N re-read row N-1 (their scores are
-  // masked).
+  // masked).  Offsets are below N*D <= 2^31 (N <= 2^24, D <= 128), so the
+  // int arithmetic does not wrap.
   template <bool CLAMP>
   __device__ __forceinline__ void issue(v4i rs, int key0, int N, uint32_t kb, int wave) const {
     uint32_t m0[PER];
@@ -212,9 +229,11 @@ template <int D, int PV, int NW>
 struct VLoader {
   static constexpr int PER = VTile<D, PV>::CHUNKS / (64 * NW);
   static_assert(PER * 64 * NW == VTile<D, PV>::CHUNKS, "wavefronts must tile the V tile");
-  // rs: buffer resource of the head's prepared V (tile t starts at
-  // t * VTile::BYTES); vb: LDS byte address of the tile slot.
-  __device__ __forceinline__ static void issue(v4i rs, int tile, uint32_t vb, int wave, int lane) {
+  // v_bh: the head's prepared V (tile t starts at byte t * VTile::BYTES, a
+  // 64-bit offset: a head of 2^24 keys holds 4 GiB of FP16 V); vb: LDS byte
+  // address of the tile slot.  The buffer resource covers the one tile.
+  __device__ __forceinline__ static void issue(const uint8_t* v_bh, int tile, uint32_t vb,
+                                               int wave, int lane) {
     uint32_t m0[PER];
     int vo[PER];
 #pragma unroll
@@ -222,7 +241,8 @@ struct VLoader {
       m0[i] = vb + (i * NW + wave) * 1024;
       vo[i] = ((i * NW + wave) * 64 + lane) * 16;
     }
-    lds_copy_x4<PER>(rs, tile * VTile<D, PV>::BYTES, m0, vo);
+    lds_copy_x4<PER>(buffer_rsrc(v_bh + (size_t)tile * VTile<D, PV>::BYTES, VTile<D, PV>::BYTES),
+                     0, m0, vo);
   }
 };
 
@@ -829,6 +849,36 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
   }
 }
 
+// The debug instantiation (DUMP) of the kernel below stores every INT32
+// score it computes inside a window of one head, exactly as the softmax then
+// reads it, minus the accumulator's start bias (FP16 mode's 1.5 * 2^23; with
+// Q smoothed the start values are the compensation C, which stays in): so
+// the stored value is S = Q^ K^^T, or S + C.  It runs the query blocks qb0,
+// qb0 + 1, ... of the head the kernel's pointers are offset to.
+struct DumpWin {
+  int32_t* s;   // int32 [nq, nk], row-major; entries not computed are untouched
+  int q0, nq, k0, nk, qb0;
+};
+
+template <int PV>
+__device__ __forceinline__ void dump_tile(const DumpWin& dw, const v16i (&s)[2], int tile,
+                                          int qrow, int N, int hh) {
+  const int qi = qrow - dw.q0;
+  if (qrow >= N || qi < 0 || qi >= dw.nq) return;
+  constexpr int bias = PV == kPvFp16 ? kMagicBits : 0;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = tile * kKvTile + 32 * blk + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int kj = key - dw.k0;
+      if (key < N && kj >= 0 && kj < dw.nk) {
+        const int v = s[blk][r];   // element to a scalar first (see softmax_tile)
+        dw.s[(size_t)qi * dw.nk + kj] = v - bias;
+      }
+    }
+}
+
 // Software pipeline over the KV tiles of one workgroup (NW wavefronts), two
 // tiles deep.  Entering step j a wavefront holds P~(j) (MFMA operand) and the
 // INT32 scores S(j+1); step j issues
@@ -844,14 +894,14 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
 // NW wavefronts per workgroup (32 query rows each): 4, one delta_Q block, or
 // 8 (two blocks; FP16 P~V, d = 128, non-causal), where every K^ and V tile
 // copied into LDS serves twice the rows.
-template <int D, int PV, int OUT, bool CAUSAL, bool SQ, bool ACC, int NW>
+template <int D, int PV, int OUT, bool CAUSAL, bool SQ, bool ACC, int NW, bool DUMP>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__ k_i8,
                      const uint8_t* __restrict__ v_t, const float* __restrict__ q_scale,
                      const float* __restrict__ k_scale, const float* __restrict__ v_scale,
                      const int32_t* __restrict__ comp, int BH, int N, int nqb, int ntiles,
-                     int xcd_remap, int H, int nhd, void* __restrict__ out) {
+                     int xcd_remap, int H, int nhd, void* __restrict__ out, DumpWin dw) {
   // K^ slot: the tile, then (SQ) its 64 compensation values
   constexpr int KB = KTile<D>::BYTES + (SQ ? kSqTileBytes * (NW / 4) : 0);
   constexpr int VB = VTile<D, PV>::BYTES;
@@ -873,7 +923,10 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     if (wg < g8) wg = (wg & 7) * (g8 >> 3) + (wg >> 3);
   }
   int bh, qb;
-  if constexpr (CAUSAL) {   // heaviest query blocks first
+  if constexpr (DUMP) {     // one head (pointers offset to it), blocks qb0, qb0 + 1, ...
+    bh = 0;
+    qb = dw.qb0 + (int)blockIdx.x;
+  } else if constexpr (CAUSAL) {   // heaviest query blocks first
     qb = nqb - 1 - wg / BH;
     bh = wg % BH;
   } else {
@@ -925,13 +978,12 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
 
   const KLoader<D, NW> kld(wave, lane);
   using VL = VLoader<D, PV, NW>;
-  const v4i krs = buffer_rsrc(k_bh, N * D);
-  const v4i vrs = buffer_rsrc(v_bh, ntiles * VB);
+  const v4i krs = buffer_rsrc(k_bh, (uint32_t)((size_t)N * D));
   // SQ: the row of compensation values of this wavefront's 128-row block,
   // ntiles * 64 INT32, and their place in each K^ slot
   v4i crs = {0, 0, 0, 0};
   if constexpr (SQ) crs = buffer_rsrc(comp + ((size_t)bh * nq128 + qblk) * ntiles * kKvTile,
-                                      ntiles * kSqTileBytes);
+                                      (uint32_t)ntiles * kSqTileBytes);
   const int sqo = (wave / 4) * kSqTileBytes;
   // K^ tile `tile` into the slot at LDS address `dst`, with (SQ) the
   // compensation values of each 128-row block behind it (wavefronts 0 and 4,
@@ -996,13 +1048,17 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   // first copies (FP16 mode), or into the slot of K^(0) once every wavefront
   // has read it (two slots).
   issue_k.template operator()<true>(0, kl0);
-  VL::issue(vrs, 0, vl[0], wave, lane);
+  VL::issue(v_bh, 0, vl[0], wave, lane);
   if (nt > 1) issue_k.template operator()<true>(1, kl0 + KB);
   if (NKS == 3 && nt > 2) issue_k.template operator()<true>(2, kl0 + 2 * KB);
   wait_lds_loads();
   __syncthreads();
   qk_tile<D, SQ>(sA, qf, kbuf[0], n, hh, init, sqo);
   if (nt > 1) qk_tile<D, SQ>(sB, qf, kbuf[1], n, hh, init, sqo);
+  if constexpr (DUMP) {
+    dump_tile<PV>(dw, sA, 0, qrow, N, hh);
+    if (nt > 1) dump_tile<PV>(dw, sB, 1, qrow, N, hh);
+  }
   softmax_any(sA, pA, 0);   // alpha irrelevant: O is still zero
   __syncthreads();          // every wave has read K^(0)
   if (NKS == 2) {
@@ -1022,7 +1078,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   float dk_next = ks_bh[min(1, ntiles - 1)];
   auto steady = [&]<int U>(int jj, int sw, int sr, int sp) __attribute__((always_inline)) {
     issue_k.template operator()<false>(jj + 3, kl0 + sw * KB);
-    VL::issue(vrs, jj + 1, vl[1 - (U & 1)], wave, lane);
+    VL::issue(v_bh, jj + 1, vl[1 - (U & 1)], wave, lane);
     v16i(&s_cur)[2] = (U & 1) == 0 ? sB : sA;
     v16i(&s_new)[2] = (U & 1) == 0 ? sA : sB;
     PTile<PV>& p_cur = (U & 1) == 0 ? pA : pB;
@@ -1034,6 +1090,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     if constexpr (PV == kPvFp16 && !SQ) asm volatile("" : "+v"(init));
     fused_step<D, PV, SQ>(o, qf, s_cur, s_new, p_cur, p_new, kbuf[sr], kbuf[sp], vbuf[U & 1], m_run,
                       l_run, tile_scale<PV>(cq, dk), grid, init, n, hh, sqo);
+    if constexpr (DUMP) dump_tile<PV>(dw, s_new, jj + 2, qrow, N, hh);
     asm volatile("" ::"s"(dk_next));
     wait_lds_loads();
     __syncthreads();
@@ -1063,7 +1120,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     // together
     auto plain = [&]<int U>(int jj) __attribute__((always_inline)) {
       issue_k.template operator()<false>(jj + 3, kl0 + ((U + 3) & 1) * KB);
-      VL::issue(vrs, jj + 1, vl[1 - U], wave, lane);
+      VL::issue(v_bh, jj + 1, vl[1 - U], wave, lane);
       v16i(&s_cur)[2] = U == 0 ? sB : sA;
       v16i(&s_new)[2] = U == 0 ? sA : sB;
       PTile<PV>& p_cur = U == 0 ? pA : pB;
@@ -1074,6 +1131,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
       alpha_pend = softmax_tile<PV, false>(s_cur, m_run, l_run, p_new, tile_scale<PV>(cq, dk),
                                            grid, ~0u, hh);
       qk_tile<D, SQ>(s_new, qf, kbuf[U], n, hh, init, sqo);
+      if constexpr (DUMP) dump_tile<PV>(dw, s_new, jj + 2, qrow, N, hh);
       asm volatile("" ::"s"(dk_next));
       wait_lds_loads();
       __syncthreads();
@@ -1091,7 +1149,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
       if (jj < nt) {
         if (jj + 3 < nt)
           issue_k.template operator()<true>(jj + 3, kl0 + kslot(jj + 3, u + 3) * KB);
-        if (jj + 1 < nt) VL::issue(vrs, jj + 1, vl[1 - u], wave, lane);
+        if (jj + 1 < nt) VL::issue(v_bh, jj + 1, vl[1 - u], wave, lane);
         v16i(&s_cur)[2] = u == 0 ? sB : sA;
         v16i(&s_new)[2] = u == 0 ? sA : sB;
         PTile<PV>& p_cur = u == 0 ? pA : pB;
@@ -1102,9 +1160,15 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
           if constexpr (ACC) rescale_i32<D>(o, alpha_pend);
           pv_tile<D, PV, ACC>(o, p_cur, vbuf[u], n, hh, alpha_pend);
           if (jj + 1 < nt) alpha_pend = softmax_any(s_cur, p_new, jj + 1);
-          if (jj + 2 < nt) qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init, sqo);
+          if (jj + 2 < nt) {
+            qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init, sqo);
+            if constexpr (DUMP) dump_tile<PV>(dw, s_new, jj + 2, qrow, N, hh);
+          }
         } else {
-          if (jj + 2 < nt) qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init, sqo);
+          if (jj + 2 < nt) {
+            qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init, sqo);
+            if constexpr (DUMP) dump_tile<PV>(dw, s_new, jj + 2, qrow, N, hh);
+          }
           pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh, alpha_pend);
           if (jj + 1 < nt) rescale<D>(o, softmax_any(s_cur, p_new, jj + 1));
         }
@@ -1118,10 +1182,12 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   // delta_V per channel).
   const float l_tot = pair_sum_f32(l_run);
   const float inv = 1.0f / l_tot;
-  if (qrow < N) {
-    // O row of (b, h, qrow): [B,H,N,d] or token-major [B,N,H,d]
-    const size_t orow = nhd ? (((size_t)(bh / H) * N + qrow) * H + bh % H) * D
-                            : ((size_t)bh * N + qrow) * D;
+  if (qrow < N && (!DUMP || (qrow >= dw.q0 && qrow - dw.q0 < dw.nq))) {
+    // O row of (b, h, qrow): [B,H,N,d] or token-major [B,N,H,d]; the dump
+    // instantiation writes the rows of its window, [nq, d] from row q0
+    const size_t orow = DUMP  ? (size_t)(qrow - dw.q0) * D
+                        : nhd ? (((size_t)(bh / H) * N + qrow) * H + bh % H) * D
+                              : ((size_t)bh * N + qrow) * D;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -1139,39 +1205,6 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   }
 }
 
-// ---------------------------------------------------------------------------
-// Debug kernel: one wavefront per 32-query x 64-key block, using the same
-// Q^ fragment load, K^ staging/LDS layout and INT8 MFMA block as above.
-template <int D>
-__global__ __launch_bounds__(64) void debug_s_kernel(const int8_t* __restrict__ q_bh,
-                                                     const int8_t* __restrict__ k_bh, int N,
-                                                     int q0, int nq, int k0, int nk,
-                                                     int32_t* __restrict__ s_out) {
-  __shared__ __attribute__((aligned(16))) uint8_t kb[KTile<D>::BYTES];
-  const int lane = threadIdx.x;
-  const int n = lane & 31, hh = lane >> 5;
-  const int qbase = q0 + 32 * blockIdx.x;
-  const int kbase = k0 + 64 * blockIdx.y;
-  v4i qf[D / 32];
-  load_q_frag<D>(qf, q_bh, qbase + n, N, hh);
-  const KLoader<D, 1> kld(0, lane);
-  kld.template issue<true>(buffer_rsrc(k_bh, N * D), kbase, N, lds_addr(kb), 0);
-  wait_lds_loads();
-  __syncthreads();
-  const int query = qbase + n;
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const v16i s = qk_block<D>(qf, kb, blk, n, hh, v16i{});
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kbase + 32 * blk + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (key < k0 + nk) {
-        const int32_t val = (query < N && key < N) ? s[r] : 0;
-        s_out[(size_t)(query - q0) * nk + (key - k0)] = val;
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // INT8 P~V keeps O as an INT32 sum of the tiles' products for heads of up to
@@ -1185,78 +1218,63 @@ constexpr int kInt8AccMaxKeys = 1 << 17;
 // whose steps rarely rescale; with the exact max of FP8 and INT8 P~V the
 // rescales of single wavefronts hold all eight at each step's barrier.  With
 // Q smoothed each K^ slot carries the compensation values of both blocks.
-template <int D, int PV, int OUT, bool CAUSAL, bool SQ>
-static hipError_t attn_dispatch(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
-                                const float* q_scale, const float* k_scale,
-                                const float* v_scale, const int32_t* comp, int B, int H, int N,
-                                int nhd, void* out, hipStream_t s) {
-  constexpr int NW = PV == kPvFp16 && D == 128 && !CAUSAL ? 8 : 4;
-  const int nqb = ceil_div(N, kWaveQ * NW);
-  const int ntiles = ceil_div(N, kKvTile);
-  const int BH = B * H;
-  const long long grid = (long long)BH * nqb;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+template <int D, int PV, bool CAUSAL>
+constexpr int kWaves = PV == kPvFp16 && D == 128 && !CAUSAL ? 8 : 4;
+
+template <int D, int PV, int OUT, bool CAUSAL, bool SQ, bool DUMP>
+static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
+  constexpr int NW = kWaves<D, PV, CAUSAL>;
+  constexpr int BQW = kWaveQ * NW;
+  const int nqb = ceil_div(a.N, BQW);
+  const int ntiles = ceil_div(a.N, kKvTile);
+  int BH = a.B * a.H;
+  long long grid = (long long)BH * nqb;
+  DumpWin dw{};
+  if constexpr (DUMP) {
+    const int qb0 = a.dump_q0 / BQW;
+    grid = ceil_div(a.dump_q0 + a.dump_nq, BQW) - qb0;
+    BH = 1;
+    dw = DumpWin{a.s_dump, a.dump_q0, a.dump_nq, a.dump_k0, a.dump_nk, qb0};
+  }
+  if (grid < 1 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int remap = CAUSAL || DUMP ? 0 : 1;
+  auto go = [&](auto acc) {
+    attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ, decltype(acc)::value, NW, DUMP>
+        <<<dim3((unsigned)grid), 64 * NW, 0, s>>>(a.q_i8, a.k_i8, a.v_t, a.q_scale, a.k_scale,
+                                                  a.v_scale, a.comp, BH, a.N, nqb, ntiles, remap,
+                                                  a.H, a.nhd, a.out, dw);
+    return hipGetLastError();
+  };
   if constexpr (PV == kPvInt8) {
-    if (N <= kInt8AccMaxKeys) {
-      attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ, true, NW><<<dim3((unsigned)grid), 64 * NW, 0, s>>>(
-          q_i8, k_i8, v_t, q_scale, k_scale, v_scale, comp, BH, N, nqb, ntiles, CAUSAL ? 0 : 1,
-          H, nhd, out);
-      return hipGetLastError();
-    }
+    if (a.N <= kInt8AccMaxKeys) return go(std::true_type{});
   }
-  attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ, false, NW><<<dim3((unsigned)grid), 64 * NW, 0, s>>>(
-      q_i8, k_i8, v_t, q_scale, k_scale, v_scale, comp, BH, N, nqb, ntiles, CAUSAL ? 0 : 1, H,
-      nhd, out);
-  return hipGetLastError();
+  return go(std::false_type{});
 }
 
-template <int D, int PV, int OUT>
-static hipError_t attn_dispatch_c(int causal, const int8_t* q_i8, const int8_t* k_i8,
-                                  const uint8_t* v_t, const float* q_scale, const float* k_scale,
-                                  const float* v_scale, const int32_t* comp, int B, int H, int N,
-                                  int nhd, void* out, hipStream_t s) {
-#define SAGE_DISPATCH(C, SQ)                                                                   \
-  return attn_dispatch<D, PV, OUT, C, SQ>(q_i8, k_i8, v_t, q_scale, k_scale, v_scale, comp, B, \
-                                          H, N, nhd, out, s);
-  if (comp) {
-    if (causal) { SAGE_DISPATCH(true, true) } else { SAGE_DISPATCH(false, true) }
+// All variants of one head dimension and P~V mode (instantiated once per
+// mode by the attn_fwd_d*_*.hip translation units).  The dump launch
+// (a.s_dump set) writes float32 O.
+template <int D, int PV>
+hipError_t attn_launch_dp(const AttnArgs& a, hipStream_t s) {
+  const bool sq = a.comp != nullptr;
+#define SAGE_DISPATCH(OUT, DUMP)                                                         \
+  {                                                                                     \
+    if (a.causal) return sq ? attn_dispatch<D, PV, OUT, true, true, DUMP>(a, s)         \
+                            : attn_dispatch<D, PV, OUT, true, false, DUMP>(a, s);       \
+    return sq ? attn_dispatch<D, PV, OUT, false, true, DUMP>(a, s)                      \
+              : attn_dispatch<D, PV, OUT, false, false, DUMP>(a, s);                    \
   }
-  if (causal) { SAGE_DISPATCH(true, false) } else { SAGE_DISPATCH(false, false) }
+  if (a.s_dump) {
+    if (a.out_kind != 2) return hipErrorInvalidValue;
+    SAGE_DISPATCH(2, true)
+  }
+  switch (a.out_kind) {
+    case 0: SAGE_DISPATCH(0, false)
+    case 1: SAGE_DISPATCH(1, false)
+    case 2: SAGE_DISPATCH(2, false)
+    default: return hipErrorInvalidValue;
+  }
 #undef SAGE_DISPATCH
-}
-
-hipError_t launch_attn(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
-                       const float* q_scale, const float* k_scale, const float* v_scale,
-                       const int32_t* comp, int B, int H, int N, int d, int causal, int pv_mode,
-                       int out_kind, int nhd, void* out, hipStream_t s) {
-#define SAGE_ATTN_CASE(D, PV, OUT)                                                          \
-  if (d == D && pv_mode == PV && out_kind == OUT)                                          \
-    return attn_dispatch_c<D, PV, OUT>(causal, q_i8, k_i8, v_t, q_scale, k_scale, v_scale, \
-                                       comp, B, H, N, nhd, out, s);
-  SAGE_ATTN_CASE(64, 0, 0) SAGE_ATTN_CASE(64, 0, 1) SAGE_ATTN_CASE(64, 0, 2)
-  SAGE_ATTN_CASE(64, 1, 0) SAGE_ATTN_CASE(64, 1, 1) SAGE_ATTN_CASE(64, 1, 2)
-  SAGE_ATTN_CASE(64, 2, 0) SAGE_ATTN_CASE(64, 2, 1) SAGE_ATTN_CASE(64, 2, 2)
-  SAGE_ATTN_CASE(128, 0, 0) SAGE_ATTN_CASE(128, 0, 1) SAGE_ATTN_CASE(128, 0, 2)
-  SAGE_ATTN_CASE(128, 1, 0) SAGE_ATTN_CASE(128, 1, 1) SAGE_ATTN_CASE(128, 1, 2)
-  SAGE_ATTN_CASE(128, 2, 0) SAGE_ATTN_CASE(128, 2, 1) SAGE_ATTN_CASE(128, 2, 2)
-#undef SAGE_ATTN_CASE
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_debug_s(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
-                          int b, int h, int q0, int nq, int k0, int nk, int32_t* s_out,
-                          hipStream_t s) {
-  const size_t bh = (size_t)b * H + h;
-  dim3 grid(nq / 32, ceil_div(nk, 64));
-  if (d == 64)
-    debug_s_kernel<64><<<grid, 64, 0, s>>>(q_i8 + bh * N * 64, k_i8 + bh * N * 64, N, q0, nq, k0,
-                                          nk, s_out);
-  else if (d == 128)
-    debug_s_kernel<128><<<grid, 64, 0, s>>>(q_i8 + bh * N * 128, k_i8 + bh * N * 128, N, q0, nq,
-                                           k0, nk, s_out);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 }  // namespace sage

@@ -15,7 +15,7 @@ namespace {
 
 using sage::ceil_div;
 
-constexpr int kMaxN = 1 << 24;   // (float)N is exact; block indices fit in int
+using sage::kMaxN;
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
@@ -482,6 +482,45 @@ int sage_attn_debug_s_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, 
   if (st != SAGE_OK) return st;
   return hip_status(sage::launch_debug_s(q_i8, k_i8, B, H, N, d, b, h, q0, nq, k0, nk, s_out,
                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int sage_attn_debug_s_fwd(const void* workspace, size_t workspace_bytes, int B, int H, int N,
+                          int d, int causal, int pv_mode, int smooth_q, int b, int h, int q0,
+                          int nq, int k0, int nk, int32_t* s_out, float* o_rows, void* stream) {
+  if (!workspace || !s_out || !o_rows) return SAGE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0 ||
+      (reinterpret_cast<uintptr_t>(s_out) & 3u) || (reinterpret_cast<uintptr_t>(o_rows) & 15u))
+    return SAGE_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (smooth_q != 0 && smooth_q != 1) return SAGE_ERR_INVALID_ARG;
+  if (!sage::pv_valid(pv_mode)) return SAGE_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
+  if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
+  if (b < 0 || b >= B || h < 0 || h >= H) return SAGE_ERR_INVALID_ARG;
+  if (q0 < 0 || q0 >= N || nq < 1 || nq > N - q0 || k0 < 0 || k0 >= N || nk < 1 || nk > N - k0)
+    return SAGE_ERR_INVALID_ARG;
+  const Layout L = make_layout(B, H, N, d, pv_mode, smooth_q == 1);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  int st = device_check();
+  if (st != SAGE_OK) return st;
+  const uint8_t* w = static_cast<const uint8_t*>(workspace);
+  auto F = [&](size_t off) { return reinterpret_cast<const float*>(w + off); };
+  return hip_status(sage::launch_attn_dump(
+      reinterpret_cast<const int8_t*>(w + L.q_i8), reinterpret_cast<const int8_t*>(w + L.k_i8),
+      w + L.v_t, F(L.q_scale), F(L.k_scale), sage::v_quantised(pv_mode) ? F(L.v_scale) : nullptr,
+      smooth_q ? reinterpret_cast<const int32_t*>(w + L.comp) : nullptr, B, H, N, d, causal,
+      pv_mode, b, h, q0, nq, k0, nk, s_out, o_rows, static_cast<hipStream_t>(stream)));
+}
+
+int sage_attn_debug_fwd_f32(const void* q, const void* k, const void* v, float* o, int B, int H,
+                            int N, int d, int causal, int pv_mode, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return sage_attn_fwd_f32out(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, workspace,
+                              workspace_bytes, stream);
 }
 
 }  // extern "C"

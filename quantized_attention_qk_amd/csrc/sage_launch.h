@@ -15,6 +15,10 @@ constexpr int kKBlock = 64;      // tokens per delta_K block
 constexpr int kKvTile = 64;      // keys per online-softmax step
 constexpr int kMeanChunk = 256;  // tokens per float32 partial column sum
 constexpr int kWaveQ = 32;       // query rows per wavefront (one 32x32 MFMA column block)
+// Longest sequence the library accepts: (float)N is exact, and the byte
+// offsets of one head's K^ (N d <= 2^31) fit the kernels' 32-bit buffer
+// offsets (checked where they are formed, attn_fwd_kernel.h).
+constexpr int kMaxN = 1 << 24;
 static_assert(kQBlock % kWaveQ == 0, "a delta_Q block is whole wavefronts of rows");
 static_assert(kKvTile == kKBlock, "one delta_K per KV tile");
 
@@ -90,6 +94,32 @@ hipError_t launch_attn(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_
                        const float* q_scale, const float* k_scale, const float* v_scale,
                        const int32_t* comp, int B, int H, int N, int d, int causal, int pv_mode,
                        int out_kind, int nhd, void* out, hipStream_t s);
+
+// Debug: the attention kernel's own dump instantiation on head (b, h) for the
+// query rows [q0, q0+nq): every INT32 score it computes for keys [k0, k0+nk)
+// (minus the accumulator's start bias) into s_out int32 [nq, nk], and the
+// float32 O of those rows into o_rows [nq, d].  Operands as for launch_attn.
+hipError_t launch_attn_dump(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
+                            const float* q_scale, const float* k_scale, const float* v_scale,
+                            const int32_t* comp, int B, int H, int N, int d, int causal,
+                            int pv_mode, int b, int h, int q0, int nq, int k0, int nk,
+                            int32_t* s_out, float* o_rows, hipStream_t s);
+
+// Arguments of one attention launch (attn_fwd_kernel.h).  The dump fields are
+// used only when s_dump is set; the pointers then address one head.
+struct AttnArgs {
+  const int8_t* q_i8;
+  const int8_t* k_i8;
+  const uint8_t* v_t;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* comp;
+  int B, H, N, causal, out_kind, nhd;
+  void* out;
+  int32_t* s_dump;
+  int dump_q0, dump_nq, dump_k0, dump_nk;
+};
 
 // Smoothed Q (smooth_q.hip): per 128-token block the mean qbar is removed
 // before quantisation (q_i8, q_scale as for plain Q; q_mean float32 and q_w

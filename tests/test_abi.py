@@ -263,3 +263,66 @@ def test_smooth_q_entries_validation():
     if not torch.cuda.is_available():
         assert h.sage_smooth_q(*args) == NO_DEVICE
         assert h.sage_attn_fwd_quantized_sq(*qargs) == NO_DEVICE
+
+
+def test_debug_s_fwd_validation():
+    # workspace, bytes, B, H, N, d, causal, pv, smooth_q, b, h, q0, nq, k0, nk, s_out, o_rows, stream
+    h = lib()
+    ws = P + 0x100000
+    need = h.sage_attn_workspace_bytes(1, 2, 100, 64, 0)
+    need_sq = h.sage_attn_sq_workspace_bytes(1, 2, 100, 64, 0)
+    args = [ws, need, 1, 2, 100, 64, 0, 0, 0, 0, 1, 0, 100, 0, 100, P, P + 0x1000, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return h.sage_attn_debug_s_fwd(*a)
+    assert call(a0=None) == INVALID
+    assert call(a0=P + 16) == INVALID           # workspace not 256-byte aligned
+    assert call(a15=None) == INVALID
+    assert call(a16=P + 4) == INVALID           # o_rows not 16-byte aligned
+    assert call(a6=2) == INVALID
+    assert call(a8=2) == INVALID
+    assert call(a7=3) == INVALID
+    assert call(a10=2) == INVALID               # head out of range
+    assert call(a11=100) == INVALID             # q0 >= N
+    assert call(a12=101) == INVALID             # window past N
+    assert call(a13=-1) == INVALID
+    assert call(a14=0) == INVALID
+    assert call(a5=96) == UNSUPPORTED
+    assert call(a1=need - 1) == WORKSPACE
+    assert call(a8=1, a1=need) == WORKSPACE     # Q smoothed needs the larger workspace
+    if not torch.cuda.is_available():
+        assert call() == NO_DEVICE
+        assert call(a8=1, a1=need_sq) == NO_DEVICE
+        assert h.sage_attn_debug_fwd_f32(P, P, P, P + 0x1000, 1, 2, 100, 64, 0, 0, 0,
+                                         P + 0x100000, 1 << 40, None) == NO_DEVICE
+
+
+def test_sequence_length_limit():
+    # the documented limit 2^24 tokens is accepted, one more is not (the
+    # kernels' 32-bit buffer offsets are sized for it: static_asserts in the
+    # attention kernel's source)
+    h = lib()
+    assert "N <= 2^24" in open(HEADER).read()
+    for pv in (0, 1, 2):
+        for d in (64, 128):
+            assert h.sage_attn_workspace_bytes(1, 1, 1 << 24, d, pv) > (1 << 24) * d * 2
+            assert h.sage_attn_workspace_bytes(1, 1, (1 << 24) + 1, d, pv) == 0
+    assert fwd(N=1 << 24, d=128, wsb=1000) == WORKSPACE    # shape accepted, workspace checked
+
+
+def test_probe_library_exports():
+    from quantized_attention_qk_amd import probe
+    src = open(os.path.join(ROOT, "include", "sage_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", src)))
+    assert names == ["sage_probe_cu_count", "sage_probe_run", "sage_probe_wallclock_khz"]
+    h = probe.lib()
+    for n in names:
+        assert hasattr(h, n), n
+    # invalid arguments are rejected before any launch
+    assert h.sage_probe_run(0, 0, 0, 3, 256, 1024, P, P, None) == 1
+    assert h.sage_probe_run(0, 0, 0, 2, 256, 1023, P, P, None) == 1
+    assert h.sage_probe_run(5, 0, 0, 2, 256, 1024, P, P, None) == 1

@@ -286,7 +286,10 @@ def test_full_workload(name):
         allow = None if allow is None else allow[0, 0]
         g32 = to_np(o32[b, h, torch.from_numpy(rows).cuda()])
         g16 = to_np(o16[b, h, torch.from_numpy(rows).cuda()].float())
-        compare_o(g32, ref, f"{name} (b={b},h={h}) O f32", allow)
+        # the five workloads meet 2e-3 with no allowance for P^ boundary
+        # cases; the allowance stays for the INT8 P~V variants of c3, c4
+        strict = name in ("c1", "c2", "c3", "c4", "c5", "c3_shard8")
+        compare_o(g32, ref, f"{name} (b={b},h={h}) O f32", None if strict else allow)
         lim16 = O_MAX_ABS + ulp16(ref, wl.dtype) + (0.0 if allow is None else allow)
         assert np.all(np.abs(g16 - ref) <= lim16), "16-bit O"
 
