@@ -328,6 +328,29 @@ int sage_attn_debug_s_fwd(const void* workspace, size_t workspace_bytes, int B, 
                           int d, int causal, int pv_mode, int smooth_q, int b, int h, int q0,
                           int nq, int k0, int nk, int32_t* s_out, float* o_rows, void* stream);
 
+/*
+ * sage_attn_fwd for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc:
+ * the same forward pass (same kernels, same results bit for bit) with no
+ * workspace argument.  The workspace is a fixed device array of
+ * SAGE_NOALLOC_MAX_WORKSPACE bytes inside this library, one per device, held
+ * from this library's load until the process ends; its address on the
+ * current device is looked up on the first call on that device.  The call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).
+ *   Limit: shapes whose sage_attn_workspace_bytes(B,H,N,d,pv_mode) exceeds
+ *   SAGE_NOALLOC_MAX_WORKSPACE return SAGE_ERR_WORKSPACE (c3's 1x24x16384x128
+ *   needs about 200 MB; 1x32x4096x128 fits).
+ *   Sharing: every call on a device uses that device's one array and leaves
+ *   its contents behind (nothing in it needs to start at zero).  Calls whose
+ *   work overlaps on one device -- on different streams, or from several host
+ *   threads -- race on it and give wrong results: order them on one stream.
+ * Other arguments, validation and errors as sage_attn_fwd.
+ */
+#define SAGE_NOALLOC_MAX_WORKSPACE ((size_t)128 << 20)
+int sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H,
+                          int N, int d, int causal, int pv_mode, int dtype, void* stream);
+
 /* The name this entry point has in the hot-path contract: identical to
  * sage_attn_fwd_f32out (float32 O of the whole pass). */
 int sage_attn_debug_fwd_f32(const void* q, const void* k, const void* v, float* o, int B, int H,

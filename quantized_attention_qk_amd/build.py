@@ -38,6 +38,7 @@ SOURCES = {
     "smooth_q.hip": ["-ffp-contract=off"],
     "ref_rows.hip": [],
     "sage_api.cpp": [],
+    "sage_noalloc.hip": [],
 }
 PROBE_SOURCES = {"probe.hip": []}
 

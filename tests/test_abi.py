@@ -326,3 +326,19 @@ def test_probe_library_exports():
     assert h.sage_probe_run(0, 0, 0, 3, 256, 1024, P, P, None) == 1
     assert h.sage_probe_run(0, 0, 0, 2, 256, 1023, P, P, None) == 1
     assert h.sage_probe_run(5, 0, 0, 2, 256, 1024, P, P, None) == 1
+
+
+def test_noalloc_validation():
+    # q, k, v, o, B, H, N, d, causal, pv_mode, dtype, stream
+    h = lib()
+    assert h.sage_attn_fwd_noalloc(P, P, P, P + 0x1000, 1, 2, 100, 64, 0, 3, 0, None) == INVALID
+    assert h.sage_attn_fwd_noalloc(P, P, P, P + 0x1000, 0, 2, 100, 64, 0, 0, 0, None) == INVALID
+    assert h.sage_attn_fwd_noalloc(P, P, P, P + 0x1000, 1, 2, 100, 96, 0, 0, 0, None) == UNSUPPORTED
+    # beyond the fixed workspace (c3's shape needs about 200 MB)
+    assert h.sage_attn_workspace_bytes(1, 24, 16384, 128, 0) > (128 << 20)
+    assert h.sage_attn_fwd_noalloc(P, P, P, P + 0x1000, 1, 24, 16384, 128, 0, 0, 1,
+                                   None) == WORKSPACE
+    assert "#define SAGE_NOALLOC_MAX_WORKSPACE ((size_t)128 << 20)" in open(HEADER).read()
+    if not torch.cuda.is_available():
+        assert h.sage_attn_fwd_noalloc(P, P, P, P + 0x1000, 1, 2, 100, 64, 0, 0, 0,
+                                       None) == NO_DEVICE
