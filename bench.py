@@ -91,6 +91,33 @@ def traffic_from_profiles(workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
+def clock_from_profiles(workload: str):
+    """The shader clock during the attention kernel, from the committed
+    rocprofv3 counter run (GRBM_GUI_ACTIVE cycles per dispatch over the
+    dispatch duration, per XCD), or None when absent or the kernel changed."""
+    try:
+        data = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("kernel_src_hash") != kernel_src_hash():
+        return None
+    return entry.get("clock_ghz")
+
+
+def measured_mfma_peak(pv_mode: str):
+    """Sustained MFMA rates on this GPU right now (libsage_probe.so, two
+    wavefronts per SIMD on every CU, ~25 ms of back-to-back launches so the
+    power-limited clock settles): the INT8 rate, and the mixed rate of the
+    kernel's P~V mode (half the operations INT8, half FP16 / FP8 / INT8)."""
+    from quantized_attention_qk_amd import probe
+    i8 = probe.run(probe.I8, wps=2, iters=32768, repeats=10)["tops"]
+    other = {"fp16": probe.F16, "fp8": probe.F8, "int8": probe.I8}[pv_mode]
+    pv = i8 if other == probe.I8 else \
+        probe.run(other, wps=2, iters=32768 if other == probe.F16 else 16384, repeats=10)["tops"]
+    return i8, 1.0 / (0.5 / i8 + 0.5 / pv)
+
+
 def cpu_baseline(wl, min_seconds: float):
     """Time the CPU oracle (as it stands) on whole heads of the workload until
     at least `min_seconds` have elapsed (at most 4 heads)."""
@@ -202,6 +229,8 @@ def main():
     assert torch.equal(o_hnd, out2), "attention-only path must reproduce the full pass"
 
     traffic = traffic_from_profiles(wl.name)
+    clock = clock_from_profiles(wl.name)
+    i8_meas, mixed_meas = measured_mfma_peak(wl.pv_mode)
     # FP8 and INT8 P~V run at the INT8 MFMA rate; FP16 P~V at half of it
     mixed_peak = INT8_PEAK_TOPS if wl.pv_mode in ("fp8", "int8") else \
         1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / FP16_PEAK_TFLOPS)
@@ -232,7 +261,15 @@ def main():
                      "kernel_ms": round(kms, 4),
                      "ops_per_launch": wl.ops,
                      "mixed_mfma_peak": round(mixed_peak, 1),
-                     "frac_of_mixed_peak": round(ktops / mixed_peak, 4)},
+                     "frac_of_mixed_peak": round(ktops / mixed_peak, 4),
+                     # the same ratios against rates measured on this GPU
+                     # just now (bench.py --mfma-probe kernels)
+                     "measured_int8_peak": round(i8_meas, 1),
+                     "frac_of_measured_int8_peak": round(ktops / i8_meas, 4),
+                     "measured_mixed_peak": round(mixed_meas, 1),
+                     "frac_of_measured_mixed_peak": round(ktops / mixed_meas, 4),
+                     "clock_ghz": clock,
+                     "hbm_gbps": None if traffic is None else round(traffic / (kms * 1e-3) / 1e9, 1)},
         "prepass_ms": round(ms - kms, 4),
         "wall_s_timed": round(t_wall, 3),
     }

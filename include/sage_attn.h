@@ -158,9 +158,11 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
  * |C| <= 2^21); any other block is quantised as in sage_attn_fwd (w = 0).
  * Arguments as sage_attn_fwd_ex without RoPE (layout SAGE_LAYOUT_HND or
  * SAGE_LAYOUT_NHD; out_f32 0/1); the workspace must hold
- * sage_attn_sq_workspace_bytes(...) bytes.  It adds ceil(N/128) * ceil(N/64)
- * * 64 int32 compensation values per head, about N^2/32 bytes: 8 MiB at
- * N = 16384, 512 MiB at N = 131072, so this pass suits moderate N.
+ * sage_attn_sq_workspace_bytes(...) bytes.  It adds ceil(N/64) * 64 int32
+ * compensation values per head and 128-row query block, about N^2/32 bytes per
+ * head (8 MiB at N = 16384), capped at 256 MiB in all: beyond that the pass
+ * computes them, and runs the attention kernel, in chunks of query blocks
+ * (N = 131072 on one head: three chunks instead of a 512 MiB table).
  */
 size_t sage_attn_sq_workspace_bytes(int B, int H, int N, int d, int pv_mode);
 int sage_attn_fwd_sq(const void* q, const void* k, const void* v, void* o,
@@ -322,7 +324,9 @@ int sage_attn_debug_s_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, 
  *   o_rows float32 [nq, d]: O of those rows, from the same launch.
  * 0 <= q0 < N, 1 <= nq <= N - q0, 0 <= k0 < N, 1 <= nk <= N - k0; s_out
  * 4-byte and o_rows 16-byte aligned; workspace as for the forward call
- * (SAGE_ERR_WORKSPACE if smaller than that call needs).
+ * (SAGE_ERR_WORKSPACE if smaller than that call needs).  With smooth_q the
+ * forward pass must have kept its whole compensation table in one chunk
+ * (at most 256 MiB, see sage_attn_fwd_sq), else SAGE_ERR_UNSUPPORTED.
  */
 int sage_attn_debug_s_fwd(const void* workspace, size_t workspace_bytes, int B, int H, int N,
                           int d, int causal, int pv_mode, int smooth_q, int b, int h, int q0,

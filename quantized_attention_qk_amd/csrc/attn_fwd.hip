@@ -29,9 +29,11 @@ static hipError_t attn_launch(const AttnArgs& a, int d, int pv_mode, hipStream_t
 hipError_t launch_attn(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
                        const float* q_scale, const float* k_scale, const float* v_scale,
                        const int32_t* comp, int B, int H, int N, int d, int causal, int pv_mode,
-                       int out_kind, int nhd, void* out, hipStream_t s) {
-  const AttnArgs a{q_i8, k_i8,   v_t, q_scale,  k_scale, v_scale, comp, B, H, N,
-                   causal, out_kind, nhd, out, nullptr, 0, 0, 0, 0};
+                       int out_kind, int nhd, void* out, hipStream_t s, int q128_begin,
+                       int q128_count) {
+  const AttnArgs a{q_i8,   k_i8,     v_t, q_scale, k_scale, v_scale, comp, B, H,          N,
+                   causal, out_kind, nhd, out,     nullptr, 0,       0,    0, 0, q128_begin,
+                   q128_count};
   return attn_launch(a, d, pv_mode, s);
 }
 
@@ -50,7 +52,7 @@ hipError_t launch_attn_dump(const int8_t* q_i8, const int8_t* k_i8, const uint8_
                    k_scale + bh * nt,
                    v_scale ? v_scale + bh * d : nullptr,
                    comp ? comp + bh * nq128 * nt * kKvTile : nullptr,
-                   1, 1, N, causal, 2, 0, o_rows, s_out, q0, nq, k0, nk};
+                   1, 1, N, causal, 2, 0, o_rows, s_out, q0, nq, k0, nk, 0, 0};
   (void)B;
   return attn_launch(a, d, pv_mode, s);
 }

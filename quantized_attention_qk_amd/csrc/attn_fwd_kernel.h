@@ -900,7 +900,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
 void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__ k_i8,
                      const uint8_t* __restrict__ v_t, const float* __restrict__ q_scale,
                      const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-                     const int32_t* __restrict__ comp, int BH, int N, int nqb, int ntiles,
+                     const int32_t* __restrict__ comp, int BH, int N, int qb_begin, int nqb,
+                     int ntiles,
                      int xcd_remap, int H, int nhd, void* __restrict__ out, DumpWin dw) {
   // K^ slot: the tile, then (SQ) its 64 compensation values
   constexpr int KB = KTile<D>::BYTES + (SQ ? kSqTileBytes * (NW / 4) : 0);
@@ -914,11 +915,12 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][VB];
 
   // Workgroup -> (b*h, query block).
+  // Consecutive workgroups are dispatched round-robin over the 8 XCDs (each
+  // with its own L2); the remap keeps the workgroups of a head on one XCD so
+  // that its K^/V tiles are shared in that L2.
   int wg = blockIdx.x;
   if (xcd_remap) {
-    // Consecutive workgroups are dispatched round-robin over the 8 XCDs; give
-    // each XCD a contiguous range of (head, block) ids so that the K/V tiles
-    // of a head are shared in that XCD's L2.
+    // each XCD a contiguous range of (head, block) ids
     const int g8 = gridDim.x & ~7;
     if (wg < g8) wg = (wg & 7) * (g8 >> 3) + (wg >> 3);
   }
@@ -926,13 +928,18 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   if constexpr (DUMP) {     // one head (pointers offset to it), blocks qb0, qb0 + 1, ...
     bh = 0;
     qb = dw.qb0 + (int)blockIdx.x;
-  } else if constexpr (CAUSAL) {   // heaviest query blocks first
+  } else if constexpr (CAUSAL) {
+    // heaviest query blocks first, over all heads.  (Keeping each head on
+    // one XCD cut the HBM fetches of c2 threefold but not its time, and the
+    // head-by-head order it needs balanced short grids worse.)
     qb = nqb - 1 - wg / BH;
     bh = wg % BH;
   } else {
     bh = wg / nqb;
     qb = wg % nqb;
   }
+  // this launch covers query blocks [qb_begin, qb_begin + nqb) of each head
+  if constexpr (!DUMP) qb += qb_begin;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
@@ -982,8 +989,14 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
   // SQ: the row of compensation values of this wavefront's 128-row block,
   // ntiles * 64 INT32, and their place in each K^ slot
   v4i crs = {0, 0, 0, 0};
-  if constexpr (SQ) crs = buffer_rsrc(comp + ((size_t)bh * nq128 + qblk) * ntiles * kKvTile,
-                                      (uint32_t)ntiles * kSqTileBytes);
+  // (a launch over part of the query blocks gets the rows of its own blocks:
+  // 128-row blocks [q128_0, q128_0 + n128) of each head)
+  if constexpr (SQ) {
+    const int q128_0 = DUMP ? 0 : qb_begin * BQW / kQBlock;
+    const int n128 = DUMP ? nq128 : (min(N, (qb_begin + nqb) * BQW) + kQBlock - 1) / kQBlock - q128_0;
+    crs = buffer_rsrc(comp + ((size_t)bh * n128 + (qblk - q128_0)) * ntiles * kKvTile,
+                      (uint32_t)ntiles * kSqTileBytes);
+  }
   const int sqo = (wave / 4) * kSqTileBytes;
   // K^ tile `tile` into the slot at LDS address `dst`, with (SQ) the
   // compensation values of each 128-row block behind it (wavefronts 0 and 4,
@@ -1225,8 +1238,12 @@ template <int D, int PV, int OUT, bool CAUSAL, bool SQ, bool DUMP>
 static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   constexpr int NW = kWaves<D, PV, CAUSAL>;
   constexpr int BQW = kWaveQ * NW;
-  const int nqb = ceil_div(a.N, BQW);
   const int ntiles = ceil_div(a.N, kKvTile);
+  // query blocks of this launch: 128-row blocks [q128_begin, + q128_count)
+  // (count 0: to the end), in workgroup blocks of BQW rows
+  const int qb_begin = a.q128_begin * kQBlock / BQW;
+  const int q_end = a.q128_count ? min(a.N, (a.q128_begin + a.q128_count) * kQBlock) : a.N;
+  const int nqb = ceil_div(q_end, BQW) - qb_begin;
   int BH = a.B * a.H;
   long long grid = (long long)BH * nqb;
   DumpWin dw{};
@@ -1241,7 +1258,8 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   auto go = [&](auto acc) {
     attn_fwd_kernel<D, PV, OUT, CAUSAL, SQ, decltype(acc)::value, NW, DUMP>
         <<<dim3((unsigned)grid), 64 * NW, 0, s>>>(a.q_i8, a.k_i8, a.v_t, a.q_scale, a.k_scale,
-                                                  a.v_scale, a.comp, BH, a.N, nqb, ntiles, remap,
+                                                  a.v_scale, a.comp, BH, a.N, qb_begin, nqb,
+                                                  ntiles, remap,
                                                   a.H, a.nhd, a.out, dw);
     return hipGetLastError();
   };

@@ -32,8 +32,25 @@ bool shape_ok(int B, int H, int N, int d) {
   return true;
 }
 
+// The smoothed-Q compensation values of one pass take at most this many bytes
+// of workspace; longer sequences compute them, and run the attention kernel,
+// in chunks of query blocks.
+constexpr size_t kSqCompMaxBytes = size_t(256) << 20;
+
+// 128-row query blocks per chunk of the smoothed-Q pass: all of them when the
+// whole table fits, else a multiple of 2 (the widest attention workgroup
+// covers 256 rows).
+int sq_chunk_blocks(int B, int H, int N) {
+  const size_t nq128 = ceil_div(N, sage::kQBlock), nt = ceil_div(N, sage::kKvTile);
+  const size_t per_block = (size_t)B * H * nt * sage::kKvTile * 4;
+  if (per_block * nq128 <= kSqCompMaxBytes) return (int)nq128;
+  const size_t c = (kSqCompMaxBytes / per_block) & ~size_t(1);
+  return (int)(c < 2 ? 2 : c);
+}
+
 // Workspace carve-up of sage_attn_fwd (private layout); with smoothed Q also
-// the block means, the integer means w and the compensation values.
+// the block means, the integer means w and the compensation values (of one
+// chunk of query blocks).
 struct Layout {
   size_t q_i8, k_i8, v_t, q_scale, k_scale, k_mean, v_scale, v_recip, part_sum, part_max;
   size_t q_mean, q_w, comp, total;
@@ -58,7 +75,7 @@ Layout make_layout(int B, int H, int N, int d, int pv_mode, bool sq = false) {
   L.part_max = take(sage::v_quantised(pv_mode) ? bh * nch * d * 4 : 0);
   L.q_mean = take(sq ? bh * nqb * d * 4 : 0);
   L.q_w = take(sq ? bh * nqb * d * 4 : 0);
-  L.comp = take(sq ? bh * nqb * nt * sage::kKvTile * 4 : 0);
+  L.comp = take(sq ? bh * (size_t)sq_chunk_blocks(B, H, N) * nt * sage::kKvTile * 4 : 0);
   L.total = off;
   return L;
 }
@@ -189,12 +206,20 @@ int run_fwd_sq(const void* q, const void* k, const void* v, void* o, int B, int 
   e = sage::launch_smooth_q(q, dtype, B, H, N, d, layout, q_i8, F(L.q_scale), F(L.q_mean), q_w,
                             s);
   if (e != hipSuccess) return SAGE_ERR_HIP;
-  e = sage::launch_sq_comp(k_i8, q_w, B, H, N, d, ceil_div(N, sage::kKvTile) * sage::kKvTile,
-                           pv_mode == SAGE_PV_FP16 ? sage::kSqBiasFp16 : 0, comp, s);
-  if (e != hipSuccess) return SAGE_ERR_HIP;
-  e = sage::launch_attn(q_i8, k_i8, v_t, F(L.q_scale), F(L.k_scale), F(L.v_scale), comp, B, H,
-                        N, d, causal, pv_mode, out_kind, layout, o, s);
-  return hip_status(e);
+  // the compensation values and the attention kernel, one chunk of query
+  // blocks at a time (one chunk unless the table passes kSqCompMaxBytes)
+  const int nq128 = ceil_div(N, sage::kQBlock), chunk = sq_chunk_blocks(B, H, N);
+  for (int q0 = 0; q0 < nq128; q0 += chunk) {
+    const int cnt = nq128 - q0 < chunk ? nq128 - q0 : chunk;
+    e = sage::launch_sq_comp(k_i8, q_w, B, H, N, d, ceil_div(N, sage::kKvTile) * sage::kKvTile,
+                             pv_mode == SAGE_PV_FP16 ? sage::kSqBiasFp16 : 0, comp, s, q0, cnt);
+    if (e != hipSuccess) return SAGE_ERR_HIP;
+    e = sage::launch_attn(q_i8, k_i8, v_t, F(L.q_scale), F(L.k_scale), F(L.v_scale), comp, B, H,
+                          N, d, causal, pv_mode, out_kind, layout, o, s, q0,
+                          q0 + cnt >= nq128 ? 0 : cnt);
+    if (e != hipSuccess) return SAGE_ERR_HIP;
+  }
+  return SAGE_OK;
 }
 
 }  // namespace
@@ -505,6 +530,9 @@ int sage_attn_debug_s_fwd(const void* workspace, size_t workspace_bytes, int B, 
     return SAGE_ERR_INVALID_ARG;
   const Layout L = make_layout(B, H, N, d, pv_mode, smooth_q == 1);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  // with Q smoothed the workspace holds the compensation values of the last
+  // chunk only: the whole table must have fit in one
+  if (smooth_q && sq_chunk_blocks(B, H, N) < ceil_div(N, sage::kQBlock)) return SAGE_ERR_UNSUPPORTED;
   int st = device_check();
   if (st != SAGE_OK) return st;
   const uint8_t* w = static_cast<const uint8_t*>(workspace);

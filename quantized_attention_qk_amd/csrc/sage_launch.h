@@ -90,10 +90,15 @@ hipError_t launch_prepass_head(const void* q, const void* k, const void* v, int 
 // token-major [B,N,H,d] instead of [B,H,N,d].  comp: null, or (Q smoothed per
 // block) the compensation values int32 [B*H, ceil(N/128), ceil(N/64)*64],
 // with FP16 mode's magic bias (kSqBiasFp16) already added in FP16 mode.
+// q128_begin, q128_count: only the query rows of 128-row blocks [q128_begin,
+// q128_begin + q128_count) of every head (count 0: to the last row); both
+// multiples of 2 (the widest workgroup covers 256 rows) unless the range
+// ends at N.  comp then holds those blocks only: [B*H, blocks in range, ld].
 hipError_t launch_attn(const int8_t* q_i8, const int8_t* k_i8, const uint8_t* v_t,
                        const float* q_scale, const float* k_scale, const float* v_scale,
                        const int32_t* comp, int B, int H, int N, int d, int causal, int pv_mode,
-                       int out_kind, int nhd, void* out, hipStream_t s);
+                       int out_kind, int nhd, void* out, hipStream_t s, int q128_begin = 0,
+                       int q128_count = 0);
 
 // Debug: the attention kernel's own dump instantiation on head (b, h) for the
 // query rows [q0, q0+nq): every INT32 score it computes for keys [k0, k0+nk)
@@ -119,6 +124,7 @@ struct AttnArgs {
   void* out;
   int32_t* s_dump;
   int dump_q0, dump_nq, dump_k0, dump_nk;
+  int q128_begin, q128_count;
 };
 
 // Smoothed Q (smooth_q.hip): per 128-token block the mean qbar is removed
@@ -128,8 +134,11 @@ struct AttnArgs {
 hipError_t launch_smooth_q(const void* q, int dtype, int B, int H, int N, int d, int nhd,
                            int8_t* q_i8, float* q_scale, float* q_mean, int32_t* q_w,
                            hipStream_t s);
+// Blocks [qb0, qb0 + nqr) only (nqr < 0: to the last block), written as
+// int32 [B*H, nqr, ld].
 hipError_t launch_sq_comp(const int8_t* k_i8, const int32_t* q_w, int B, int H, int N, int d,
-                          int ld, int bias, int32_t* comp, hipStream_t s);
+                          int ld, int bias, int32_t* comp, hipStream_t s, int qb0 = 0,
+                          int nqr = -1);
 // The FP16-mode accumulator start (bit pattern of 1.5 * 2^23) that the
 // compensation carries when it seeds the attention kernel's INT32 product.
 constexpr int kSqBiasFp16 = 0x4B400000;

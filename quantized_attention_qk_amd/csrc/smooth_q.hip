@@ -139,10 +139,12 @@ __global__ __launch_bounds__(256) void smooth_q_kernel(
 // build their blocks' digit operands once and walk the chunk's 32-key tiles,
 // so each K^ tile comes from HBM once and is shared in L2 by the wavefronts.
 constexpr int kSqChunk = 256;
+// Blocks [qb0, qb0 + nqr) of the nqb of each head; comp holds nqr rows of ld
+// values per head.
 template <int D>
 __global__ __launch_bounds__(256) void sq_comp_kernel(const int8_t* __restrict__ k_i8,
                                                       const int32_t* __restrict__ q_w, int N,
-                                                      int nqb, int ld, int bias,
+                                                      int nqb, int qb0, int nqr, int ld, int bias,
                                                       int32_t* __restrict__ comp) {
   constexpr int KT = D / 32;
   const int bh = blockIdx.y;
@@ -151,8 +153,10 @@ __global__ __launch_bounds__(256) void sq_comp_kernel(const int8_t* __restrict__
   const int c0 = blockIdx.x * kSqChunk;
   const int c1 = min(c0 + kSqChunk, ld);
   const bool vec = (ld & 3) == 0;   // rows 16-byte aligned: 16-byte stores
-  for (int g = wave; g * 32 < nqb; g += 4) {
-    const int qb = g * 32 + n;      // B column of this lane
+  for (int g = wave; g * 32 < nqr; g += 4) {
+    const int qr = g * 32 + n;      // B column of this lane: block qb0 + qr
+    const bool in = qr < nqr;
+    const int qb = qb0 + qr;
     // the digit operands of this lane's block: plane p, d-step kt
     v4i dig[4][KT];
 #pragma unroll
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(256) void sq_comp_kernel(const int8_t* __restrict__
       uint32_t dd[4][4] = {};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const v4i x = qb < nqb ? *reinterpret_cast<const v4i*>(
+        const v4i x = in ? *reinterpret_cast<const v4i*>(
                                      q_w + ((size_t)bh * nqb + qb) * D + 32 * kt + 16 * hh + 4 * j)
                                : v4i{0, 0, 0, 0};
 #pragma unroll
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(256) void sq_comp_kernel(const int8_t* __restrict__
       for (int p = 0; p < 4; ++p)
         dig[p][kt] = v4i{(int)dd[p][0], (int)dd[p][1], (int)dd[p][2], (int)dd[p][3]};
     }
-    int32_t* out = comp + ((size_t)bh * nqb + qb) * ld;
+    int32_t* out = comp + ((size_t)bh * nqr + qr) * ld;
     // A operand (this lane's key row of K^) of a 32-key tile; the next
     // tile's is loaded while the current one is multiplied
     auto load_a = [&](int t0, v4i (&a)[KT]) __attribute__((always_inline)) {
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(256) void sq_comp_kernel(const int8_t* __restrict__
 #pragma unroll
         for (int p = 0; p < 4; ++p)
           acc[p] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[kt], dig[p][kt], acc[p], 0, 0, 0);
-      if (qb >= nqb) continue;
+      if (!in) continue;
       int cv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -251,13 +255,14 @@ hipError_t launch_smooth_q(const void* q, int dtype, int B, int H, int N, int d,
 }
 
 hipError_t launch_sq_comp(const int8_t* k_i8, const int32_t* q_w, int B, int H, int N, int d,
-                          int ld, int bias, int32_t* comp, hipStream_t s) {
+                          int ld, int bias, int32_t* comp, hipStream_t s, int qb0, int nqr) {
   const int nqb = ceil_div(N, kQBlock);
+  if (nqr < 0) nqr = nqb - qb0;
   dim3 grid(ceil_div(ld, kSqChunk), B * H);
   if (d == 64)
-    sq_comp_kernel<64><<<grid, 256, 0, s>>>(k_i8, q_w, N, nqb, ld, bias, comp);
+    sq_comp_kernel<64><<<grid, 256, 0, s>>>(k_i8, q_w, N, nqb, qb0, nqr, ld, bias, comp);
   else if (d == 128)
-    sq_comp_kernel<128><<<grid, 256, 0, s>>>(k_i8, q_w, N, nqb, ld, bias, comp);
+    sq_comp_kernel<128><<<grid, 256, 0, s>>>(k_i8, q_w, N, nqb, qb0, nqr, ld, bias, comp);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
