@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--mfma-probe", action="store_true",
                     help="only run the micro-benchmarks of libsage_probe.so: sustained INT8, "
                          "FP16 and FP8 MFMA rates with the clock they ran at, and the issue "
-                         "cost of VALU work next to a stream of MFMAs")
+                         "cost of VALU work and the LDS read bandwidth next to a stream of MFMAs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES (3 launches), to calibrate "
                          "the HBM byte counters against a known traffic")
@@ -157,6 +157,8 @@ def main():
         from quantized_attention_qk_amd import probe
         print(json.dumps({"mfma_rates": probe.mfma_rates()}), flush=True)
         for row in probe.issue_table():
+            print(json.dumps(row), flush=True)
+        for row in probe.lds_table():
             print(json.dumps(row), flush=True)
         return
 

@@ -42,6 +42,17 @@ enum { SAGE_PROBE_NONE = -1, SAGE_PROBE_MFMA_I8 = 0, SAGE_PROBE_MFMA_F16 = 1,
 int sage_probe_run(int mfma_kind, int nv, int ne, int waves_per_simd, int ncu, int iters,
                    long long* stamps, float* sink, void* stream);
 
+/*
+ * LDS read bandwidth next to MFMAs: the same launch, stamps and sink, but
+ * each group issues one MFMA of `mfma_kind` (none for SAGE_PROBE_NONE) and
+ * nl (1, 2 or 4) independent ds_read_b128, each moving 1 KiB per wavefront
+ * (consecutive 16-byte lanes, no bank conflicts) from the workgroup's LDS; a
+ * group consumes the reads issued four groups earlier.  Returns as
+ * sage_probe_run (2 for an unsupported nl).
+ */
+int sage_probe_run_lds(int mfma_kind, int nl, int waves_per_simd, int ncu, int iters,
+                       long long* stamps, float* sink, void* stream);
+
 /* Rate of the s_memrealtime counter in kHz; the device's CU count. */
 int sage_probe_wallclock_khz(int* khz);
 int sage_probe_cu_count(int* ncu);

@@ -283,7 +283,8 @@ struct PTile<kPvInt8> {
 // Four floats in [0, 255] -> four u8 codes, round to nearest even
 // (v_cvt_pk_u8_f32), first value in the low byte.
 __device__ __forceinline__ uint32_t pack_u8x4(float a, float b, float c, float d) {
-  uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(a, 0u, 0u);
+  // every byte is written below, so the register may be a's own
+  uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(a, 0u, __builtin_bit_cast(uint32_t, a));
   w = __builtin_amdgcn_cvt_pk_u8_f32(b, 1u, w);
   w = __builtin_amdgcn_cvt_pk_u8_f32(c, 2u, w);
   return __builtin_amdgcn_cvt_pk_u8_f32(d, 3u, w);

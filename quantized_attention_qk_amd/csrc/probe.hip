@@ -131,6 +131,92 @@ hipError_t launch_mix(int nv, int ne, int wps, int ncu, int iters, int seed, lon
   return hipErrorInvalidValue;
 }
 
+// LDS read bandwidth next to MFMAs: every wavefront runs `iters` groups of
+// [one MFMA of kind K (K < 0: none), NL independent ds_read_b128], each read
+// moving 1 KiB (64 lanes x 16 bytes, consecutive addresses, no bank
+// conflicts) from the workgroup's LDS claim.  A group consumes the reads
+// issued four groups earlier, so each read has four groups' time to land.
+template <int K, int NL, int WPS>
+__global__ __launch_bounds__(256) void probe_lds_kernel(int iters, int seed,
+                                                       long long* __restrict__ stamps,
+                                                       float* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) float claim[kLdsClaim<WPS> / 4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  for (int i = tid; i < kLdsClaim<WPS> / 4; i += 256) claim[i] = (float)(seed + i);
+  v8i a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = 0x38383838 ^ (seed + i + tid);
+    b[i] = 0x30303030 ^ (seed - i + tid);
+  }
+  v16f acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = v16f{};
+  v4i r[kChains][NL];
+#pragma unroll
+  for (int h = 0; h < kChains; ++h)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) r[h][i] = v4i{};
+  const char* lds = reinterpret_cast<const char*>(claim);
+  __syncthreads();
+
+  const long long c0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; it += kChains) {
+    // a 32 KiB window that moves every trip; the groups' reads sit at fixed
+    // offsets from it (at most 16 KiB further), inside the 64 KiB claim
+    const int base = (lane * 16 + it * (NL * 1024)) & 0x7fff;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+      if constexpr (K >= 0) acc[c] = mfma<K>(a, b, acc[c]);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        asm volatile("" ::"v"(r[c][i]));
+        r[c][i] = *reinterpret_cast<const v4i*>(lds + base + (c * NL + i) * 1024);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  const long long c1 = __builtin_amdgcn_s_memtime();
+  const long long r1 = __builtin_amdgcn_s_memrealtime();
+
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) s += acc[c][tid & 15];
+#pragma unroll
+  for (int h = 0; h < kChains; ++h)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) s += (float)(r[h][i][0] ^ r[h][i][3]);
+  sink[blockIdx.x * 256 + tid] = s;
+  if ((tid & 63) == 0) {
+    const size_t w = (size_t)blockIdx.x * 4 + (tid >> 6);
+    stamps[4 * w + 0] = c0;
+    stamps[4 * w + 1] = c1;
+    stamps[4 * w + 2] = r0;
+    stamps[4 * w + 3] = r1;
+  }
+}
+
+template <int K, int NL>
+hipError_t launch_lds(int wps, int ncu, int iters, int seed, long long* stamps, float* sink,
+                      hipStream_t s) {
+  if (wps == 1)
+    probe_lds_kernel<K, NL, 1><<<dim3(ncu), 256, 0, s>>>(iters, seed, stamps, sink);
+  else
+    probe_lds_kernel<K, NL, 2><<<dim3(ncu * 2), 256, 0, s>>>(iters, seed, stamps, sink);
+  return hipGetLastError();
+}
+
+template <int K>
+hipError_t launch_lds_n(int nl, int wps, int ncu, int iters, int seed, long long* stamps,
+                        float* sink, hipStream_t s) {
+  if (nl == 1) return launch_lds<K, 1>(wps, ncu, iters, seed, stamps, sink, s);
+  if (nl == 2) return launch_lds<K, 2>(wps, ncu, iters, seed, stamps, sink, s);
+  if (nl == 4) return launch_lds<K, 4>(wps, ncu, iters, seed, stamps, sink, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,6 +248,23 @@ int sage_probe_run(int mfma_kind, int nv, int ne, int waves_per_simd, int ncu, i
     case SAGE_PROBE_MFMA_I8: e = launch_mix<SAGE_PROBE_MFMA_I8>(nv, ne, waves_per_simd, ncu, iters, 1, stamps, sink, s); break;
     case SAGE_PROBE_MFMA_F16: e = launch_mix<SAGE_PROBE_MFMA_F16>(nv, ne, waves_per_simd, ncu, iters, 1, stamps, sink, s); break;
     case SAGE_PROBE_MFMA_F8: e = launch_mix<SAGE_PROBE_MFMA_F8>(nv, ne, waves_per_simd, ncu, iters, 1, stamps, sink, s); break;
+    default: return 1;
+  }
+  return e == hipSuccess ? 0 : (e == hipErrorInvalidValue ? 2 : 4);
+}
+
+int sage_probe_run_lds(int mfma_kind, int nl, int waves_per_simd, int ncu, int iters,
+                       long long* stamps, float* sink, void* stream) {
+  if (waves_per_simd != 1 && waves_per_simd != 2) return 1;
+  if (ncu < 1 || ncu > 4096 || iters < kChains || iters % kChains) return 1;
+  if (!stamps || !sink) return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (mfma_kind) {
+    case SAGE_PROBE_NONE: e = launch_lds_n<-1>(nl, waves_per_simd, ncu, iters, 1, stamps, sink, s); break;
+    case SAGE_PROBE_MFMA_I8: e = launch_lds_n<SAGE_PROBE_MFMA_I8>(nl, waves_per_simd, ncu, iters, 1, stamps, sink, s); break;
+    case SAGE_PROBE_MFMA_F16: e = launch_lds_n<SAGE_PROBE_MFMA_F16>(nl, waves_per_simd, ncu, iters, 1, stamps, sink, s); break;
+    case SAGE_PROBE_MFMA_F8: e = launch_lds_n<SAGE_PROBE_MFMA_F8>(nl, waves_per_simd, ncu, iters, 1, stamps, sink, s); break;
     default: return 1;
   }
   return e == hipSuccess ? 0 : (e == hipErrorInvalidValue ? 2 : 4);

@@ -53,8 +53,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 // Four floats -> four OCP E4M3 codes (v_cvt_pk_fp8_f32, round to nearest even).
+// The first conversion writes the low half of a register whose high half
+// the second one overwrites, so that register may be a's own (no clearing
+// or copying instruction).
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }

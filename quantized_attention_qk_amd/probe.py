@@ -6,6 +6,8 @@ mfma_rates(): sustained INT8, FP16 and FP8 MFMA rates with every SIMD busy,
 issue_table(): cycles per group of [one MFMA + nv v_fma_f32 + ne v_exp_f32]
               per SIMD, with one or two wavefronts per SIMD -- how much VALU
               work hides under a stream of MFMAs.
+lds_table():  LDS read bandwidth (16-byte reads per lane) alone and next to a
+              stream of MFMAs.
 """
 from __future__ import annotations
 
@@ -32,6 +34,8 @@ def lib() -> ctypes.CDLL:
         h = ctypes.CDLL(PROBE_PATH)
         h.sage_probe_run.restype = ctypes.c_int
         h.sage_probe_run.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 3
+        h.sage_probe_run_lds.restype = ctypes.c_int
+        h.sage_probe_run_lds.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p] * 3
         for name in ("sage_probe_wallclock_khz", "sage_probe_cu_count"):
             getattr(h, name).restype = ctypes.c_int
             getattr(h, name).argtypes = [ctypes.POINTER(ctypes.c_int)]
@@ -48,9 +52,12 @@ def _query(name: str) -> int:
 
 
 def run(kind: int, nv: int = 0, ne: int = 0, wps: int = 2, iters: int = 16384,
-        repeats: int = 3) -> dict:
+        repeats: int = 3, nl: int = 0) -> dict:
     """One probe configuration on every CU; the last of `repeats` launches is
-    measured.  Returns the wall time, the clock and per-SIMD cycle counts."""
+    measured.  Returns the wall time, the clock and per-SIMD cycle counts.
+    nl > 0: the LDS probe (nl 16-byte reads per lane and group, nv = ne = 0)."""
+    if nl and (nv or ne):
+        raise ValueError("the LDS probe runs no VALU groups")
     ncu = _query("sage_probe_cu_count")
     rt_khz = _query("sage_probe_wallclock_khz")
     nwaves = 4 * ncu * wps
@@ -61,10 +68,14 @@ def run(kind: int, nv: int = 0, ne: int = 0, wps: int = 2, iters: int = 16384,
     for r in range(repeats):
         if r == repeats - 1:
             e0.record(stream)
-        rc = lib().sage_probe_run(kind, nv, ne, wps, ncu, iters, stamps.data_ptr(),
-                                  sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        if nl:
+            rc = lib().sage_probe_run_lds(kind, nl, wps, ncu, iters, stamps.data_ptr(),
+                                          sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        else:
+            rc = lib().sage_probe_run(kind, nv, ne, wps, ncu, iters, stamps.data_ptr(),
+                                      sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
         if rc != 0:
-            raise RuntimeError(f"sage_probe_run({kind}, {nv}, {ne}, {wps}) failed ({rc})")
+            raise RuntimeError(f"probe ({kind}, nv={nv}, ne={ne}, nl={nl}, {wps}) failed ({rc})")
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
@@ -72,10 +83,14 @@ def run(kind: int, nv: int = 0, ne: int = 0, wps: int = 2, iters: int = 16384,
     cyc = (st[:, 1] - st[:, 0])
     rtt = (st[:, 3] - st[:, 2])
     clock_ghz = float((cyc / rtt).median()) * rt_khz * 1e3 / 1e9
-    res = {"mfma": NAMES[kind], "nv": nv, "ne": ne, "waves_per_simd": wps, "iters": iters,
+    res = {"mfma": NAMES[kind], "nv": nv, "ne": ne, "nl": nl, "waves_per_simd": wps, "iters": iters,
            "cus": ncu, "ms": round(ms, 4), "clock_ghz": round(clock_ghz, 3),
            # one SIMD runs wps wavefronts of `iters` groups each
            "cycles_per_group_per_simd": round(float(cyc.median()) / (iters * wps), 2)}
+    if nl:
+        # 1 KiB per read and wavefront; per CU and shader clock
+        res["lds_bytes_per_clk_per_cu"] = round(
+            1024.0 * nl * iters * 4 * wps / float(cyc.median()), 1)
     if kind != NONE:
         ops = OPS_PER_MFMA[kind] * iters * nwaves
         res["tops"] = round(ops / (ms * 1e-3) / 1e12, 1)
@@ -105,4 +120,14 @@ def issue_table(kinds=(NONE, F16, I8), wps_list=(1, 2)) -> list[dict]:
                 if kind == NONE and nv == 0 and ne == 0:
                     continue
                 rows.append(run(kind, nv, ne, wps=wps, iters=8192, repeats=2))
+    return rows
+
+
+def lds_table(kinds=(NONE, F16, I8), nls=(1, 2, 4), wps_list=(1, 2)) -> list[dict]:
+    """LDS read bandwidth alone (kind NONE) and with one MFMA per group."""
+    rows = []
+    for kind in kinds:
+        for wps in wps_list:
+            for nl in nls:
+                rows.append(run(kind, wps=wps, iters=8192, repeats=2, nl=nl))
     return rows

@@ -318,7 +318,8 @@ def test_probe_library_exports():
     src = open(os.path.join(ROOT, "include", "sage_probe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", src)))
-    assert names == ["sage_probe_cu_count", "sage_probe_run", "sage_probe_wallclock_khz"]
+    assert names == ["sage_probe_cu_count", "sage_probe_run", "sage_probe_run_lds",
+                     "sage_probe_wallclock_khz"]
     h = probe.lib()
     for n in names:
         assert hasattr(h, n), n
@@ -326,6 +327,10 @@ def test_probe_library_exports():
     assert h.sage_probe_run(0, 0, 0, 3, 256, 1024, P, P, None) == 1
     assert h.sage_probe_run(0, 0, 0, 2, 256, 1023, P, P, None) == 1
     assert h.sage_probe_run(5, 0, 0, 2, 256, 1024, P, P, None) == 1
+    assert h.sage_probe_run_lds(1, 1, 3, 256, 1024, P, P, None) == 1
+    assert h.sage_probe_run_lds(1, 1, 2, 256, 1022, P, P, None) == 1
+    assert h.sage_probe_run_lds(7, 1, 2, 256, 1024, P, P, None) == 1
+    assert h.sage_probe_run_lds(1, 3, 2, 256, 1024, P, P, None) == 2   # nl not 1, 2, 4
 
 
 def test_noalloc_validation():
