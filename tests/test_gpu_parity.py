@@ -249,9 +249,14 @@ def test_stages_equal_whole_pass(wl):
 # The five full workloads, at their real sizes and in the launch configuration
 # the benchmark times.
 def sample_rows(N, causal, seed):
+    """Edge rows, 24 seeded rows, and every row of one seeded 256-row span
+    (aligned, so all 32 lanes of all eight wavefronts of one workgroup, or of
+    two 128-row workgroups)."""
     rng = np.random.default_rng(seed)
     rows = {0, 1, 63, 64, 127, 128, N - 1, N - 2, N // 2, (N // 128) * 128 - 1}
     rows |= set(int(x) for x in rng.integers(0, N, 24))
+    span = 256 * int(rng.integers(0, max(1, N // 256)))
+    rows |= set(range(span, span + 256))
     return np.array(sorted(r for r in rows if 0 <= r < N))
 
 
