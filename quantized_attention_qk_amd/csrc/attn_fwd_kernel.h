@@ -895,9 +895,21 @@ __device__ __forceinline__ void dump_tile(const DumpWin& dw, const v16i (&s)[2],
 // NW wavefronts per workgroup (32 query rows each): 4, one delta_Q block, or
 // 8 (two blocks; FP16 P~V, d = 128, non-causal), where every K^ and V tile
 // copied into LDS serves twice the rows.
+//
+// Wavefronts per SIMD: two (up to 256 registers each), or three (168) for
+// FP8 and INT8-sum P~V at d = 64 without smoothed Q, whose steps are
+// VALU-bound (6 or 8 MFMAs against about 200 VALU instructions): a third
+// wavefront fills more of the VALU's idle issue cycles (c4 -2%, c4i8 -4%).
+// Their steady-state loops keep every value in registers; the spills are in
+// the tail steps.
+template <int D, int PV, bool ACC, bool SQ>
+constexpr int kWavesPerSimd =
+    D == 64 && !SQ && (PV == kPvFp8 || (PV == kPvInt8 && ACC)) ? 3 : 2;
+
 template <int D, int PV, int OUT, bool CAUSAL, bool SQ, bool ACC, int NW, bool DUMP>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
-                          amdgpu_waves_per_eu(2, 2)))
+                          amdgpu_waves_per_eu(kWavesPerSimd<D, PV, ACC, SQ>,
+                                              kWavesPerSimd<D, PV, ACC, SQ>)))
 void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__ k_i8,
                      const uint8_t* __restrict__ v_t, const float* __restrict__ q_scale,
                      const float* __restrict__ k_scale, const float* __restrict__ v_scale,
