@@ -329,6 +329,7 @@ __device__ __forceinline__ void qk_tile(v16i (&s)[2], const v4i (&qf)[D / 32], c
 // the argument is the correctly rounded s c - m as before.
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+constexpr int kNegInfBits = (int)0xFF800000u;   // -infinity
 
 // Grid of the FP16-mode running max: step (a power of two) and 1/step.
 struct MaxGrid {
@@ -398,8 +399,16 @@ __device__ __forceinline__ float softmax_tile(v16i (&s)[2], float& m_run, float&
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        // FP16: the biased scores are positive floats, 0 is below all of them
-        if (!((keep >> (16 * blk + r)) & 1u)) s[blk][r] = F16 ? 0 : INT32_MIN;
+        // FP16: the biased scores are positive floats and a hidden one
+        // becomes -infinity, below all of them as an integer too, whose exp
+        // is exactly 0 (for c > 0, below)
+        if (!((keep >> (16 * blk + r)) & 1u)) s[blk][r] = F16 ? kNegInfBits : INT32_MIN;
+  }
+  if constexpr (MASK && F16) {
+    // c = 0 (an all-zero delta_Q or delta_K block) would turn -inf * c into
+    // NaN; the smallest normal float gives the same exps to float precision
+    ts.c = fmaxf(ts.c, __FLT_MIN__);
+    ts.k0 = kMagic * ts.c;
   }
   // row max: chain of 3-input maxima over the lane's 32 scores, then the pair
   // (in FP16 mode on the bit patterns of positive floats, which order alike)
@@ -438,7 +447,7 @@ __device__ __forceinline__ float softmax_tile(v16i (&s)[2], float& m_run, float&
       const int si = s[blk][r];
       const float x = F16 ? __builtin_bit_cast(float, si) : (float)si;
       float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x, ts.c, nb));
-      if constexpr (MASK) e = ((keep >> (16 * blk + r)) & 1u) ? e : 0.f;
+      if constexpr (MASK && !F16) e = ((keep >> (16 * blk + r)) & 1u) ? e : 0.f;
       p[blk][r] = e;
       if constexpr (!F16) ls[r & 3] += e;
     }
