@@ -160,9 +160,10 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
  * SAGE_LAYOUT_NHD; out_f32 0/1); the workspace must hold
  * sage_attn_sq_workspace_bytes(...) bytes.  It adds ceil(N/64) * 64 int32
  * compensation values per head and 128-row query block, about N^2/32 bytes per
- * head (8 MiB at N = 16384), capped at 256 MiB in all: beyond that the pass
- * computes them, and runs the attention kernel, in chunks of query blocks
- * (N = 131072 on one head: three chunks instead of a 512 MiB table).
+ * head (8 MiB at N = 16384), up to 256 MiB in all (or two query blocks of
+ * every head where that is more): beyond that the pass computes them, and runs the
+ * attention kernel, in chunks of query blocks (N = 131072 on one head: two
+ * chunks of 512 blocks instead of a 512 MiB table).
  */
 size_t sage_attn_sq_workspace_bytes(int B, int H, int N, int d, int pv_mode);
 int sage_attn_fwd_sq(const void* q, const void* k, const void* v, void* o,

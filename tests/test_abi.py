@@ -226,6 +226,34 @@ def test_layout_and_rope_validation():
         assert h.sage_quant_v_ex(P, 0, 1, 1, 1, 300, 64, 0, P, None, P, 1 << 30, None) == NO_DEVICE
 
 
+def test_smooth_q_workspace_chunks():
+    """The smoothed-Q seed table: int32 values for ceil(N/64)*64 keys per head
+    and 128-row query block, all blocks while that stays within 256 MiB, else
+    an even number of blocks per chunk (at least two).  The difference between
+    the two workspace sizes is that table plus q-bar and w (2 x d x 4 bytes per
+    block and head) and their 256-byte slice alignment."""
+    h = lib()
+    MiB = 1 << 20
+
+    def table(B, H, N, d):
+        return h.sage_attn_sq_workspace_bytes(B, H, N, d, 0) - h.sage_attn_workspace_bytes(B, H, N, d, 0)
+
+    def expect(B, H, N, d, blocks):
+        nt64 = -(-N // 64) * 64
+        extra = B * H * blocks * nt64 * 4 + 2 * B * H * (-(-N // 128)) * d * 4
+        return extra
+
+    # c3's shape: one chunk, 201 MB of seeds
+    assert abs(table(1, 24, 16384, 128) - expect(1, 24, 16384, 128, 128)) <= 3 * 256
+    # one head of 2^17 tokens: 1024 blocks of 512 KiB would be 512 MiB -> 512 per chunk
+    assert abs(table(1, 1, 1 << 17, 128) - expect(1, 1, 1 << 17, 128, 512)) <= 3 * 256
+    # 2^17 + 17 tokens: 2049 key tiles, 256 MiB holds 511 blocks -> 510 (even)
+    assert abs(table(1, 1, (1 << 17) + 17, 128) - expect(1, 1, (1 << 17) + 17, 128, 510)) <= 3 * 256
+    assert table(1, 1, (1 << 17) + 17, 128) < 260 * MiB
+    # many heads at a long N: one block of every head exceeds 256 MiB -> two per chunk
+    assert abs(table(4, 32, 1 << 20, 64) - expect(4, 32, 1 << 20, 64, 2)) <= 3 * 256
+
+
 def test_smooth_q_entries_validation():
     # sage_attn_fwd_sq: q, k, v, o, B, H, N, d, causal, pv, dtype, layout, out_f32, ws, bytes, stream
     h = lib()
