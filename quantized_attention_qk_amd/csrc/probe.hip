@@ -1,7 +1,8 @@
 // probe.hip -- micro-benchmarks of the gfx950 units the attention kernel
 // leans on: the sustained rate of the three MFMA shapes it issues, the issue
-// cost of v_exp_f32 next to v_fma_f32, and how VALU work overlaps a stream of
-// MFMAs with one or two wavefronts per SIMD.  Every wavefront also stamps its
+// cost of v_exp_f32 next to v_fma_f32, how VALU work overlaps a stream of
+// MFMAs with one or two wavefronts per SIMD, and the LDS read bandwidth alone
+// and next to MFMAs.  Every wavefront also stamps its
 // loop with the shader clock (s_memtime) and the constant-rate real-time
 // counter (s_memrealtime), so the host can derive the clock the chip ran at.
 //
