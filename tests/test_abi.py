@@ -321,6 +321,12 @@ def test_debug_s_fwd_validation():
     assert call(a5=96) == UNSUPPORTED
     assert call(a1=need - 1) == WORKSPACE
     assert call(a8=1, a1=need) == WORKSPACE     # Q smoothed needs the larger workspace
+    # Q smoothed on a head whose seed table took more than one chunk: the
+    # workspace holds the last chunk only, so the scores cannot be rebuilt
+    NL = (1 << 17) + 17
+    need_long = h.sage_attn_sq_workspace_bytes(1, 1, NL, 128, 0)
+    assert h.sage_attn_debug_s_fwd(ws, need_long, 1, 1, NL, 128, 0, 0, 1, 0, 0, 0, 128, 0, 64,
+                                   P, P + 0x1000, None) == UNSUPPORTED
     if not torch.cuda.is_available():
         assert call() == NO_DEVICE
         assert call(a8=1, a1=need_sq) == NO_DEVICE
