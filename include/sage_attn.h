@@ -306,6 +306,20 @@ int sage_attn_debug_s_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, 
                           void* stream);
 
 /*
+ * The prepass of sage_attn_fwd alone ([SA] §4 Eq. 6 and §3 Algorithm 1 up to
+ * the quantised operands: K smoothed by its column mean, Q^ and K^ in INT8 per
+ * block with delta_Q, delta_K, and V prepared for the P~V mode): fills the
+ * private workspace exactly as sage_attn_fwd does before its attention kernel,
+ * and launches no attention.  For sage_attn_debug_s_fwd on shapes where the
+ * whole attention would take too long to run just to fill the workspace (a
+ * head of 2^24 tokens).  Arguments, validation and errors as sage_attn_fwd
+ * (SAGE_LAYOUT_HND, no output pointer, causal irrelevant).
+ */
+int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                      int pv_mode, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * Debug: the INT32 scores of the timed attention kernel itself ([SA] §3
  * Algorithm 1: S = Q^ K^^T in INT32).  Re-runs the attention kernel's debug
  * instantiation -- the same source, instruction schedule, LDS staging and
@@ -313,9 +327,9 @@ int sage_attn_debug_s_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, 
  * starts every INT32 accumulation at the bit pattern of 1.5 * 2^23; with Q
  * smoothed, at the compensation values of sage_attn_fwd_sq) -- for head (b, h)
  * and the query rows [q0, q0 + nq), on the operands that a preceding
- * sage_attn_fwd / sage_attn_fwd_ex (smooth_q = 0) or sage_attn_fwd_sq
- * (smooth_q = 1) call with the same B, H, N, d, causal, pv_mode left in
- * `workspace`.  Writes
+ * sage_attn_fwd / sage_attn_fwd_ex / sage_attn_prepare (smooth_q = 0) or
+ * sage_attn_fwd_sq (smooth_q = 1) call with the same B, H, N, d, pv_mode (and
+ * causal, for the forward calls) left in `workspace`.  Writes
  *   s_out  int32 [nq, nk] row-major: for query q0 + i and key k0 + j of a KV
  *          tile the kernel computes for that row, the accumulator minus its
  *          start bias, i.e. S = Q^ K^^T (S + C with Q smoothed, C as in

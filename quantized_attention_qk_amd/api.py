@@ -243,6 +243,17 @@ def debug_s_i32(q_i8: torch.Tensor, k_i8: torch.Tensor, b: int, h: int, q0: int,
 S_NOT_COMPUTED = -(2 ** 31)   # entries of debug_s_fwd's S the kernel did not compute
 
 
+def prepare(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pv_mode: str,
+            workspace: torch.Tensor) -> None:
+    """The prepass of sage_attn alone (sage_attn_prepare): leaves the quantised
+    operands in `workspace` for debug_s_fwd and launches no attention.  q, k, v
+    contiguous [B, H, N, d] fp16/bf16 on the GPU."""
+    B, H, N, d = _check_qkv(q, k, v)
+    check(lib().sage_attn_prepare(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d,
+                                  SAGE_PV[pv_mode], SAGE_DT[q.dtype], workspace.data_ptr(),
+                                  workspace.numel(), _stream_ptr(q.device)), "sage_attn_prepare")
+
+
 def debug_s_fwd(workspace: torch.Tensor, B: int, H: int, N: int, d: int, causal: bool,
                 pv_mode: str, smooth_q: bool, b: int, h: int, q0: int, nq: int, k0: int,
                 nk: int):

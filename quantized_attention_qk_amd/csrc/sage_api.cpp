@@ -118,11 +118,13 @@ int validate_in(int layout, const float* rope_cos, const float* rope_sin) {
   return SAGE_OK;
 }
 
+// need_o = false: the prepass alone (sage_attn_prepare), o is not used.
 int validate_fwd(const void* q, const void* k, const void* v, const void* o, int B, int H, int N,
                  int d, int causal, int pv_mode, int dtype, const void* ws, size_t ws_bytes,
-                 bool sq = false) {
-  if (!q || !k || !v || !o || !ws) return SAGE_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SAGE_ERR_INVALID_ARG;
+                 bool sq = false, bool need_o = true) {
+  if (!q || !k || !v || (need_o && !o) || !ws) return SAGE_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (need_o && !aligned16(o)))
+    return SAGE_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return SAGE_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
   if (!sage::pv_valid(pv_mode)) return SAGE_ERR_INVALID_ARG;
@@ -130,15 +132,17 @@ int validate_fwd(const void* q, const void* k, const void* v, const void* o, int
   if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
   if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
-  if (o == q || o == k || o == v) return SAGE_ERR_INVALID_ARG;
+  if (need_o && (o == q || o == k || o == v)) return SAGE_ERR_INVALID_ARG;
   if (ws_bytes < make_layout(B, H, N, d, pv_mode, sq).total) return SAGE_ERR_WORKSPACE;
   return SAGE_OK;
 }
 
+// out_kind < 0: the prepass alone (the workspace's operands, no attention).
 int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
             int causal, int pv_mode, int dtype, int layout, const float* rope_cos,
             const float* rope_sin, void* ws, size_t ws_bytes, void* stream, int out_kind) {
-  int st = validate_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, ws, ws_bytes);
+  int st = validate_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, ws, ws_bytes, false,
+                        out_kind >= 0);
   if (st != SAGE_OK) return st;
   if ((st = validate_in(layout, rope_cos, rope_sin)) != SAGE_OK) return st;
   const sage::InLayout in{layout, rope_cos, rope_sin};
@@ -168,6 +172,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, 
     e = sage::launch_prep_v(v, F(L.v_recip), dtype, B, H, N, d, pv_mode, layout, v_t, s);
     if (e != hipSuccess) return SAGE_ERR_HIP;
   }
+  if (out_kind < 0) return SAGE_OK;
   e = sage::launch_attn(q_i8, k_i8, v_t, F(L.q_scale), F(L.k_scale), F(L.v_scale), nullptr, B,
                         H, N, d, causal, pv_mode, out_kind, layout, o, s);
   return hip_status(e);
@@ -261,6 +266,13 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
                   size_t workspace_bytes, void* stream) {
   return run_fwd(q, k, v, o, B, H, N, d, causal, pv_mode, dtype, SAGE_LAYOUT_HND, nullptr,
                  nullptr, workspace, workspace_bytes, stream, dtype == SAGE_DT_BF16 ? 1 : 0);
+}
+
+int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                      int pv_mode, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return run_fwd(q, k, v, nullptr, B, H, N, d, 0, pv_mode, dtype, SAGE_LAYOUT_HND, nullptr,
+                 nullptr, workspace, workspace_bytes, stream, -1);
 }
 
 int sage_attn_fwd_f32out(const void* q, const void* k, const void* v, float* o, int B, int H,

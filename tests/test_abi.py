@@ -293,6 +293,31 @@ def test_smooth_q_entries_validation():
         assert h.sage_attn_fwd_quantized_sq(*qargs) == NO_DEVICE
 
 
+def test_prepare_validation():
+    # q, k, v, B, H, N, d, pv, dtype, workspace, bytes, stream
+    h = lib()
+    ws = P + 0x100000
+    need = h.sage_attn_workspace_bytes(1, 2, 100, 64, 0)
+    base = [P, P + 0x1000, P + 0x2000, 1, 2, 100, 64, 0, 0, ws, need, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return h.sage_attn_prepare(*a)
+    assert call(a0=None) == INVALID
+    assert call(a2=P + 4) == INVALID            # v not 16-byte aligned
+    assert call(a9=P + 16) == INVALID           # workspace not 256-byte aligned
+    assert call(a7=3) == INVALID
+    assert call(a8=2) == INVALID
+    assert call(a5=0) == INVALID
+    assert call(a6=96) == UNSUPPORTED
+    assert call(a5=(1 << 24) + 1) == UNSUPPORTED
+    assert call(a10=need - 1) == WORKSPACE
+    if not torch.cuda.is_available():
+        assert call() == NO_DEVICE
+
+
 def test_debug_s_fwd_validation():
     # workspace, bytes, B, H, N, d, causal, pv, smooth_q, b, h, q0, nq, k0, nk, s_out, o_rows, stream
     h = lib()

@@ -23,7 +23,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import make_inputs, named, small
+from workloads import make_inputs, make_inputs_uniform, named, small
 
 pytestmark = pytest.mark.gpu
 
@@ -170,3 +170,60 @@ def test_s_exact_long_head():
         for (k0, nk) in ((0, 4096), (N - 4096, 4096)):
             note(f"  rows from {q0}, keys [{k0},{k0 + nk})")
             check_window(wl, inp, ws, pq, 0, 0, q0, min(QROWS, N - q0), k0, nk, o_full)
+
+
+def test_s_exact_max_length():
+    """One head of 2^24 tokens, the longest the library takes (d = 128, FP16
+    P~V: K^ spans 2^31 bytes, V' 4 GiB).  Q is drawn on its first and last
+    128-token blocks and zero elsewhere.  The prepass alone fills the workspace
+    (sage_attn_prepare; the whole attention would take minutes), then the timed
+    kernel's debug launch runs the first and the last query block over all
+    2^24 keys: its INT32 scores on the first and last 4096 keys equal the
+    oracle's, and O of sampled rows of those blocks is within the 2e-3 bar of
+    the oracle's attention over all keys."""
+    N = 1 << 24
+    wl = small("sxmax", B=1, H=1, N=N, d=128, dtype="fp16", seed=37)
+    spans = [(0, QROWS), (N - QROWS, QROWS)]
+    note(f"max length: drawing inputs {wl} (uniform in [-2, 2), Q on two blocks)")
+    inp = make_inputs_uniform(wl, q_spans=spans)
+    q, k, v = inp.torch_tensors("cuda")
+    ws = torch.empty(qa().workspace_bytes(1, 1, N, 128, "fp16"), dtype=torch.uint8, device="cuda")
+    note("max length: prepass on the GPU")
+    qa().prepare(q, k, v, "fp16", ws)
+    torch.cuda.synchronize()
+    del q, k, v
+    # the oracle's prepass of K (all tokens) and of the two Q blocks (a Q
+    # block's codes and scale depend on that block alone)
+    note("max length: oracle prepass")
+    q_sub = np.concatenate([inp.qf[:, :, t0:t0 + c] for (t0, c) in spans], axis=2)
+    pq = oracle.smooth_quant_qk(q_sub, inp.kf)
+    o_rows = {}
+    for i, (q0, _) in enumerate(spans):
+        for (k0, nk) in ((0, 4096), (N - 4096, 4096)):
+            note(f"  rows [{q0},{q0 + QROWS}) keys [{k0},{k0 + nk})")
+            s, o = qa().debug_s_fwd(ws, 1, 1, N, 128, False, "fp16", False, 0, 0, q0, QROWS, k0, nk)
+            torch.cuda.synchronize()
+            s = s.cpu().numpy()
+            ref = oracle.s_int32_tile(pq["q_i8"], pq["k_i8"], 0, 0, i * QROWS, QROWS, k0, nk)
+            assert np.array_equal(s.astype(np.int64), ref.astype(np.int64)), \
+                f"S differs at {int((s != ref).sum())} entries (q0={q0}, k0={k0})"
+            o = o.cpu().numpy()
+            if q0 in o_rows:   # the same rows from another launch: the same bits
+                assert np.array_equal(o.view(np.uint32), o_rows[q0].view(np.uint32))
+            o_rows[q0] = o
+    # O of sampled rows: the oracle's tiled attention over all keys, on the
+    # operands of its prepass (as oracle.sage_attention assembles them)
+    note("max length: oracle O of sampled rows over all keys")
+    sub = np.array([0, 1, 77, 127, 128, 196, 254, 255])          # rows of q_sub
+    rows = np.where(sub < QROWS, sub, sub - QROWS + N - QROWS)     # rows of the head
+    vvals, _, _ = oracle.prep_v(inp.vf, "fp16")
+    ref = oracle.attention(pq["q_i8"][0, 0, sub].astype(np.float64),
+                           pq["q_scale"][0, 0, sub // QROWS],
+                           pq["k_i8"][0, 0].astype(np.float64),
+                           pq["k_scale"][0, 0, np.arange(N) // 64], vvals[0, 0], np.ones(128),
+                           causal=False, p_round=oracle.fp16_round, rows=rows)
+    got = np.stack([o_rows[0][r] if r < QROWS else o_rows[N - QROWS][r - (N - QROWS)]
+                    for r in rows])
+    err = np.abs(got.astype(np.float64) - ref)
+    note(f"max length: max|dO| = {err.max():.3e}")
+    assert err.max() <= 2e-3 and oracle.cos_sim(got, ref) >= 0.9999

@@ -240,6 +240,41 @@ def make_inputs(wl: Workload | str, **overrides) -> Inputs:
     raise ValueError(f"dtype {wl.dtype!r}")
 
 
+def make_inputs_uniform(wl: Workload, scale: float = 2.0, q_spans=None) -> Inputs:
+    """As make_inputs, but q, k, v uniform in [-scale, scale) (float32 draws in
+    the order Q, K, V, then the extras, then the 16-bit rounding): for heads of
+    millions of tokens, where normal draws alone would take minutes.
+    q_spans: optional [(t0, count), ...]; Q is then drawn on those token spans
+    only (in that order) and zero elsewhere."""
+    shape = (wl.B, wl.H, wl.N, wl.d)
+    rng = np.random.default_rng(wl.seed)
+
+    def draw(shp):
+        x = rng.random(shp, dtype=np.float32)
+        x *= np.float32(2.0 * scale)
+        x -= np.float32(scale)
+        return x
+    if q_spans is None:
+        q = draw(shape)
+    else:
+        q = np.zeros(shape, np.float32)
+        for (t0, cnt) in q_spans:
+            q[:, :, t0:t0 + cnt] = draw((wl.B, wl.H, cnt, wl.d))
+    k, v = draw(shape), draw(shape)
+    _apply_extras(wl, rng, q, k, v)
+    if wl.dtype == "fp16":
+        qh, kh, vh = (round_to_fp16(t) for t in (q, k, v))
+        del q, k, v
+        return Inputs(wl, qh.view(np.uint16), kh.view(np.uint16), vh.view(np.uint16),
+                      qh.astype(np.float32), kh.astype(np.float32), vh.astype(np.float32))
+    if wl.dtype == "bf16":
+        qb, kb, vb = (round_to_bf16_bits(t) for t in (q, k, v))
+        del q, k, v
+        return Inputs(wl, qb, kb, vb, bf16_bits_to_f32(qb), bf16_bits_to_f32(kb),
+                      bf16_bits_to_f32(vb))
+    raise ValueError(f"dtype {wl.dtype!r}")
+
+
 def small(name="t", B=1, H=2, N=200, d=64, dtype="fp16", causal=False, pv_mode="fp16",
           seed=11, extras="kbias4") -> Workload:
     """A small ad-hoc workload for tests."""
