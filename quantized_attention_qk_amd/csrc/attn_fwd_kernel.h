@@ -1177,6 +1177,16 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
     }
   }
   // Tail: the last steps, with masking and missing tiles handled explicitly.
+  // Causal: a tile whose first key lies past this wavefront's last row is
+  // hidden from all of its rows (the second diagonal tile, for the first two
+  // wavefronts of a block); its scores, softmax and P~V would change nothing
+  // (P~ = 0, alpha = 1), so the wavefront skips them and only takes part in
+  // the copies and barriers.  The debug instantiation computes them (its
+  // scores are checked).
+  const int last_row = qb * BQW + wave * kWaveQ + (kWaveQ - 1);
+  auto dead = [&](int t) __attribute__((always_inline)) {
+    return CAUSAL && !DUMP && t * kKvTile > last_row;
+  };
   for (; j < nt; j += 2) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -1192,20 +1202,22 @@ void attn_fwd_kernel(const int8_t* __restrict__ q_i8, const int8_t* __restrict__
         if constexpr (PV == kPvInt8) {
           // P^ V^, softmax, then the next scores: the two score tiles are
           // never live at once (the INT32 product needs the registers)
-          if constexpr (ACC) rescale_i32<D>(o, alpha_pend);
-          pv_tile<D, PV, ACC>(o, p_cur, vbuf[u], n, hh, alpha_pend);
-          if (jj + 1 < nt) alpha_pend = softmax_any(s_cur, p_new, jj + 1);
-          if (jj + 2 < nt) {
+          if (!dead(jj)) {
+            if constexpr (ACC) rescale_i32<D>(o, alpha_pend);
+            pv_tile<D, PV, ACC>(o, p_cur, vbuf[u], n, hh, alpha_pend);
+          }
+          if (jj + 1 < nt) alpha_pend = dead(jj + 1) ? 1.f : softmax_any(s_cur, p_new, jj + 1);
+          if (jj + 2 < nt && !dead(jj + 2)) {
             qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init, sqo);
             if constexpr (DUMP) dump_tile<PV>(dw, s_new, jj + 2, qrow, N, hh);
           }
         } else {
-          if (jj + 2 < nt) {
+          if (jj + 2 < nt && !dead(jj + 2)) {
             qk_tile<D, SQ>(s_new, qf, kbuf[kslot(jj + 2, u + 2)], n, hh, init, sqo);
             if constexpr (DUMP) dump_tile<PV>(dw, s_new, jj + 2, qrow, N, hh);
           }
-          pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh, alpha_pend);
-          if (jj + 1 < nt) rescale<D>(o, softmax_any(s_cur, p_new, jj + 1));
+          if (!dead(jj)) pv_tile<D, PV>(o, p_cur, vbuf[u], n, hh, alpha_pend);
+          if (jj + 1 < nt && !dead(jj + 1)) rescale<D>(o, softmax_any(s_cur, p_new, jj + 1));
         }
         wait_lds_loads();
         __syncthreads();
