@@ -86,17 +86,21 @@ __global__ __launch_bounds__(256) void smooth_q_kernel(
       f[e] = in_to_f32<DT>((uint16_t)(wd[e >> 1] >> (16 * (e & 1)))) * inv_sqrt_d;
   };
   // the block's largest |value| with (s) and without (p) the mean taken
-  // out; the second only where the block is left unsmoothed
+  // out; the second only where the block is left unsmoothed.  The smoothed
+  // values stay in registers for the quantisation below.
+  float xs[MAXC][8];
   auto block_amax = [&](bool smoothed, float* red) __attribute__((always_inline)) {
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int c = tid + i * 256;
-      if (c < nchunk) {
-        float f[8];
-        chunk(c, f);
+      float f[8];
+      chunk(c < nchunk ? c : 0, f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(smoothed ? f[e] - qb8[e] : f[e]));
+      for (int e = 0; e < 8; ++e) {
+        const float x = c < nchunk ? (smoothed ? f[e] - qb8[e] : f[e]) : 0.f;
+        if (smoothed) xs[i][e] = x;
+        m = fmaxf(m, fabsf(x));
       }
     }
     m = wave_max(m);
@@ -132,11 +136,16 @@ __global__ __launch_bounds__(256) void smooth_q_kernel(
     const int c = tid + i * 256;
     if (c < nchunk) {
       float f[8];
-      chunk(c, f);
+      if (ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = xs[i][e];
+      } else {
+        chunk(c, f);
+      }
       uint32_t packed[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float t = __builtin_rintf((ok ? f[e] - qb8[e] : f[e]) * r);
+        float t = __builtin_rintf(f[e] * r);
         t = fminf(fmaxf(t, -127.f), 127.f);
         packed[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)t) << ((e & 3) * 8);
       }
