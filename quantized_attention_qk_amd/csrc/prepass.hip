@@ -51,8 +51,10 @@ __device__ __forceinline__ void colstats_chunk(const uint16_t* __restrict__ k,
   const size_t ts = nhd ? (size_t)H * D : (size_t)D;   // token stride (elements)
   const size_t base = row_off<D>(bh, t0, H, N, nhd) + 2 * p;
   const size_t out = ((size_t)bh * nchunks + chunk) * D + 2 * p;
-  // Loads are issued in batches of UNR tokens (those at or past the chunk's
-  // end are skipped) before the batch is added in token order.
+  // Loads are issued in batches of UNR tokens before the batch is added in
+  // token order (the chunk's 256 tokens in two batches: each batch costs a
+  // full memory round trip, and a chunk is walked by one thread per channel
+  // pair).
   if constexpr (!ROPE) {
     if constexpr (DO_K) {
       const uint16_t* kp = k + base;
@@ -60,8 +62,8 @@ __device__ __forceinline__ void colstats_chunk(const uint16_t* __restrict__ k,
       for (int t0 = 0; t0 < cnt; t0 += UNR) {
         uint32_t w[UNR];
 #pragma unroll
-        for (int u = 0; u < UNR; ++u)
-          w[u] = t0 + u < cnt ? *reinterpret_cast<const uint32_t*>(kp + (t0 + u) * ts) : 0u;
+        for (int u = 0; u < UNR; ++u)   // (past the end: the last token again, not added)
+          w[u] = *reinterpret_cast<const uint32_t*>(kp + min(t0 + u, cnt - 1) * ts);
 #pragma unroll
         for (int u = 0; u < UNR; ++u)
           if (t0 + u < cnt) {
@@ -77,10 +79,10 @@ __device__ __forceinline__ void colstats_chunk(const uint16_t* __restrict__ k,
       for (int t0 = 0; t0 < cnt; t0 += UNR) {
         uint32_t w[UNR];
 #pragma unroll
-        for (int u = 0; u < UNR; ++u)
-          w[u] = t0 + u < cnt ? *reinterpret_cast<const uint32_t*>(vp + (t0 + u) * ts) : 0u;
+        for (int u = 0; u < UNR; ++u)   // (past the end: the last token again, same maximum)
+          w[u] = *reinterpret_cast<const uint32_t*>(vp + min(t0 + u, cnt - 1) * ts);
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {   // a skipped token reads 0, which changes no maximum
+        for (int u = 0; u < UNR; ++u) {
           m0 = fmaxf(m0, fabsf(in_to_f32<DT>((uint16_t)(w[u] & 0xffffu))));
           m1 = fmaxf(m1, fabsf(in_to_f32<DT>((uint16_t)(w[u] >> 16))));
         }
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(256) void colstats_kernel(const uint16_t* __restric
   constexpr int CPW = 256 / P;
   const int chunk = blockIdx.x * CPW + threadIdx.x / P;
   if (chunk >= nchunks) return;
-  colstats_chunk<DT, D, DO_K, DO_V, ROPE, 32>(k, v, N, H, nhd, nchunks, rope_cos, rope_sin, part_sum,
+  colstats_chunk<DT, D, DO_K, DO_V, ROPE, 128>(k, v, N, H, nhd, nchunks, rope_cos, rope_sin, part_sum,
                                           part_max, blockIdx.y, chunk, threadIdx.x % P);
 }
 
