@@ -64,12 +64,20 @@ __device__ __forceinline__ void colstats_chunk(const uint16_t* __restrict__ k,
 #pragma unroll
         for (int u = 0; u < UNR; ++u)   // (past the end: the last token again, not added)
           w[u] = *reinterpret_cast<const uint32_t*>(kp + min(t0 + u, cnt - 1) * ts);
+        if (t0 + UNR <= cnt) {   // a whole batch (every batch but a ragged last one)
 #pragma unroll
-        for (int u = 0; u < UNR; ++u)
-          if (t0 + u < cnt) {
+          for (int u = 0; u < UNR; ++u) {
             s0 += in_to_f32<DT>((uint16_t)(w[u] & 0xffffu));
             s1 += in_to_f32<DT>((uint16_t)(w[u] >> 16));
           }
+        } else {
+#pragma unroll
+          for (int u = 0; u < UNR; ++u)
+            if (t0 + u < cnt) {
+              s0 += in_to_f32<DT>((uint16_t)(w[u] & 0xffffu));
+              s1 += in_to_f32<DT>((uint16_t)(w[u] >> 16));
+            }
+        }
       }
       *reinterpret_cast<v2f*>(part_sum + out) = v2f{s0, s1};
     }
@@ -152,7 +160,9 @@ __global__ __launch_bounds__(256) void colstats_kernel(const uint16_t* __restric
                                                        float* __restrict__ part_max) {
   constexpr int P = ColstatsShape<D, ROPE>::P;
   constexpr int CPW = 256 / P;
-  const int chunk = blockIdx.x * CPW + threadIdx.x / P;
+  int chunk = blockIdx.x * CPW + threadIdx.x / P;
+  // a chunk per wavefront (P = 64): uniform, so its bounds are scalar
+  if constexpr (P % 64 == 0) chunk = __builtin_amdgcn_readfirstlane(chunk);
   if (chunk >= nchunks) return;
   colstats_chunk<DT, D, DO_K, DO_V, ROPE, 128>(k, v, N, H, nhd, nchunks, rope_cos, rope_sin, part_sum,
                                           part_max, blockIdx.y, chunk, threadIdx.x % P);
