@@ -783,6 +783,69 @@ hipError_t launch_prep_v(const void* v, const float* v_recip, int dtype, int B, 
   return hipErrorInvalidValue;
 }
 
+// Q^ and K^ blocks and V tiles in one launch (after the column statistics):
+// workgroups [0, nqk) take quant_block's blocks first_blk + x (Q^ blocks,
+// then K^ blocks), the rest one V tile each, as quant_qk_kernel and
+// prep_v_kernel do in two launches.
+template <int DT, int D, int PV, bool ROPE>
+__global__ __launch_bounds__(256) void quant_qkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ k_mean,
+    const float* __restrict__ v_recip, int N, int H, int nhd, int nqb, int nkb, int first_blk,
+    int nqk, int ntiles, float inv_sqrt_d, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8,
+    float* __restrict__ q_scale, float* __restrict__ k_scale, uint8_t* __restrict__ v_out) {
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[PrepVTile<D>::HALVES];
+  const int bh = blockIdx.y, bx = blockIdx.x;
+  if (bx < nqk) {
+    quant_block<DT, D, ROPE>(q, k, k_mean, N, H, nhd, nqb, nkb, inv_sqrt_d, rope_cos, rope_sin,
+                             q_i8, k_i8, q_scale, k_scale, bh, bx + first_blk, red);
+  } else {
+    prep_v_tile<DT, D, PV>(v, PV != kPvFp16 ? v_recip + (size_t)bh * D : nullptr, N, H, nhd,
+                           ntiles, v_out, bh, bx - nqk, tile);
+  }
+}
+
+template <int DT, int D, int PV, bool ROPE>
+static hipError_t quant_qkv_dispatch(const void* q, const void* k, const void* v,
+                                     const float* k_mean, const float* v_recip, int B, int H,
+                                     int N, const InLayout& in, int8_t* q_i8, int8_t* k_i8,
+                                     float* q_scale, float* k_scale, uint8_t* v_out,
+                                     hipStream_t s) {
+  const int nqb = ceil_div(N, kQBlock), nkb = ceil_div(N, kKBlock);
+  const int nt = ceil_div(N, kKvTile);
+  const float isd = (float)(1.0 / __builtin_sqrt((double)D));
+  const int first = q ? 0 : nqb;
+  const int nqk = (q ? nqb : 0) + nkb;
+  dim3 grid(nqk + nt, B * H);
+  quant_qkv_kernel<DT, D, PV, ROPE><<<grid, 256, 0, s>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), k_mean, v_recip, N, H, in.nhd, nqb, nkb, first, nqk, nt,
+      isd, in.rope_cos, in.rope_sin, q_i8, k_i8, q_scale, k_scale, v_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_qkv(const void* q, const void* k, const void* v, const float* k_mean,
+                            const float* v_recip, int dtype, int B, int H, int N, int d,
+                            int pv_mode, const InLayout& in, int8_t* q_i8, int8_t* k_i8,
+                            float* q_scale, float* k_scale, uint8_t* v_out, hipStream_t s) {
+  if (!k || !v) return hipErrorInvalidValue;
+  const bool rope = in.rope_cos != nullptr;
+#define SAGE_QKV(DT, D, PV)                                                                   \
+  if (dtype == DT && d == D && pv_mode == PV)                                                 \
+    return rope ? quant_qkv_dispatch<DT, D, PV, true>(q, k, v, k_mean, v_recip, B, H, N, in,   \
+                                                      q_i8, k_i8, q_scale, k_scale, v_out, s) \
+                : quant_qkv_dispatch<DT, D, PV, false>(q, k, v, k_mean, v_recip, B, H, N, in,  \
+                                                       q_i8, k_i8, q_scale, k_scale, v_out, s);
+  SAGE_QKV(0, 64, 0) SAGE_QKV(0, 64, 1) SAGE_QKV(0, 64, 2)
+  SAGE_QKV(0, 128, 0) SAGE_QKV(0, 128, 1) SAGE_QKV(0, 128, 2)
+  SAGE_QKV(1, 64, 0) SAGE_QKV(1, 64, 1) SAGE_QKV(1, 64, 2)
+  SAGE_QKV(1, 128, 0) SAGE_QKV(1, 128, 1) SAGE_QKV(1, 128, 2)
+#undef SAGE_QKV
+  return hipErrorInvalidValue;
+}
+
 template <int DT, int D, int PV>
 static hipError_t prepass_head_dispatch(const void* q, const void* k, const void* v, int B,
                                         int H, int N, const InLayout& in, const PrepassOut& o,

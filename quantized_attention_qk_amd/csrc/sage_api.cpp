@@ -166,10 +166,8 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, 
                               F(L.part_sum), qv ? F(L.part_max) : nullptr, F(L.k_mean),
                               F(L.v_scale), F(L.v_recip), s);
     if (e != hipSuccess) return SAGE_ERR_HIP;
-    e = sage::launch_quant_qk(q, k, F(L.k_mean), dtype, B, H, N, d, in, q_i8, k_i8,
-                              F(L.q_scale), F(L.k_scale), s);
-    if (e != hipSuccess) return SAGE_ERR_HIP;
-    e = sage::launch_prep_v(v, F(L.v_recip), dtype, B, H, N, d, pv_mode, layout, v_t, s);
+    e = sage::launch_quant_qkv(q, k, v, F(L.k_mean), F(L.v_recip), dtype, B, H, N, d, pv_mode,
+                               in, q_i8, k_i8, F(L.q_scale), F(L.k_scale), v_t, s);
     if (e != hipSuccess) return SAGE_ERR_HIP;
   }
   if (out_kind < 0) return SAGE_OK;
@@ -203,10 +201,8 @@ int run_fwd_sq(const void* q, const void* k, const void* v, void* o, int B, int 
                                        F(L.part_sum), qv ? F(L.part_max) : nullptr, F(L.k_mean),
                                        F(L.v_scale), F(L.v_recip), s);
   if (e != hipSuccess) return SAGE_ERR_HIP;
-  e = sage::launch_quant_qk(nullptr, k, F(L.k_mean), dtype, B, H, N, d, in, nullptr, k_i8,
-                            nullptr, F(L.k_scale), s);
-  if (e != hipSuccess) return SAGE_ERR_HIP;
-  e = sage::launch_prep_v(v, F(L.v_recip), dtype, B, H, N, d, pv_mode, layout, v_t, s);
+  e = sage::launch_quant_qkv(nullptr, k, v, F(L.k_mean), F(L.v_recip), dtype, B, H, N, d,
+                             pv_mode, in, nullptr, k_i8, nullptr, F(L.k_scale), v_t, s);
   if (e != hipSuccess) return SAGE_ERR_HIP;
   e = sage::launch_smooth_q(q, dtype, B, H, N, d, layout, q_i8, F(L.q_scale), F(L.q_mean), q_w,
                             s);

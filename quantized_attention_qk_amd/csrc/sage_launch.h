@@ -63,6 +63,13 @@ hipError_t launch_quant_qk(const void* q, const void* k, const float* k_mean, in
 hipError_t launch_prep_v(const void* v, const float* v_recip, int dtype, int B, int H, int N,
                          int d, int pv_mode, int nhd, uint8_t* v_out, hipStream_t s);
 
+// launch_quant_qk and launch_prep_v as one launch (q may be null: K^ and V
+// only; V in the layout in.nhd).
+hipError_t launch_quant_qkv(const void* q, const void* k, const void* v, const float* k_mean,
+                            const float* v_recip, int dtype, int B, int H, int N, int d,
+                            int pv_mode, const InLayout& in, int8_t* q_i8, int8_t* k_i8,
+                            float* q_scale, float* k_scale, uint8_t* v_out, hipStream_t s);
+
 // Outputs of the one-launch prepass (any may be null when its stage is skipped).
 struct PrepassOut {
   float* part_sum;   // float32 [B*H, ceil(N/256), d] column partial sums of K
