@@ -214,7 +214,7 @@ __global__ __launch_bounds__(128) void finalize_kernel(const float* __restrict__
 template <int DT, int D, bool ROPE>
 __device__ __forceinline__ void quant_block(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const float* __restrict__ k_mean, int N, int H, int nhd, int nqb, int nkb, float inv_sqrt_d,
+    const float* __restrict__ mean, int N, int H, int nhd, int nqb, int nkb, float inv_sqrt_d,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
     int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8, float* __restrict__ q_scale,
     float* __restrict__ k_scale, int bh, int bx, float* red) {
@@ -226,8 +226,7 @@ __device__ __forceinline__ void quant_block(
   const int ntok = min(btok, N - tok0);
   const int nchunk = ntok * (D / 8);
   const size_t base = ((size_t)bh * N + tok0) * D;   // of the INT8 output ([B,H,N,d])
-  const uint16_t* src = isq ? q : k;
-  const float* mean = k_mean + (size_t)bh * D;
+  const uint16_t* src = isq ? q : k;   // (mean: head bh's K mean, read by K blocks only)
   constexpr int CPR = D / 8;   // chunks per token row
 
   // Every chunk of this thread covers the same 8 channels (256 * 8 is a
@@ -325,8 +324,9 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
     int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8, float* __restrict__ q_scale,
     float* __restrict__ k_scale) {
   __shared__ float red[4];
-  quant_block<DT, D, ROPE>(q, k, k_mean, N, H, nhd, nqb, nkb, inv_sqrt_d, rope_cos, rope_sin,
-                           q_i8, k_i8, q_scale, k_scale, blockIdx.y, blockIdx.x + first_blk, red);
+  quant_block<DT, D, ROPE>(q, k, k_mean ? k_mean + (size_t)blockIdx.y * D : nullptr, N, H, nhd,
+                           nqb, nkb, inv_sqrt_d, rope_cos, rope_sin, q_i8, k_i8, q_scale,
+                           k_scale, blockIdx.y, blockIdx.x + first_blk, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -632,8 +632,8 @@ __global__ __launch_bounds__(256) void prepass_roles_kernel(
     }
     role -= nch;
     if (role < nqb) {   // a Q block: quant_block's index bx < nqb selects Q
-      quant_block<DT, D, ROPE>(q, k, k_mean, N, H, nhd, nqb, nkb, inv_sqrt_d, rope_cos,
-                               rope_sin, q_i8, k_i8, q_scale, k_scale, bh, role, red);
+      quant_block<DT, D, ROPE>(q, k, k_mean + (size_t)bh * D, N, H, nhd, nqb, nkb, inv_sqrt_d,
+                               rope_cos, rope_sin, q_i8, k_i8, q_scale, k_scale, bh, role, red);
       return;
     }
     role -= nqb;
@@ -688,7 +688,7 @@ template <int DT, int D, bool ROPE>
 static hipError_t colstats_dispatch(const void* k, const void* v, int B, int H, int N, float vr,
                                     const InLayout& in, float* part_sum, float* part_max,
                                     float* k_mean, float* v_scale, float* v_recip,
-                                    hipStream_t s) {
+                                    bool finalize, hipStream_t s) {
   const int nch = ceil_div(N, kMeanChunk);
   const int cpw = 256 / (ROPE ? D / 4 : D / 2);
   dim3 grid(ceil_div(nch, cpw), B * H);
@@ -699,8 +699,9 @@ static hipError_t colstats_dispatch(const void* k, const void* v, int B, int H, 
   colstats_kernel<DT, D, DK, DV, ROPE><<<grid, 256, 0, s>>>(kp, vp, N, H, in.nhd, nch,         \
                                                             in.rope_cos, in.rope_sin, part_sum, \
                                                             part_max);                          \
-  finalize_kernel<D, DK, DV><<<B * H, 128, 0, s>>>(part_sum, part_max, N, nch, k_mean, v_scale, \
-                                                   v_recip, vr);
+  if (finalize)                                                                               \
+    finalize_kernel<D, DK, DV><<<B * H, 128, 0, s>>>(part_sum, part_max, N, nch, k_mean,       \
+                                                     v_scale, v_recip, vr);
   if (dk && dv) {
     SAGE_COLSTATS(true, true)
   } else if (dk) {
@@ -714,16 +715,17 @@ static hipError_t colstats_dispatch(const void* k, const void* v, int B, int H, 
 
 hipError_t launch_colstats(const void* k, const void* v, int dtype, int B, int H, int N, int d,
                            int pv_mode, const InLayout& in, float* part_sum, float* part_max,
-                           float* k_mean, float* v_scale, float* v_recip, hipStream_t s) {
+                           float* k_mean, float* v_scale, float* v_recip, hipStream_t s,
+                           bool finalize) {
   // RoPE rotates K only; V statistics never see it
   const bool rope = in.rope_cos != nullptr && k != nullptr;
   const float vr = pv_mode == kPvInt8 ? 127.f : 448.f;
 #define SAGE_CS(DT, D)                                                                        \
   if (dtype == DT && d == D)                                                                  \
     return rope ? colstats_dispatch<DT, D, true>(k, v, B, H, N, vr, in, part_sum, part_max,     \
-                                                 k_mean, v_scale, v_recip, s)                    \
+                                                 k_mean, v_scale, v_recip, finalize, s)          \
                 : colstats_dispatch<DT, D, false>(k, v, B, H, N, vr, in, part_sum, part_max,    \
-                                                  k_mean, v_scale, v_recip, s);
+                                                  k_mean, v_scale, v_recip, finalize, s);
   SAGE_CS(0, 64) SAGE_CS(0, 128) SAGE_CS(1, 64) SAGE_CS(1, 128)
 #undef SAGE_CS
   return hipErrorInvalidValue;
@@ -786,58 +788,113 @@ hipError_t launch_prep_v(const void* v, const float* v_recip, int dtype, int B, 
 // Q^ and K^ blocks and V tiles in one launch (after the column statistics):
 // workgroups [0, nqk) take quant_block's blocks first_blk + x (Q^ blocks,
 // then K^ blocks), the rest one V tile each, as quant_qk_kernel and
-// prep_v_kernel do in two launches.
-template <int DT, int D, int PV, bool ROPE>
+// prep_v_kernel do in two launches.  FOLD (heads of at most kFoldMaxChunks
+// 256-token chunks): no finalize_kernel launch before this one; each K^
+// workgroup forms its head's mean from the chunk partials, and each V
+// workgroup (FP8, INT8) its head's 1/delta_V, with finalize_channel's
+// expressions, into LDS; the head's first K^ block and first V tile also
+// store them, as finalize_kernel would.
+constexpr int kFoldMaxChunks = 16;
+template <int DT, int D, int PV, bool ROPE, bool FOLD>
 __global__ __launch_bounds__(256) void quant_qkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ k_mean,
-    const float* __restrict__ v_recip, int N, int H, int nhd, int nqb, int nkb, int first_blk,
-    int nqk, int ntiles, float inv_sqrt_d, const float* __restrict__ rope_cos,
-    const float* __restrict__ rope_sin, int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8,
-    float* __restrict__ q_scale, float* __restrict__ k_scale, uint8_t* __restrict__ v_out) {
+    const uint16_t* __restrict__ v, float* __restrict__ k_mean, float* __restrict__ v_recip,
+    int N, int H, int nhd, int nqb, int nkb, int first_blk, int nqk, int ntiles,
+    float inv_sqrt_d, const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
+    int8_t* __restrict__ q_i8, int8_t* __restrict__ k_i8, float* __restrict__ q_scale,
+    float* __restrict__ k_scale, uint8_t* __restrict__ v_out, const float* __restrict__ part_sum,
+    const float* __restrict__ part_max, int nch, float* __restrict__ v_scale) {
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint16_t tile[PrepVTile<D>::HALVES];
+  __shared__ __attribute__((aligned(16))) float stat[FOLD ? D : 4];
   const int bh = blockIdx.y, bx = blockIdx.x;
+  if constexpr (FOLD) {
+    const bool kblk = bx < nqk && bx + first_blk >= nqb;
+    if (kblk) {
+      for (int c = threadIdx.x; c < D; c += 256) {
+        // the (at most 16) partials loaded at once, then added in chunk order
+        float pv[kFoldMaxChunks];
+#pragma unroll
+        for (int j = 0; j < kFoldMaxChunks; ++j)
+          pv[j] = part_sum[((size_t)bh * nch + min(j, nch - 1)) * D + c];
+        float tot = 0.f;
+#pragma unroll
+        for (int j = 0; j < kFoldMaxChunks; ++j)
+          if (j < nch) tot += pv[j];
+        stat[c] = tot / (float)N;
+        if (bx + first_blk == nqb) k_mean[(size_t)bh * D + c] = stat[c];
+      }
+    } else if (PV != kPvFp16 && bx >= nqk) {
+      constexpr float VR = PV == kPvInt8 ? 127.f : 448.f;
+      for (int c = threadIdx.x; c < D; c += 256) {
+        float cm = 0.f;   // (the last partial re-read past nch: the same maximum)
+#pragma unroll
+        for (int j = 0; j < kFoldMaxChunks; ++j)
+          cm = fmaxf(cm, part_max[((size_t)bh * nch + min(j, nch - 1)) * D + c]);
+        stat[c] = cm > 0.f ? VR / cm : 0.f;
+        if (bx == nqk) {
+          v_scale[(size_t)bh * D + c] = cm / VR;
+          v_recip[(size_t)bh * D + c] = stat[c];
+        }
+      }
+    }
+    __syncthreads();
+  }
   if (bx < nqk) {
-    quant_block<DT, D, ROPE>(q, k, k_mean, N, H, nhd, nqb, nkb, inv_sqrt_d, rope_cos, rope_sin,
-                             q_i8, k_i8, q_scale, k_scale, bh, bx + first_blk, red);
+    quant_block<DT, D, ROPE>(q, k, FOLD ? stat : k_mean + (size_t)bh * D, N, H, nhd, nqb, nkb,
+                             inv_sqrt_d, rope_cos, rope_sin, q_i8, k_i8, q_scale, k_scale, bh,
+                             bx + first_blk, red);
   } else {
-    prep_v_tile<DT, D, PV>(v, PV != kPvFp16 ? v_recip + (size_t)bh * D : nullptr, N, H, nhd,
-                           ntiles, v_out, bh, bx - nqk, tile);
+    const float* rc = PV == kPvFp16 ? nullptr : FOLD ? stat : v_recip + (size_t)bh * D;
+    prep_v_tile<DT, D, PV>(v, rc, N, H, nhd, ntiles, v_out, bh, bx - nqk, tile);
   }
 }
 
 template <int DT, int D, int PV, bool ROPE>
 static hipError_t quant_qkv_dispatch(const void* q, const void* k, const void* v,
-                                     const float* k_mean, const float* v_recip, int B, int H,
-                                     int N, const InLayout& in, int8_t* q_i8, int8_t* k_i8,
+                                     float* k_mean, float* v_recip, int B, int H, int N,
+                                     const InLayout& in, int8_t* q_i8, int8_t* k_i8,
                                      float* q_scale, float* k_scale, uint8_t* v_out,
-                                     hipStream_t s) {
+                                     const float* part_sum, const float* part_max,
+                                     float* v_scale, bool fold, hipStream_t s) {
   const int nqb = ceil_div(N, kQBlock), nkb = ceil_div(N, kKBlock);
-  const int nt = ceil_div(N, kKvTile);
+  const int nt = ceil_div(N, kKvTile), nch = ceil_div(N, kMeanChunk);
   const float isd = (float)(1.0 / __builtin_sqrt((double)D));
   const int first = q ? 0 : nqb;
   const int nqk = (q ? nqb : 0) + nkb;
   dim3 grid(nqk + nt, B * H);
-  quant_qkv_kernel<DT, D, PV, ROPE><<<grid, 256, 0, s>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), k_mean, v_recip, N, H, in.nhd, nqb, nkb, first, nqk, nt,
-      isd, in.rope_cos, in.rope_sin, q_i8, k_i8, q_scale, k_scale, v_out);
+  auto qp = static_cast<const uint16_t*>(q);
+  auto kp = static_cast<const uint16_t*>(k);
+  auto vp = static_cast<const uint16_t*>(v);
+  if (fold)
+    quant_qkv_kernel<DT, D, PV, ROPE, true><<<grid, 256, 0, s>>>(
+        qp, kp, vp, k_mean, v_recip, N, H, in.nhd, nqb, nkb, first, nqk, nt, isd, in.rope_cos,
+        in.rope_sin, q_i8, k_i8, q_scale, k_scale, v_out, part_sum, part_max, nch, v_scale);
+  else
+    quant_qkv_kernel<DT, D, PV, ROPE, false><<<grid, 256, 0, s>>>(
+        qp, kp, vp, k_mean, v_recip, N, H, in.nhd, nqb, nkb, first, nqk, nt, isd, in.rope_cos,
+        in.rope_sin, q_i8, k_i8, q_scale, k_scale, v_out, part_sum, part_max, nch, v_scale);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_qkv(const void* q, const void* k, const void* v, const float* k_mean,
-                            const float* v_recip, int dtype, int B, int H, int N, int d,
-                            int pv_mode, const InLayout& in, int8_t* q_i8, int8_t* k_i8,
-                            float* q_scale, float* k_scale, uint8_t* v_out, hipStream_t s) {
+bool quant_qkv_folds(int N) { return ceil_div(N, kMeanChunk) <= kFoldMaxChunks; }
+
+hipError_t launch_quant_qkv(const void* q, const void* k, const void* v, float* k_mean,
+                            float* v_recip, int dtype, int B, int H, int N, int d, int pv_mode,
+                            const InLayout& in, int8_t* q_i8, int8_t* k_i8, float* q_scale,
+                            float* k_scale, uint8_t* v_out, const float* part_sum,
+                            const float* part_max, float* v_scale, hipStream_t s) {
   if (!k || !v) return hipErrorInvalidValue;
   const bool rope = in.rope_cos != nullptr;
+  const bool fold = quant_qkv_folds(N);
 #define SAGE_QKV(DT, D, PV)                                                                   \
   if (dtype == DT && d == D && pv_mode == PV)                                                 \
     return rope ? quant_qkv_dispatch<DT, D, PV, true>(q, k, v, k_mean, v_recip, B, H, N, in,   \
-                                                      q_i8, k_i8, q_scale, k_scale, v_out, s) \
+                                                      q_i8, k_i8, q_scale, k_scale, v_out,    \
+                                                      part_sum, part_max, v_scale, fold, s)   \
                 : quant_qkv_dispatch<DT, D, PV, false>(q, k, v, k_mean, v_recip, B, H, N, in,  \
-                                                       q_i8, k_i8, q_scale, k_scale, v_out, s);
+                                                       q_i8, k_i8, q_scale, k_scale, v_out,   \
+                                                       part_sum, part_max, v_scale, fold, s);
   SAGE_QKV(0, 64, 0) SAGE_QKV(0, 64, 1) SAGE_QKV(0, 64, 2)
   SAGE_QKV(0, 128, 0) SAGE_QKV(0, 128, 1) SAGE_QKV(0, 128, 2)
   SAGE_QKV(1, 64, 0) SAGE_QKV(1, 64, 1) SAGE_QKV(1, 64, 2)

@@ -164,10 +164,11 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, 
   } else {
     e = sage::launch_colstats(k, qv ? v : nullptr, dtype, B, H, N, d, pv_mode, in,
                               F(L.part_sum), qv ? F(L.part_max) : nullptr, F(L.k_mean),
-                              F(L.v_scale), F(L.v_recip), s);
+                              F(L.v_scale), F(L.v_recip), s, !sage::quant_qkv_folds(N));
     if (e != hipSuccess) return SAGE_ERR_HIP;
     e = sage::launch_quant_qkv(q, k, v, F(L.k_mean), F(L.v_recip), dtype, B, H, N, d, pv_mode,
-                               in, q_i8, k_i8, F(L.q_scale), F(L.k_scale), v_t, s);
+                               in, q_i8, k_i8, F(L.q_scale), F(L.k_scale), v_t, F(L.part_sum),
+                               qv ? F(L.part_max) : nullptr, F(L.v_scale), s);
     if (e != hipSuccess) return SAGE_ERR_HIP;
   }
   if (out_kind < 0) return SAGE_OK;
@@ -199,10 +200,12 @@ int run_fwd_sq(const void* q, const void* k, const void* v, void* o, int B, int 
   const bool qv = sage::v_quantised(pv_mode);
   hipError_t e = sage::launch_colstats(k, qv ? v : nullptr, dtype, B, H, N, d, pv_mode, in,
                                        F(L.part_sum), qv ? F(L.part_max) : nullptr, F(L.k_mean),
-                                       F(L.v_scale), F(L.v_recip), s);
+                                       F(L.v_scale), F(L.v_recip), s,
+                                       !sage::quant_qkv_folds(N));
   if (e != hipSuccess) return SAGE_ERR_HIP;
   e = sage::launch_quant_qkv(nullptr, k, v, F(L.k_mean), F(L.v_recip), dtype, B, H, N, d,
-                             pv_mode, in, nullptr, k_i8, nullptr, F(L.k_scale), v_t, s);
+                             pv_mode, in, nullptr, k_i8, nullptr, F(L.k_scale), v_t,
+                             F(L.part_sum), qv ? F(L.part_max) : nullptr, F(L.v_scale), s);
   if (e != hipSuccess) return SAGE_ERR_HIP;
   e = sage::launch_smooth_q(q, dtype, B, H, N, d, layout, q_i8, F(L.q_scale), F(L.q_mean), q_w,
                             s);

@@ -49,9 +49,12 @@ struct InLayout {
 // and, if v != nullptr, of |V| (partial maxima into part_max), then the
 // finalised mean and, for V, delta_V and its reciprocal in the range of
 // pv_mode (FP8 448, INT8 127).
+// finalize = false: the partials only (launch_quant_qkv forms the statistics
+// itself where quant_qkv_folds(N)).
 hipError_t launch_colstats(const void* k, const void* v, int dtype, int B, int H, int N, int d,
                            int pv_mode, const InLayout& in, float* part_sum, float* part_max,
-                           float* k_mean, float* v_scale, float* v_recip, hipStream_t s);
+                           float* k_mean, float* v_scale, float* v_recip, hipStream_t s,
+                           bool finalize = true);
 
 // Prepass: INT8 quantisation of Q/sqrt(d) (128-token blocks) and of K - mean
 // (64-token blocks).  Either q or k may be null to skip that tensor.
@@ -64,11 +67,17 @@ hipError_t launch_prep_v(const void* v, const float* v_recip, int dtype, int B, 
                          int d, int pv_mode, int nhd, uint8_t* v_out, hipStream_t s);
 
 // launch_quant_qk and launch_prep_v as one launch (q may be null: K^ and V
-// only; V in the layout in.nhd).
-hipError_t launch_quant_qkv(const void* q, const void* k, const void* v, const float* k_mean,
-                            const float* v_recip, int dtype, int B, int H, int N, int d,
-                            int pv_mode, const InLayout& in, int8_t* q_i8, int8_t* k_i8,
-                            float* q_scale, float* k_scale, uint8_t* v_out, hipStream_t s);
+// only; V in the layout in.nhd).  Where quant_qkv_folds(N) (at most 16
+// 256-token chunks) the launch also forms the K mean and, with V quantised,
+// delta_V and its reciprocal from the column partials (part_sum, part_max),
+// storing them into k_mean, v_scale, v_recip: the column statistics are
+// then launched without their finalisation.
+bool quant_qkv_folds(int N);
+hipError_t launch_quant_qkv(const void* q, const void* k, const void* v, float* k_mean,
+                            float* v_recip, int dtype, int B, int H, int N, int d, int pv_mode,
+                            const InLayout& in, int8_t* q_i8, int8_t* k_i8, float* q_scale,
+                            float* k_scale, uint8_t* v_out, const float* part_sum,
+                            const float* part_max, float* v_scale, hipStream_t s);
 
 // Outputs of the one-launch prepass (any may be null when its stage is skipped).
 struct PrepassOut {
