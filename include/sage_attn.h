@@ -320,6 +320,25 @@ int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H,
                       void* stream);
 
 /*
+ * The rest of sage_attn_fwd: its attention kernel ([SA] §3 Algorithm 1 from
+ * the INT8 product on: dequantisation, online softmax, P~V in the pv_mode
+ * precision, O = O / l) on the operands a preceding sage_attn_prepare with the
+ * same B, H, N, d, pv_mode left in `workspace` (stream-ordered: launch both
+ * on the same stream, or wait between them).  o: [B,H,N,d] of out_dtype
+ * (SAGE_DT_F16, SAGE_DT_BF16 or SAGE_OUT_F32), caller-owned, 16-byte aligned.
+ * sage_attn_prepare followed by sage_attn_attend computes exactly what
+ * sage_attn_fwd computes (the same launches, bit for bit); the split lets a
+ * caller time or schedule the two halves.  The workspace is only read.
+ * Errors: SAGE_ERR_INVALID_ARG (null or misaligned pointers, bad flags),
+ * SAGE_ERR_UNSUPPORTED (shape), SAGE_ERR_WORKSPACE (smaller than
+ * sage_attn_workspace_bytes(B, H, N, d, pv_mode)).  Workspace contents not
+ * written by such a sage_attn_prepare give undefined output (no fault: every
+ * read stays inside the documented layout).
+ */
+int sage_attn_attend(const void* workspace, size_t workspace_bytes, void* o, int B, int H,
+                     int N, int d, int causal, int pv_mode, int out_dtype, void* stream);
+
+/*
  * Debug: the INT32 scores of the timed attention kernel itself ([SA] §3
  * Algorithm 1: S = Q^ K^^T in INT32).  Re-runs the attention kernel's debug
  * instantiation -- the same source, instruction schedule, LDS staging and

@@ -6,7 +6,7 @@ Importing this package does not require a GPU; calling into it does, and it
 fails loudly (RuntimeError) when the HIP library is missing or no device is
 visible.  There is no CPU fallback.
 """
-from .api import (debug_s_fwd, debug_s_i32, prepare, quant_v, ref_rows, sage_attn,  # noqa: F401
+from .api import (attend, debug_s_fwd, debug_s_i32, prepare, quant_v, ref_rows, sage_attn,  # noqa: F401
                   sage_attn_quantized, smooth_q, smooth_quant_qk, tiling, untile_v,
                   workspace_bytes)
 from .adaptive import choose_mode, load_modes, save_modes, select_pv_modes  # noqa: F401

@@ -46,6 +46,7 @@ _SIGNATURES = {
     "sage_attn_debug_fwd_f32": (_c_int, [_vp] * 4 + [_c_int] * 7 + [_vp, _c_size, _vp]),
     "sage_attn_fwd_noalloc": (_c_int, [_vp] * 4 + [_c_int] * 7 + [_vp]),
     "sage_attn_prepare": (_c_int, [_vp] * 3 + [_c_int] * 6 + [_vp, _c_size, _vp]),
+    "sage_attn_attend": (_c_int, [_vp, _c_size, _vp] + [_c_int] * 7 + [_vp]),
 }
 
 _lib = None

@@ -254,6 +254,21 @@ def prepare(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pv_mode: str,
                                   workspace.numel(), _stream_ptr(q.device)), "sage_attn_prepare")
 
 
+def attend(workspace: torch.Tensor, B: int, H: int, N: int, d: int, causal: bool = False,
+           pv_mode: str = "fp16", out_dtype: torch.dtype = torch.bfloat16,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """The attention kernel of sage_attn alone (sage_attn_attend) on the
+    operands a preceding prepare(...) with the same shape and pv_mode left in
+    `workspace` (same stream).  prepare + attend = sage_attn, bit for bit."""
+    odt = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}[out_dtype]
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=workspace.device)
+    check(lib().sage_attn_attend(workspace.data_ptr(), workspace.numel(), out.data_ptr(), B, H,
+                                 N, d, int(causal), SAGE_PV[pv_mode], odt,
+                                 _stream_ptr(workspace.device)), "sage_attn_attend")
+    return out
+
+
 def debug_s_fwd(workspace: torch.Tensor, B: int, H: int, N: int, d: int, causal: bool,
                 pv_mode: str, smooth_q: bool, b: int, h: int, q0: int, nq: int, k0: int,
                 nk: int):

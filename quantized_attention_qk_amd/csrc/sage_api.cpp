@@ -274,6 +274,32 @@ int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H,
                  nullptr, workspace, workspace_bytes, stream, -1);
 }
 
+int sage_attn_attend(const void* workspace, size_t workspace_bytes, void* o, int B, int H,
+                     int N, int d, int causal, int pv_mode, int out_dtype, void* stream) {
+  if (!workspace || !o) return SAGE_ERR_INVALID_ARG;
+  if (!aligned16(o) || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return SAGE_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (!sage::pv_valid(pv_mode)) return SAGE_ERR_INVALID_ARG;
+  if (out_dtype != SAGE_DT_F16 && out_dtype != SAGE_DT_BF16 && out_dtype != SAGE_OUT_F32)
+    return SAGE_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
+  if (!shape_ok(B, H, N, d)) return SAGE_ERR_UNSUPPORTED;
+  const Layout L = make_layout(B, H, N, d, pv_mode);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  int st = device_check();
+  if (st != SAGE_OK) return st;
+  // the same launch as the end of run_fwd, on the operands its prepass left
+  uint8_t* w = static_cast<uint8_t*>(const_cast<void*>(workspace));
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+  return hip_status(sage::launch_attn(reinterpret_cast<int8_t*>(w + L.q_i8),
+                                      reinterpret_cast<int8_t*>(w + L.k_i8), w + L.v_t,
+                                      F(L.q_scale), F(L.k_scale), F(L.v_scale), nullptr, B, H,
+                                      N, d, causal, pv_mode, out_dtype, SAGE_LAYOUT_HND, o,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 int sage_attn_fwd_f32out(const void* q, const void* k, const void* v, float* o, int B, int H,
                          int N, int d, int causal, int pv_mode, int dtype, void* workspace,
                          size_t workspace_bytes, void* stream) {

@@ -318,6 +318,34 @@ def test_prepare_validation():
         assert call() == NO_DEVICE
 
 
+def test_attend_validation():
+    # workspace, bytes, o, B, H, N, d, causal, pv, out_dtype, stream
+    h = lib()
+    ws = P + 0x100000
+    need = h.sage_attn_workspace_bytes(1, 2, 100, 64, 1)
+    base = [ws, need, P, 1, 2, 100, 64, 0, 1, 0, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return h.sage_attn_attend(*a)
+    assert call(a0=None) == INVALID
+    assert call(a2=None) == INVALID
+    assert call(a2=P + 8) == INVALID            # o not 16-byte aligned
+    assert call(a0=ws + 16) == INVALID          # workspace not 256-byte aligned
+    assert call(a7=2) == INVALID                # causal flag
+    assert call(a8=3) == INVALID                # P~V mode
+    assert call(a9=3) == INVALID                # output type
+    assert call(a4=0) == INVALID
+    assert call(a6=96) == UNSUPPORTED
+    assert call(a5=(1 << 24) + 1) == UNSUPPORTED
+    assert call(a1=need - 1) == WORKSPACE
+    if not torch.cuda.is_available():
+        assert call() == NO_DEVICE
+        assert call(a9=2) == NO_DEVICE          # float32 output is a valid type
+
+
 def test_debug_s_fwd_validation():
     # workspace, bytes, B, H, N, d, causal, pv, smooth_q, b, h, q0, nq, k0, nk, s_out, o_rows, stream
     h = lib()

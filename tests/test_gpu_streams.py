@@ -93,3 +93,28 @@ def test_graph_capture_and_replay(wl):
         assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {rep}"
         del junk
     note(f"{wl.name}: 4 graph replays bitwise equal to eager runs")
+
+
+@pytest.mark.parametrize("wl", [small("pa300", N=300, d=64, seed=44),
+                                small("pa3000c8", B=1, H=2, N=3000, d=128, dtype="bf16",
+                                      causal=True, pv_mode="fp8", seed=45),
+                                small("pa5000i8", B=1, H=2, N=5000, d=64, pv_mode="int8",
+                                      seed=46)],
+                         ids=lambda w: w.name)
+def test_prepare_then_attend_is_the_forward_pass(wl):
+    """sage_attn_prepare followed by sage_attn_attend on one workspace gives
+    the forward pass's output bit for bit (16-bit and float32 outputs), for
+    the short, folded-statistics and long prepass paths."""
+    q, k, v = make_inputs(wl).torch_tensors("cuda")
+    B, H, N, d = q.shape
+    ref16 = qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode)
+    ref32 = qa().sage_attn(q, k, v, causal=wl.causal, pv_mode=wl.pv_mode, out_f32=True)
+    ws = torch.empty(qa().workspace_bytes(B, H, N, d, wl.pv_mode), dtype=torch.uint8,
+                     device="cuda")
+    qa().prepare(q, k, v, wl.pv_mode, ws)
+    o16 = qa().attend(ws, B, H, N, d, wl.causal, wl.pv_mode, out_dtype=q.dtype)
+    o32 = qa().attend(ws, B, H, N, d, wl.causal, wl.pv_mode, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o16.view(torch.int16), ref16.view(torch.int16))
+    assert torch.equal(o32.view(torch.int32), ref32.view(torch.int32))
+    note(f"{wl.name}: prepare + attend bitwise equal to sage_attn")
