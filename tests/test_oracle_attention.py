@@ -267,6 +267,34 @@ def test_fp8_flip_bound_covers_perturbed_rounding():
     assert moved > 0.0
 
 
+def test_fp8_codes_follow_the_exact_max():
+    """Why FP8 P~V keeps the exact running max.  P^ = E4M3(448 P~) has 3
+    mantissa bits, so scaling every 448 P~ by a common factor 1 + r (O and l
+    alike, as a max rounded up onto a grid would) moves codes across rounding
+    boundaries: at r = -1e-4 (a max 1.4e-4 log2 units high) O moves by more
+    than the 2e-3 parity bar on these inputs, although without rounding the
+    factor would cancel in O / l exactly.  A shift of 1e-6 (float32 rounding
+    of the argument) stays far inside it."""
+    import oracle.sage_oracle as so
+    from oracle.codecs import e4m3_encode
+    wl = small("s197", N=197, d=64, pv_mode="fp8", seed=11, extras="kbias4")
+    inp = make_inputs(wl)
+    pq = smooth_quant_qk(inp.qf, inp.kf)
+    _, codes, vscale = prep_v(inp.vf, "fp8")
+    vvals = e4m3_decode(codes)
+    N = wl.N
+    args = (pq["q_i8"][0, 0].astype(np.float64), pq["q_scale"][0, 0, np.arange(N) // 128],
+            pq["k_i8"][0, 0].astype(np.float64), pq["k_scale"][0, 0, np.arange(N) // 64],
+            vvals[0, 0], vscale[0, 0].astype(np.float64))
+    o = so.attention(*args, causal=False, p_round=so._p_round_for("fp8"))
+    moved = {}
+    for r in (-1e-4, 1e-6):
+        pr = lambda p, r=r: e4m3_decode(e4m3_encode(p * 448.0 * (1.0 + r))) / (448.0 * (1.0 + r))
+        moved[r] = float(np.abs(so.attention(*args, causal=False, p_round=pr) - o).max())
+    assert moved[-1e-4] > 2e-3, moved
+    assert moved[1e-6] < 1e-5, moved
+
+
 def _int8_head_args(qf, kf, vf, b=0, h=0):
     import oracle
     N = qf.shape[2]
