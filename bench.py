@@ -54,7 +54,41 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES (3 launches), to calibrate "
                          "the HBM byte counters against a known traffic")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only time torch's own streaming kernels (a device copy, a "
+                         "float32-accumulated sum of bf16 data and a fill, 128 MiB and 1 GiB): "
+                         "the HBM rates plain copy, read and write kernels reach on this GPU")
     return ap.parse_args()
+
+
+def stream_probe():
+    """HBM rates of torch's own streaming kernels, the yardstick for the
+    prepass kernels: a device copy (bytes read + written), a full sum of a
+    bf16 tensor with float32 accumulation (bytes read) and a fill (bytes
+    written), averaged over 20 launches after 3 untimed ones, at 128 MiB
+    (one 16-bit tensor of c2) and 1 GiB."""
+    import torch
+    res = {}
+    for mib in (128, 1024):
+        n = mib * 1024 * 1024 // 2
+        x = torch.randn(n, dtype=torch.bfloat16, device="cuda")
+        y = torch.empty_like(x)
+        for name, fn, nbytes in (("copy", lambda: y.copy_(x), 4 * n),
+                                 ("sum", lambda: torch.sum(x, dtype=torch.float32), 2 * n),
+                                 ("fill", lambda: y.fill_(1.0), 2 * n)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(20):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / 20
+            res[f"{name}_{mib}MiB"] = {"ms": round(ms, 4), "TB_per_s": round(nbytes / ms / 1e9, 2)}
+        del x, y
+    print(json.dumps({"stream_probe": res}), flush=True)
 
 
 def copy_probe(nbytes: int):
@@ -155,6 +189,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.stream_probe:
+        stream_probe()
         return
     if args.mfma_probe:
         from quantized_attention_qk_amd import probe
