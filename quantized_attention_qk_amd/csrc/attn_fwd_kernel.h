@@ -751,11 +751,19 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
   auto uop = [&]<int U>() __attribute__((always_inline)) {
     if constexpr (U < NPRE) {
       // FP8, INT8: triples of (max of two scores into one of 4 partial
-      // maxima, two conversions)
+      // maxima, two conversions).  The maxima are written as explicit
+      // 3-input instructions (one per score pair after the first four):
+      // left to the compiler, the chains get re-associated into pairwise
+      // maxima first and take about five more instructions per step.
       constexpr int g = U / 3, r = U % 3;
       if constexpr (r == 0) {
-        const int v = max(sc(2 * g), sc(2 * g + 1));
-        mpart[g & 3] = g < 4 ? v : max(mpart[g & 3], v);
+        if constexpr (g < 4) {
+          mpart[g] = max(sc(2 * g), sc(2 * g + 1));
+        } else {
+          asm("v_max3_i32 %0, %1, %2, %3"
+              : "=v"(mpart[g & 3])
+              : "v"(mpart[g & 3]), "v"(sc(2 * g)), "v"(sc(2 * g + 1)));
+        }
       } else {
         f[2 * g + r - 1] = (float)sc(2 * g + r - 1);
       }
@@ -766,10 +774,13 @@ __device__ __forceinline__ void fused_step(v16f (&o)[D / 32], const v4i (&qf)[D 
         nb = -(ts.k0 + m_run);
         lsum = l_run;
       } else {
-        int mx = max(max(mpart[0], mpart[1]), max(mpart[2], mpart[3]));
-        mx = pair_max_i32(mx);
+        int mx;
+        asm("v_max3_i32 %0, %1, %2, %3" : "=v"(mx) : "v"(mpart[0]), "v"(mpart[1]), "v"(mpart[2]));
+        mx = pair_max_i32(max(mx, mpart[3]));
         const float mt = (float)mx * ts.c;
-        m_new = fmaxf(m_run, mt);
+        // the larger of two finite-or-(-inf) floats (m_run starts at -inf;
+        // neither is a NaN), without the NaN quieting fmaxf adds
+        asm("v_max_f32 %0, %1, %2" : "=v"(m_new) : "v"(m_run), "v"(mt));
         nb = (PV == kPvInt8 ? kLog2_127 : kLog2_448) - m_new;
         if constexpr (PV == kPvInt8) {
           // the row's largest 127 P~ rounds to at most 127 (see softmax_tile)
